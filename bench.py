@@ -1,0 +1,265 @@
+"""Benchmark of the verified sparse-attention decode step on one MI355X.
+
+A step is one vattn_decode call (predict, select, base, budget, gather,
+combine) over one batch of the Llama-3-8B-shaped workload: 8 sequences of
+32768 tokens, 32 query / 8 KV heads, head dim 128, bf16 paged KV cache,
+rank-32 low-rank predictor, sinks 128, window 128, top-k 2.5%,
+eps = delta = 0.05.  Inputs are synthetic and resident in HBM before timing.
+Three copies of the caches are rotated so that no step finds its keys in the
+last-level cache.  The sampling seed changes every step.
+
+Prints one JSON line: heads*tokens/s, the roofline of the dominant kernel
+(per-kernel HIP events over the timed steps; algorithmic bytes from the
+kernel's own token counts), the (eps, delta) violation rate against a dense
+fp32 reference, and the CPU oracle timed on the host cores.
+"""
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode heads·tokens/s at 32K ctx; achieved HBM GB/s; ε-violation rate"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--profile", action="store_true",
+                    help="few steps, no CPU baseline or rate (for rocprofv3 runs)")
+    ap.add_argument("--rate-seeds", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self, n):
+        self.rt = C.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = C.c_void_p()
+            if self.rt.hipEventCreate(C.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed(self, a, b):
+        ms = C.c_float()
+        if self.rt.hipEventElapsedTime(C.byref(ms), C.c_void_p(self.ev[a]), C.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.ev:
+            self.rt.hipEventDestroy(C.c_void_p(h))
+
+
+def source_hash():
+    h = hashlib.sha1()
+    for f in ("vattn_kernels.hip", "vattn_device.hpp", "vattn_plan.hpp"):
+        with open(os.path.join(ROOT, "verified_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode step's (batch, KV head) groups are "
+              "independent, so N GPUs would each run this same single-GPU step on their own shard; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import verified_sparse_attention_amd as vsa
+
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    w = synthetic.WORKLOADS[args.workload]()
+    G = w.Hq // w.Hkv
+    d = w.d
+    esize = w.k_cache.element_size()
+    r = w.cfg["rank"]
+    log("workload %s: B=%d Hq=%d Hkv=%d d=%d L=%d kv=%s" % (w.name, w.B, w.Hq, w.Hkv, d,
+                                                            w.max_seq_len, w.k_cache.dtype))
+    q = w.q.to(dev)
+    bt = w.block_table.to(dev)
+    sl = w.seq_lens.to(dev)
+    proj = w.proj.to(dev) if w.proj is not None else None
+    k0 = w.k_cache.to(dev)
+    v0 = w.v_cache.to(dev)
+    kt0 = vsa.project_keys(k0, proj) if w.cfg["predictor"] == 1 else None
+    n_inst = 3
+    inst = [(k0, v0, kt0)] + [(k0.clone(), v0.clone(), kt0.clone() if kt0 is not None else None)
+                              for _ in range(n_inst - 1)]
+    decs, pdecs = [], []
+    ws = None
+    for (k, v, kt) in inst:
+        for lst, gc in ((decs, False), (pdecs, True)):
+            dd = vsa.Decoder(q, k, v, bt, sl, vsa.Config.from_dict(w.cfg), max_seq_len=w.max_seq_len,
+                             k_lowrank=kt, proj=proj, want_group_counts=gc, workspace=ws)
+            ws = dd.workspace
+            lst.append(dd)
+    torch.cuda.synchronize()
+
+    steps, warm = (min(args.steps, 5), min(args.warmup, 2)) if args.profile else (args.steps, args.warmup)
+    for s in range(warm):
+        decs[s % n_inst].set_seed(10_000 + s)
+        decs[s % n_inst]()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` decode steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        dd = decs[s % n_inst]
+        dd.set_seed(s)
+        dd()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / steps
+    heads_tokens = w.heads_tokens()
+    value = heads_tokens / (ms_per_step * 1e-3)
+    log("%.4f ms/step, %.4g heads*tokens/s (wall %.4f ms/step)" % (ms_per_step, value,
+                                                                   t_wall * 1e3 / steps))
+
+    # ---- per-kernel durations with events on the launch stream, same steps
+    nst = vsa.NUM_STAGES
+    ev = HipEvents((nst + 1) * steps)
+    stage_ms = np.zeros(nst)
+    gsum = torch.zeros(w.B, w.Hkv, 2, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        dd = pdecs[s % n_inst]
+        dd.set_seed(s)
+        dd.profiled(ev.ev[(nst + 1) * s:(nst + 1) * (s + 1)])
+        gsum += dd.group_counts
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for k in range(nst):
+            stage_ms[k] += ev.elapsed((nst + 1) * s + k, (nst + 1) * s + k + 1)
+    ev.close()
+    stage_ms /= steps
+    gmean = gsum.double().cpu().numpy() / steps  # mean |U_g|, |B_g| per group per step
+    U = gmean[..., 0]
+    Bc = gmean[..., 1]
+    L = w.seq_lens.numpy().astype(np.float64)[:, None]
+
+    # ---- algorithmic bytes per launch (mean over the timed steps)
+    ncg = (w.max_seq_len + 1023) // 1024
+    row = d * esize
+    pred_row = r * 2 if w.cfg["predictor"] == 1 else row
+    pred_bytes = float(w.Hkv * (L * pred_row + np.ceil(L / 16) * 4).sum())
+    base_bytes = float((Bc * row + Bc * G * 4).sum())
+    gather_bytes = float((U * row + (U - Bc) * row + Bc * G * 4).sum()
+                         + w.B * w.Hq * ncg * (d + 2) * 4)
+    step_bytes = pred_bytes + float((U * 2 * row).sum())
+    per_kernel_bytes = {"predict": pred_bytes, "base": base_bytes, "gather": gather_bytes}
+    names = vsa.STAGES
+    dom = int(np.argmax(stage_ms))
+    dom_name = names[dom]
+    stages = {names[k]: round(float(stage_ms[k]) * 1e3, 2) for k in range(nst)}
+    log("stage us: %s" % stages)
+    log("mean |U_g| %.0f (density %.3f), |B_g| %.0f" % (U.mean(), (U / L).mean(), Bc.mean()))
+    dom_bytes = per_kernel_bytes.get(dom_name)
+    achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9 if dom_bytes else None
+
+    traffic = None
+    pmc_file = os.path.join(ROOT, "profiles", "%s_%s.pmc.json" % (dom_name, w.name))
+    if os.path.exists(pmc_file):
+        with open(pmc_file) as f:
+            pmc = json.load(f)
+        if pmc.get("source_hash") == source_hash():
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                "traffic": traffic, "kernel": "k_" + dom_name,
+                "algorithmic_bytes_per_launch": round(dom_bytes) if dom_bytes else None,
+                "kernel_us": round(float(stage_ms[dom]) * 1e3, 2)}
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {"metric": METRIC, "value": round(value, 1), "unit": "heads·tokens/s", "n_gpus": 1,
+              "steps": steps, "warmup": warm, "ms_per_step": round(ms_per_step, 5),
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+              "data": "synthetic",
+              "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                         "head_dim": d, "seq_len": w.max_seq_len,
+                         "kv_dtype": "bf16" if esize == 2 else "f32", "predictor_rank": r,
+                         "sinks": w.cfg["sinks"], "window": w.cfg["window"],
+                         "topk_ppm": w.cfg["topk_ppm"], "eps": w.cfg["eps"], "delta": w.cfg["delta"],
+                         "cache_copies_rotated": n_inst},
+              "roofline": roofline,
+              "step_hbm": {"algorithmic_bytes": round(step_bytes), "achieved_GBps": round(step_gbs, 1),
+                           "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                           "union_density": round(float((U / L).mean()), 4)},
+              "stage_us": stages}
+
+    if not args.profile:
+        # ---- (eps, delta): denominator relative error vs a dense fp32 reference
+        with torch.no_grad():
+            lse_dense = torch.empty(w.B, w.Hq, dtype=torch.float64, device=dev)
+            scale = 1.0 / np.sqrt(d)
+            for b in range(w.B):
+                Lb = int(w.seq_lens[b])
+                pages = bt[b, :(Lb + 15) // 16].long()
+                Kb = k0[pages].permute(1, 0, 2, 3).reshape(w.Hkv, -1, d)[:, :Lb].float()
+                Kb = Kb.repeat_interleave(G, 0).contiguous()
+                s_ = torch.bmm(Kb, (q[b].float() * scale).unsqueeze(-1).contiguous()).squeeze(-1)
+                lse_dense[b] = torch.logsumexp(s_.double(), dim=-1)
+                del Kb, s_
+        viol = trials = 0
+        dd = decs[0]
+        for s in range(args.rate_seeds):
+            dd.set_seed(1_000_000 + s)
+            dd()
+            rel = (torch.exp(dd.lse.double() - lse_dense) - 1.0).abs()
+            viol += int((rel > w.cfg["eps"]).sum())
+            trials += rel.numel()
+        torch.cuda.synchronize()
+        result["eps_violation"] = {"rate": round(viol / trials, 5), "violations": viol,
+                                   "trials": trials, "seeds": args.rate_seeds,
+                                   "delta": w.cfg["delta"], "reference": "dense fp32 scores, fp64 logsumexp"}
+        log("eps violations %d / %d" % (viol, trials))
+
+    if not args.profile and not args.no_cpu_baseline:
+        import oracle
+        cores = min(len(os.sched_getaffinity(0)), 16)
+        arrays = w.oracle_arrays()
+        cpu_cfg = dict(w.cfg, seed=0)
+        t = time.perf_counter()
+        oracle.decode(**arrays, cfg=cpu_cfg, nthreads=cores, want_idx=False)
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": round(heads_tokens / dt, 1), "unit": "heads·tokens/s",
+                                  "cores": cores, "kind": "oracle",
+                                  "sample": "one full decode step of %s (all %d (batch, KV head) groups, "
+                                            "seed 0), %.2f s wall" % (w.name, w.B * w.Hkv, dt)}
+        log("cpu oracle %.2f s on %d threads" % (dt, cores))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * vattn.h -- C ABI of the MI355X (gfx950) verified sparse-attention decode step.
+ *
+ * The operation (edgentiq blog post "vAttention: a new approach to sparse
+ * attention with guaranteed accuracy", sections "Introducing vAttention" and
+ * "How vAttention Works"; SkyLight post "vAttention Computation"):
+ * for one decode step and every query head h of every sequence b,
+ *   1. a deterministic index set I_f = attention sinks (first `sinks` tokens)
+ *      + sliding window (last `window` tokens, the newest included)
+ *      + the k best tokens of the middle by a predictor score.  The predictor
+ *      is either exact scaled scores ("oracle top-k", same post, section
+ *      "Performance and Efficiency") or scores in a rank-r key space (pith.science
+ *      page "Loki: Low-rank Keys for Efficient Sparse Attention", abstract);
+ *   2. a uniform sample without replacement of the remaining tail, of N_t tokens.
+ *      A base sample of n_b tokens estimates the spread of exp(s - m) over the
+ *      tail.  The final size n is the central-limit budget
+ *      n = (z * sigma * N_t / (eps * D))^2, with z = Phi^-1(1 - delta/2),
+ *      clamped to [n_b, N_t].  It makes the softmax denominator estimate D
+ *      relatively eps-accurate with probability >= 1 - delta.  The guarantee
+ *      targets the denominator (same post, "How vAttention Works");
+ *   3. out = sum_i w_i e^{s_i} V_i / sum_i w_i e^{s_i} over I_f + sample, with
+ *      w = 1 on I_f and w = N_t / n (inverse inclusion probability) on the
+ *      sample; lse = log sum_i w_i e^{s_i}.  Scores s_i = q . K_i / sqrt(d).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-owned.  The library allocates no device or host
+ *    memory in vattn_decode / vattn_project_keys; scratch space is the caller's
+ *    workspace.
+ *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL means
+ *    the null stream).  No entry point synchronizes.
+ *  - Errors are returned as vattn_status; nothing aborts or throws across the
+ *    ABI.  Every host-checkable condition is validated before any launch; on a
+ *    non-OK return nothing has been enqueued (except VATTN_E_HIP, which reports
+ *    a failed launch).
+ *  - Undefined (not checked on the device): seq_lens[b] > max_seq_len,
+ *    block_table entries outside [0, num_blocks) for pages below
+ *    ceil(seq_lens[b] / 16), non-finite values in q, K, V, P.
+ *  - Deterministic: the same inputs and seed give bit-identical index sets,
+ *    counts and statistics on any run, and bit-identical out/lse on one GPU.
+ */
+#ifndef VATTN_H
+#define VATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VATTN_PAGE 16          /* tokens per KV page */
+#define VATTN_MAX_SEQ (1 << 20) /* longest supported sequence */
+
+typedef enum {
+    VATTN_OK = 0,
+    VATTN_E_NULL = 1,        /* a required pointer is NULL                         */
+    VATTN_E_SHAPE = 2,       /* a size is outside the supported range              */
+    VATTN_E_DTYPE = 3,       /* unknown kv dtype                                   */
+    VATTN_E_CFG = 4,         /* a vattn_cfg field is out of range                  */
+    VATTN_E_WORKSPACE = 5,   /* workspace NULL, too small or not 256-byte aligned  */
+    VATTN_E_UNSUPPORTED = 6, /* valid request this build does not implement        */
+    VATTN_E_HIP = 7          /* a HIP runtime call or kernel launch failed         */
+} vattn_status;
+
+typedef enum { VATTN_F32 = 0, VATTN_BF16 = 1 } vattn_dtype;
+
+typedef enum {
+    VATTN_PRED_EXACT = 0,  /* top-k on exact scores q_s . K_i (reads K)          */
+    VATTN_PRED_LOWRANK = 1 /* top-k on (q_s P) . Kt_i with Kt = bf16(K P) (reads Kt) */
+} vattn_predictor;
+
+/* Decode configuration (host struct, read once per call). */
+typedef struct {
+    int32_t sinks;        /* >= 0: first tokens always kept                           */
+    int32_t window;       /* >= 0: last tokens always kept (the newest included)       */
+    int32_t topk_abs;     /* >= 0: k itself; -1: k = ceil(L * topk_ppm / 1e6)          */
+    int32_t topk_ppm;     /* used when topk_abs < 0; in [0, 1e6]                       */
+    int32_t base_ppm;     /* base sample = max(2, ceil(N_t * base_ppm / 1e6)), <= N_t; */
+                          /* in [1, 1e6]; 50000 (5%) is the usual value               */
+    int32_t force_budget; /* -1: CLT budget; >= 0: n = min(N_t, force_budget)          */
+    int32_t predictor;    /* vattn_predictor                                          */
+    int32_t rank;         /* r for VATTN_PRED_LOWRANK: 16, 32 or 64, <= d              */
+    double eps;           /* > 0: relative accuracy target of the denominator         */
+    double delta;         /* in (0, 1): failure probability                           */
+    uint64_t seed;        /* Philox4x32-10 key; callers vary it per step and layer     */
+} vattn_cfg;
+
+/* Inputs.  All pointers are device pointers except where noted. */
+typedef struct {
+    const float* q;             /* [B, Hq, d] fp32                                   */
+    const void* k_cache;        /* [num_blocks, Hkv, 16, d] kv_dtype                  */
+    const void* v_cache;        /* [num_blocks, Hkv, 16, d] kv_dtype                  */
+    const uint16_t* k_lowrank;  /* [num_blocks, Hkv, 16, r] bf16 bits (LOWRANK only;  */
+                                /* produced by vattn_project_keys), else NULL         */
+    const float* proj;          /* [d, r] fp32 (LOWRANK only), else NULL              */
+    const int32_t* block_table; /* [B, max_blocks] page ids                           */
+    const int32_t* seq_lens;    /* [B] tokens in each sequence, 0 <= L <= max_seq_len  */
+    int32_t B;                  /* host: batch, >= 1                                  */
+    int32_t Hq, Hkv;            /* host: query / KV heads; Hq / Hkv in {1, 2, 4, 8}   */
+    int32_t d;                  /* host: head dim, 64 or 128                          */
+    int32_t max_blocks;         /* host: row length of block_table                    */
+    int32_t num_blocks;         /* host: pages in the caches                          */
+    int32_t max_seq_len;        /* host: bound on seq_lens, 1 .. VATTN_MAX_SEQ,       */
+                                /*       <= 16 * max_blocks                            */
+    int32_t kv_dtype;           /* host: vattn_dtype of k_cache / v_cache             */
+} vattn_inputs;
+
+/* Outputs.  out and lse are required; the others are optional (NULL = skip). */
+typedef struct {
+    float* out;       /* [B, Hq, d] fp32: attention output (0 when L = 0)              */
+    float* lse;       /* [B, Hq] fp32: log of the weighted denominator (-inf if L = 0)  */
+    int32_t* idx;     /* [B, Hq, idx_cap]: the index set ascending, -1 padded           */
+    int32_t idx_cap;  /* >= max_seq_len when idx != NULL                               */
+    int32_t* counts;  /* [B, Hq, 6]: n_fixed, N_t, n_b, n, |I|, flags                  */
+                      /*   flags bit0: n == N_t (exact), bit1: forced budget,          */
+                      /*   bit2: CLT budget below n_b raised to n_b                    */
+    uint64_t* stats;  /* [B, Hq, 4]: SF, S1, S2 high word, S2 low word: exact sums     */
+                      /*   of E_i = trunc(exp(s_i - m) 2^40) over I_f (SF) and over    */
+                      /*   the base sample (S1, and S2 of E_i^2 as 128 bits)           */
+    int32_t* group_counts; /* [B, Hkv, 2]: tokens whose V row was gathered (the union  */
+                      /*   of the group's index sets) and tokens whose K row the base-  */
+                      /*   score pass read (union of fixed sets and base samples);      */
+                      /*   for byte accounting                                          */
+    double z_used;    /* host, written by vattn_decode: fp32-rounded z                  */
+} vattn_outputs;
+
+/* Bytes of device workspace vattn_decode needs for these shapes and cfg
+ * (0 if the arguments are invalid).  Depends only on host fields. */
+size_t vattn_workspace_size(const vattn_inputs* in, const vattn_cfg* cfg);
+
+/* One decode step (see the top of this file).  `workspace` is a device buffer
+ * of at least vattn_workspace_size bytes, 256-byte aligned, not shared with a
+ * concurrently running call; its contents need no initialization and are
+ * garbage afterwards.  out->z_used is written on the host before launching. */
+vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
+                          void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Kernels of one decode step, in launch order (for vattn_decode_profiled). */
+#define VATTN_NUM_STAGES 7 /* predict, select, base, budget, gather, combine, emit */
+
+/* vattn_decode, additionally recording caller-created hipEvent_t handles on
+ * hip_stream: events[0] before the first kernel and events[s + 1] after stage s
+ * (stage 6, emit, is empty when out->idx is NULL).  n_events must be
+ * VATTN_NUM_STAGES + 1.  For measurement; timing adds event records only. */
+vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
+                                   vattn_outputs* out, void* workspace, size_t ws_bytes,
+                                   void* hip_stream, void* const* events, int32_t n_events);
+
+/* Low-rank key cache for the LOWRANK predictor (Loki page, abstract: keys
+ * scored in a low-dimensional space): k_lowrank[p][g][t][j] =
+ * bf16_rne(pdot(K[p][g][t][:], P[:, j])) for every page p < num_blocks.
+ * k_cache: [num_blocks, Hkv, 16, d] kv_dtype; proj: [d, r] fp32;
+ * k_lowrank: [num_blocks, Hkv, 16, r] bf16 bits (output).  pdot is the
+ * blocked fp32 dot product the predictor uses (fma chains over blocks of 8,
+ * then a pairwise tree over the block partials).  Asynchronous on hip_stream. */
+vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const float* proj,
+                                uint16_t* k_lowrank, int32_t num_blocks, int32_t Hkv,
+                                int32_t d, int32_t r, void* hip_stream);
+
+/* z = Phi^-1(1 - delta/2) rounded to fp32, as vattn_decode uses it (host). */
+double vattn_z_from_delta(double delta);
+
+/* Static string naming a status code. */
+const char* vattn_status_string(vattn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VATTN_H */

@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, rejects bad arguments with the documented status before any
+launch, sizes its workspace, and computes the same fp32 z as the oracle."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import verified_sparse_attention_amd as vsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vsa.LIB_PATH):
+        from verified_sparse_attention_amd import build
+        build.build()
+    return vsa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(vsa.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", vsa.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (vattn_[a-z_0-9]+)$", nm, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def _inputs(**kw):
+    a = dict(q=256, k_cache=256, v_cache=256, k_lowrank=256, proj=256, block_table=256,
+             seq_lens=256, B=2, Hq=8, Hkv=2, d=128, max_blocks=64, num_blocks=128,
+             max_seq_len=1000, kv_dtype=vsa.BF16)
+    a.update(kw)
+    return vsa.vattn_inputs(**a)
+
+
+def _cfg(**kw):
+    c = vsa.Config(sinks=16, window=16, topk_ppm=25000, rank=32)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c.to_c()
+
+
+def _decode(lib, inp, cfg, outs=None, ws=None, ws_bytes=1 << 40):
+    if outs is None:
+        outs = vsa.vattn_outputs(256, 256, None, 0, None, None, None, 0.0)
+    return lib.vattn_decode(C.byref(inp) if inp is not None else None,
+                            C.byref(cfg) if cfg is not None else None,
+                            C.byref(outs) if outs is not None else None,
+                            C.c_void_p(ws) if ws is not None else None, ws_bytes, None)
+
+
+BAD = [
+    ("hq_not_multiple", dict(Hq=6, Hkv=4), {}, 2),
+    ("gqa_16", dict(Hq=32, Hkv=2), {}, 6),
+    ("d_96", dict(d=96), {}, 6),
+    ("seq_0", dict(max_seq_len=0), {}, 2),
+    ("seq_huge", dict(max_seq_len=(1 << 20) + 1, max_blocks=70000), {}, 2),
+    ("blocks_short", dict(max_blocks=10), {}, 2),
+    ("dtype", dict(kv_dtype=7), {}, 3),
+    ("neg_sinks", {}, dict(sinks=-1), 4),
+    ("ppm", {}, dict(topk_ppm=2000000), 4),
+    ("base_ppm0", {}, dict(base_ppm=0), 4),
+    ("eps0", {}, dict(eps=0.0), 4),
+    ("delta1", {}, dict(delta=1.0), 4),
+    ("predictor", {}, dict(predictor=5), 4),
+    ("rank", {}, dict(rank=24), 6),
+    ("rank_gt_d", dict(d=64), dict(rank=128), 6),
+]
+
+
+@pytest.mark.parametrize("name,ikw,ckw,code", BAD, ids=[b[0] for b in BAD])
+def test_rejects_bad_arguments(lib, name, ikw, ckw, code):
+    inp, cfg = _inputs(**ikw), _cfg(**ckw)
+    assert _decode(lib, inp, cfg) == code
+    assert lib.vattn_workspace_size(C.byref(inp), C.byref(cfg)) == 0
+
+
+def test_null_and_workspace_errors(lib):
+    inp, cfg = _inputs(), _cfg()
+    assert _decode(lib, None, cfg) == 1
+    assert _decode(lib, inp, None) == 1
+    assert lib.vattn_decode(C.byref(inp), C.byref(cfg), None, None, 0, None) == 1
+    outs = vsa.vattn_outputs(None, 256, None, 0, None, None, None, 0.0)
+    assert _decode(lib, inp, cfg, outs=outs) == 1
+    assert _decode(lib, _inputs(k_lowrank=None), cfg, ws=256) == 1
+    assert _decode(lib, _inputs(q=None), cfg, ws=256) == 1
+    # idx capacity below max_seq_len
+    outs = vsa.vattn_outputs(256, 256, 256, 999, None, None, None, 0.0)
+    assert _decode(lib, inp, cfg, outs=outs, ws=256) == 2
+    # misaligned q
+    assert _decode(lib, _inputs(q=260), cfg, ws=256) == 2
+    need = lib.vattn_workspace_size(C.byref(inp), C.byref(cfg))
+    assert need > 0
+    assert _decode(lib, inp, cfg, ws=None) == 5
+    assert _decode(lib, inp, cfg, ws=256, ws_bytes=need - 1) == 5
+    assert _decode(lib, inp, cfg, ws=256 + 64, ws_bytes=need) == 5
+    # project_keys argument checks
+    P = C.c_void_p
+    assert lib.vattn_project_keys(None, 1, P(256), P(256), 4, 2, 128, 32, None) == 1
+    assert lib.vattn_project_keys(P(256), 3, P(256), P(256), 4, 2, 128, 32, None) == 3
+    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 4, 2, 128, 24, None) == 6
+    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 0, 2, 128, 32, None) == 2
+
+
+def test_workspace_size_monotone(lib):
+    cfg = _cfg()
+    prev = 0
+    for L in (16, 100, 1000, 5000, 32768, 131072):
+        inp = _inputs(max_seq_len=L, max_blocks=(L + 15) // 16)
+        n = lib.vattn_workspace_size(C.byref(inp), C.byref(cfg))
+        assert n >= prev and n % 256 == 0
+        prev = n
+    a = lib.vattn_workspace_size(C.byref(_inputs(B=1)), C.byref(cfg))
+    b = lib.vattn_workspace_size(C.byref(_inputs(B=4)), C.byref(cfg))
+    assert b > a
+
+
+def test_z_matches_oracle_and_status_strings(lib):
+    for delta in (0.5, 0.2, 0.1, 0.05, 0.02, 0.01, 1e-3, 1e-6, 0.9):
+        assert lib.vattn_z_from_delta(delta) == oracle.z_for_delta(delta)
+    assert lib.vattn_z_from_delta(0.0) != lib.vattn_z_from_delta(0.0)  # NaN
+    for code, name in vsa.STATUS.items():
+        assert lib.vattn_status_string(code).decode().startswith(name)
+
+
+def test_profiled_entry_point_argument_checks(lib):
+    inp, cfg = _inputs(), _cfg()
+    outs = vsa.vattn_outputs(256, 256, None, 0, None, None, None, 0.0)
+    ev = (C.c_void_p * 8)(*([256] * 8))
+    f = lib.vattn_decode_profiled
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, None, 8) == 1
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, 7) == 2
+    ev0 = (C.c_void_p * 8)(*([256] * 7 + [None]))
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev0, 8) == 1
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, 8) == 5

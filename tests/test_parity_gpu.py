@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Index sets, counts and fixed-point statistics must be bit-identical; out and
+lse within max-abs 1e-5 (fp32 KV) or 2e-3 (bf16 KV).  Small cases span several
+predictor chunks, gather chunks and ragged tails; the full-size workloads run in
+the benchmark's launch configuration and are compared on sampled (b, KV head)
+groups that the oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def _gpu():
+    from tests.gpu_run import GpuCase, log
+    return GpuCase, log
+
+
+def compare(w, g, o, groups=None, tag=""):
+    """Bit-exact discrete outputs, tolerance on out/lse, for the given groups."""
+    G = w.Hq // w.Hkv
+    tol = TOL["bf16" if w.k_cache.dtype.is_floating_point and w.k_cache.element_size() == 2 else "f32"]
+    assert g["z32"] == o["z32"]
+    if groups is None:
+        groups = [(b, kv) for b in range(w.B) for kv in range(w.Hkv)]
+    for (b, kv) in groups:
+        for h in range(kv * G, (kv + 1) * G):
+            ctx = "%s b=%d h=%d" % (tag, b, h)
+            assert np.array_equal(g["counts"][b, h], o["counts"][b, h]), \
+                (ctx, g["counts"][b, h], o["counts"][b, h])
+            assert np.array_equal(g["stats"][b, h], o["stats"][b, h]), (ctx, g["stats"][b, h], o["stats"][b, h])
+            if "idx" in g and "idx" in o:
+                assert np.array_equal(g["idx"][b, h], o["idx"][b, h]), ctx
+            L = int(w.seq_lens[b])
+            if L == 0:
+                assert np.all(g["out"][b, h] == 0) and np.isneginf(g["lse"][b, h]), ctx
+                continue
+            err_o = np.max(np.abs(g["out"][b, h].astype(np.float64) - o["out"][b, h]))
+            err_l = abs(float(g["lse"][b, h]) - o["lse"][b, h])
+            assert err_o <= tol and err_l <= tol, (ctx, err_o, err_l)
+
+
+def run_both(w, seeds=(None,), groups=None, want_idx=True, tag=""):
+    GpuCase, log = _gpu()
+    log("[parity] %s %s B=%d Hq=%d Hkv=%d d=%d L=%s" % (tag, w.name, w.B, w.Hq, w.Hkv, w.d,
+                                                       list(w.seq_lens.tolist())[:8]))
+    case = GpuCase(w, want_idx=want_idx)
+    arrays = w.oracle_arrays()
+    for s in seeds:
+        cfg = dict(w.cfg)
+        if s is not None:
+            cfg["seed"] = s
+        g = case.run(cfg["seed"])
+        o = oracle.decode(**arrays, cfg=cfg, groups=groups, want_idx=want_idx, nthreads=8)
+        compare(w, g, o, groups, tag="%s seed=%s" % (tag, cfg["seed"]))
+    return case
+
+
+SMALL_CASES = {
+    "gqa4_bf16_ragged": lambda: synthetic.make(
+        name="gqa4_bf16_ragged", B=3, Hq=16, Hkv=4, d=128, seq_lens=(5000, 2500, 777),
+        kv_dtype="bf16", recipe="outlier", predictor=1, rank=32, sinks=32, window=64,
+        topk_ppm=25000, shuffle=True, data_seed=11),
+    "gqa8_lowrank_3chunks": lambda: synthetic.make(
+        name="gqa8_lowrank_3chunks", B=2, Hq=16, Hkv=2, d=128, seq_lens=(9000, 4100),
+        kv_dtype="bf16", recipe="lowrank", predictor=1, rank=32, sinks=128, window=128,
+        topk_ppm=25000, eps=0.02, data_seed=12),
+    "gqa2_d64_f32_r16": lambda: synthetic.make(
+        name="gqa2_d64_f32_r16", B=2, Hq=4, Hkv=2, d=64, seq_lens=(3000, 1500), kv_dtype="f32",
+        recipe="planted", predictor=1, rank=16, sinks=8, window=16, topk_ppm=20000, data_seed=13),
+    "exact_bf16_d128_g2": lambda: synthetic.make(
+        name="exact_bf16_d128_g2", B=1, Hq=4, Hkv=2, d=128, seq_lens=(2000,), kv_dtype="bf16",
+        recipe="planted", predictor=0, sinks=16, window=16, topk_abs=40, data_seed=14),
+    "r64_g1_2chunks": lambda: synthetic.make(
+        name="r64_g1_2chunks", B=1, Hq=2, Hkv=2, d=128, seq_lens=(33000,), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=64, sinks=64, window=64, topk_ppm=25000,
+        data_seed=15),
+    "flat_small": lambda: synthetic.make(
+        name="flat_small", B=1, Hq=8, Hkv=2, d=128, seq_lens=(6000,), kv_dtype="bf16",
+        recipe="flat", q_std=0.3, k_std=0.3, predictor=1, rank=32, sinks=128, window=128,
+        topk_ppm=10000, eps=0.02, data_seed=16),
+    "mixed_ragged_shuffled": lambda: synthetic.make(
+        name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
+        kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
+        topk_ppm=20000, eps=0.05, delta=0.1, shuffle=True, data_seed=17),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_parity_small(name):
+    run_both(SMALL_CASES[name](), seeds=(0, 1, 977), tag=name)
+
+
+def test_parity_tiny_1000_seeds():
+    w = synthetic.tiny()
+    GpuCase, log = _gpu()
+    log("[parity] tiny_1k x 1000 seeds")
+    case = GpuCase(w)
+    arrays = w.oracle_arrays()
+    for s in range(1000):
+        cfg = dict(w.cfg, seed=s)
+        g = case.run(s)
+        o = oracle.decode(**arrays, cfg=cfg)
+        compare(w, g, o, tag="tiny seed=%d" % s)
+
+
+EDGE_CASES = {
+    "empty_one_short_seqs": lambda: synthetic.make(
+        B=4, Hq=2, Hkv=1, d=64, seq_lens=(0, 1, 20, 50), kv_dtype="f32", predictor=0, sinks=2,
+        window=2, topk_abs=4),
+    "tail_1_and_2": lambda: synthetic.make(
+        B=2, Hq=2, Hkv=1, d=64, seq_lens=(13, 14), kv_dtype="f32", predictor=0, sinks=2,
+        window=2, topk_abs=8),
+    "k_covers_middle": lambda: synthetic.make(
+        B=1, Hq=2, Hkv=1, d=64, seq_lens=(300,), kv_dtype="bf16", predictor=0, sinks=2, window=2,
+        topk_abs=1000),
+    "pure_sampling": lambda: synthetic.make(
+        B=1, Hq=4, Hkv=2, d=128, seq_lens=(3000,), kv_dtype="bf16", recipe="flat", q_std=0.3,
+        k_std=0.3, predictor=1, rank=32, sinks=0, window=0, topk_abs=0),
+    "forced_full": lambda: synthetic.make(
+        B=2, Hq=4, Hkv=2, d=128, seq_lens=(2000, 1234), kv_dtype="bf16", recipe="outlier",
+        predictor=1, rank=32, sinks=16, window=16, force_budget=10 ** 9),
+    "forced_small": lambda: synthetic.make(
+        B=1, Hq=4, Hkv=1, d=64, seq_lens=(1500,), kv_dtype="f32", predictor=0, sinks=4, window=4,
+        topk_abs=16, force_budget=7),
+    "forced_zero": lambda: synthetic.make(
+        B=1, Hq=2, Hkv=1, d=64, seq_lens=(700,), kv_dtype="f32", predictor=0, sinks=4, window=4,
+        topk_abs=16, force_budget=0),
+    "tiny_eps_dense": lambda: synthetic.make(
+        B=1, Hq=4, Hkv=1, d=128, seq_lens=(2500,), kv_dtype="bf16", recipe="outlier", predictor=1,
+        rank=32, sinks=8, window=8, eps=1e-4),
+    "base_ppm_max": lambda: synthetic.make(
+        B=1, Hq=2, Hkv=2, d=64, seq_lens=(900,), kv_dtype="f32", predictor=0, sinks=4, window=4,
+        topk_abs=10, base_ppm=1000000),
+    "page_unaligned_regions": lambda: synthetic.make(
+        B=2, Hq=8, Hkv=1, d=128, seq_lens=(1037, 4099), kv_dtype="bf16", recipe="planted",
+        predictor=1, rank=32, sinks=5, window=27, topk_abs=33, shuffle=True),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+def test_parity_edge_cases(name):
+    run_both(EDGE_CASES[name](), seeds=(0, 5), tag=name)
+
+
+def test_full_budget_matches_dense():
+    w = EDGE_CASES["forced_full"]()
+    GpuCase, log = _gpu()
+    log("[parity] forced_full vs dense")
+    g = GpuCase(w).run()
+    o = oracle.decode(**w.oracle_arrays(), cfg=w.cfg, want_dense=True)
+    assert np.max(np.abs(g["out"] - o["out_dense"])) <= 2e-3
+    assert np.max(np.abs(g["lse"] - o["lse_dense"])) <= 2e-3
+
+
+def test_project_keys_bit_exact():
+    import torch
+    import verified_sparse_attention_amd as vsa
+    _, log = _gpu()
+    for (d, r, dt) in ((128, 32, torch.bfloat16), (64, 16, torch.float32), (128, 64, torch.bfloat16),
+                       (64, 32, torch.float32), (128, 16, torch.float32)):
+        log("[parity] project_keys d=%d r=%d %s" % (d, r, dt))
+        gen = torch.Generator().manual_seed(d * 1000 + r)
+        k = (torch.randn(37, 3, 16, d, generator=gen) * 2.0).to(dt)
+        P = synthetic.orthonormal(d, r, gen)
+        kt = vsa.project_keys(k.cuda(), P.cuda()).cpu().numpy().view(np.uint16)
+        rows = k.float().reshape(-1, d).numpy()
+        want = oracle.project_rows(rows, P.numpy()).reshape(kt.shape)
+        assert np.array_equal(kt, want)
+
+
+def test_deterministic_repeat():
+    w = SMALL_CASES["gqa4_bf16_ragged"]()
+    GpuCase, log = _gpu()
+    log("[parity] determinism")
+    case = GpuCase(w)
+    a = case.run(3)
+    b = case.run(3)
+    for key in ("idx", "counts", "stats", "out", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads in the benchmark's launch configuration, sampled groups.
+# ---------------------------------------------------------------------------
+FULL = {
+    "llama8b_32k": (lambda: synthetic.llama8b_32k(), [(0, 0), (3, 5), (7, 7)]),
+    "flat_128k": (lambda: synthetic.flat_128k(), [(0, 0), (0, 6)]),
+    "ragged_b64": (lambda: synthetic.ragged_b64(), [(0, 1), (17, 4), (40, 0), (63, 7)]),
+    "wide_gqa_64k": (lambda: synthetic.wide_gqa_64k(), [(1, 2), (3, 7)]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_parity_full_size_sampled(name):
+    mk, groups = FULL[name]
+    w = mk()
+    case = run_both(w, seeds=(0,), groups=groups, want_idx=True, tag=name)
+    if name == "wide_gqa_64k":
+        arrays = w.oracle_arrays()
+        for eps in (0.01, 0.02, 0.1):
+            cfg = dict(w.cfg, eps=eps)
+            case.dec.cfg.eps = eps
+            case.dec._ccfg.eps = eps
+            g = case.run(0)
+            o = oracle.decode(**arrays, cfg=cfg, groups=groups[:1], nthreads=8)
+            compare(w, g, o, groups[:1], tag="%s eps=%g" % (name, eps))
+
+
+# ---------------------------------------------------------------------------
+# (eps, delta) on the GPU against the oracle's dense fp64 lse.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,mk", [
+    ("tiny", lambda: synthetic.tiny()),
+    ("flat_gqa", lambda: synthetic.make(name="flat_gqa", B=1, Hq=16, Hkv=4, d=128, seq_lens=(8192,),
+                                        kv_dtype="bf16", recipe="flat", q_std=0.3, k_std=0.3,
+                                        predictor=1, rank=32, sinks=128, window=128,
+                                        topk_ppm=10000, eps=0.02, data_seed=21)),
+    ("peaked_gqa", lambda: synthetic.make(name="peaked_gqa", B=1, Hq=16, Hkv=4, d=128,
+                                          seq_lens=(8192,), kv_dtype="bf16", recipe="outlier",
+                                          predictor=1, rank=32, sinks=128, window=128,
+                                          topk_ppm=25000, eps=0.05, data_seed=22)),
+])
+def test_gpu_eps_delta_rate(name, mk):
+    w = mk()
+    GpuCase, log = _gpu()
+    log("[rate] %s x 1000 seeds" % name)
+    case = GpuCase(w, want_idx=False)
+    dense = oracle.decode(**w.oracle_arrays(), cfg=w.cfg, want_dense=True, want_idx=False,
+                          nthreads=8)["lse_dense"]
+    viol = trials = 0
+    for s in range(1000):
+        g = case.run(s)
+        rel = np.abs(np.exp(g["lse"].astype(np.float64) - dense) - 1.0)
+        viol += int((rel > w.cfg["eps"]).sum())
+        trials += rel.size
+    rate = viol / trials
+    from scipy.stats import beta
+    ub = float(beta.ppf(0.95, viol + 1, trials - viol)) if viol < trials else 1.0
+    log("[rate] %s: %d / %d = %.4f (95%% CP upper %.4f), delta %.3f"
+        % (name, viol, trials, rate, ub, w.cfg["delta"]))
+    assert rate <= w.cfg["delta"]

@@ -1,0 +1,255 @@
+"""MI355X (gfx950) verified sparse-attention decode step: Python binding.
+
+Argument marshalling only: every step of the decode runs in the HIP kernels of
+``libvattn.so`` behind ``include/vattn.h``; PyTorch supplies device memory and
+the stream.  There is no fallback: if the library is missing, importing the
+entry points raises.
+
+The step (edgentiq blog post "vAttention: a new approach to sparse attention
+with guaranteed accuracy", section "How vAttention Works"): per query head,
+sinks + window + predicted top-k tokens plus a uniform sample of the tail sized
+by a central-limit bound on the softmax denominator (eps, delta), with the
+sample weighted by the inverse inclusion probability.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvattn.so")
+
+PAGE = 16
+F32, BF16 = 0, 1
+PRED_EXACT, PRED_LOWRANK = 0, 1
+
+STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
+          4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
+EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
+           "vattn_z_from_delta", "vattn_status_string")
+NUM_STAGES = 7
+STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
+
+
+class VattnError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s failed: %s" % (where, _lib_status(code)))
+
+
+class vattn_cfg(C.Structure):
+    _fields_ = [("sinks", C.c_int32), ("window", C.c_int32), ("topk_abs", C.c_int32),
+                ("topk_ppm", C.c_int32), ("base_ppm", C.c_int32), ("force_budget", C.c_int32),
+                ("predictor", C.c_int32), ("rank", C.c_int32), ("eps", C.c_double),
+                ("delta", C.c_double), ("seed", C.c_uint64)]
+
+
+class vattn_inputs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("k_lowrank", C.c_void_p), ("proj", C.c_void_p), ("block_table", C.c_void_p),
+                ("seq_lens", C.c_void_p), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
+                ("d", C.c_int32), ("max_blocks", C.c_int32), ("num_blocks", C.c_int32),
+                ("max_seq_len", C.c_int32), ("kv_dtype", C.c_int32)]
+
+
+class vattn_outputs(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("lse", C.c_void_p), ("idx", C.c_void_p),
+                ("idx_cap", C.c_int32), ("counts", C.c_void_p), ("stats", C.c_void_p),
+                ("group_counts", C.c_void_p), ("z_used", C.c_double)]
+
+
+_lib = None
+
+
+def load():
+    """Load libvattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (its HIP runtime is the one the library binds to)
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libvattn.so not built: run __graft_entry__.build() or "
+                              "python verified_sparse_attention_amd/build.py")
+        lib = C.CDLL(LIB_PATH)
+        lib.vattn_workspace_size.restype = C.c_size_t
+        lib.vattn_workspace_size.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg)]
+        lib.vattn_decode.restype = C.c_int
+        lib.vattn_decode.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg),
+                                     C.POINTER(vattn_outputs), C.c_void_p, C.c_size_t, C.c_void_p]
+        lib.vattn_decode_profiled.restype = C.c_int
+        lib.vattn_decode_profiled.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg),
+                                              C.POINTER(vattn_outputs), C.c_void_p, C.c_size_t,
+                                              C.c_void_p, C.POINTER(C.c_void_p), C.c_int32]
+        lib.vattn_project_keys.restype = C.c_int
+        lib.vattn_project_keys.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+        lib.vattn_z_from_delta.restype = C.c_double
+        lib.vattn_z_from_delta.argtypes = [C.c_double]
+        lib.vattn_status_string.restype = C.c_char_p
+        lib.vattn_status_string.argtypes = [C.c_int]
+        _lib = lib
+    return _lib
+
+
+def _lib_status(code):
+    try:
+        return load().vattn_status_string(code).decode()
+    except Exception:
+        return STATUS.get(code, str(code))
+
+
+@dataclass
+class Config:
+    sinks: int = 128
+    window: int = 128
+    topk_abs: int = -1
+    topk_ppm: int = 25000
+    base_ppm: int = 50000
+    force_budget: int = -1
+    predictor: int = PRED_LOWRANK
+    rank: int = 32
+    eps: float = 0.05
+    delta: float = 0.05
+    seed: int = 0
+
+    @classmethod
+    def from_dict(cls, d):
+        return cls(**{k: d[k] for k in cls.__dataclass_fields__ if k in d})
+
+    def to_c(self):
+        return vattn_cfg(self.sinks, self.window, self.topk_abs, self.topk_ppm, self.base_ppm,
+                         self.force_budget, self.predictor, self.rank, float(self.eps),
+                         float(self.delta), int(self.seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _kv_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("kv cache dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowrank=None, proj=None):
+    """Fill a vattn_inputs from torch tensors (no copies; all must be contiguous)."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("k_lowrank", k_lowrank),
+                    ("proj", proj)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    B, Hq, d = q.shape
+    return vattn_inputs(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                        None if k_lowrank is None else k_lowrank.data_ptr(),
+                        None if proj is None else proj.data_ptr(), block_table.data_ptr(),
+                        seq_lens.data_ptr(), B, Hq, k_cache.shape[1], d, block_table.shape[1],
+                        k_cache.shape[0], int(max_seq_len), _kv_dtype(k_cache))
+
+
+def workspace_size(inputs: vattn_inputs, cfg: Config) -> int:
+    c = cfg.to_c()
+    return int(load().vattn_workspace_size(C.byref(inputs), C.byref(c)))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+class Decoder:
+    """Holds the marshalled arguments of one decode shape so repeated calls
+    (benchmarks, tests) re-launch without re-marshalling or allocating."""
+
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_len,
+                 k_lowrank=None, proj=None, want_idx=False, want_counts=True, want_stats=True,
+                 want_group_counts=False, workspace=None):
+        import torch
+        load()
+        self.cfg = cfg
+        self.inputs = make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
+                                  k_lowrank, proj)
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, k_lowrank, proj)
+        dev = q.device
+        B, Hq, d = q.shape
+        self.out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(B, Hq, max_seq_len, dtype=torch.int32, device=dev) if want_idx else None
+        self.counts = torch.empty(B, Hq, 6, dtype=torch.int32, device=dev) if want_counts else None
+        self.stats = torch.empty(B, Hq, 4, dtype=torch.int64, device=dev) if want_stats else None
+        self.group_counts = (torch.empty(B, k_cache.shape[1], 2, dtype=torch.int32, device=dev)
+                             if want_group_counts else None)
+        self.ws_bytes = workspace_size(self.inputs, cfg)
+        if self.ws_bytes == 0:
+            raise VattnError(4, "vattn_workspace_size (invalid shapes or cfg)")
+        if workspace is None:
+            workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=dev)
+        base = workspace.data_ptr()
+        self.ws_ptr = (base + 255) // 256 * 256
+        if workspace.numel() - (self.ws_ptr - base) < self.ws_bytes:
+            raise ValueError("workspace too small: need %d bytes" % self.ws_bytes)
+        self.workspace = workspace
+        self.outputs = vattn_outputs(self.out.data_ptr(), self.lse.data_ptr(),
+                                     None if self.idx is None else self.idx.data_ptr(),
+                                     max_seq_len if want_idx else 0,
+                                     None if self.counts is None else self.counts.data_ptr(),
+                                     None if self.stats is None else self.stats.data_ptr(),
+                                     None if self.group_counts is None else self.group_counts.data_ptr(),
+                                     0.0)
+        self._ccfg = cfg.to_c()
+
+    def set_seed(self, seed: int):
+        self.cfg.seed = seed
+        self._ccfg.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+
+    def __call__(self, stream=None):
+        rc = load().vattn_decode(C.byref(self.inputs), C.byref(self._ccfg), C.byref(self.outputs),
+                                 C.c_void_p(self.ws_ptr), self.ws_bytes, _stream_handle(stream))
+        if rc != 0:
+            raise VattnError(rc, "vattn_decode")
+        return self
+
+    def profiled(self, events, stream=None):
+        """Same launch, recording NUM_STAGES + 1 caller-created hipEvent_t handles."""
+        arr = (C.c_void_p * (NUM_STAGES + 1))(*events)
+        rc = load().vattn_decode_profiled(C.byref(self.inputs), C.byref(self._ccfg),
+                                          C.byref(self.outputs), C.c_void_p(self.ws_ptr),
+                                          self.ws_bytes, _stream_handle(stream), arr, NUM_STAGES + 1)
+        if rc != 0:
+            raise VattnError(rc, "vattn_decode_profiled")
+        return self
+
+    @property
+    def z_used(self) -> float:
+        return self.outputs.z_used
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_len, k_lowrank=None,
+           proj=None, want_idx=False, stream=None):
+    """One decode step; returns the Decoder holding out, lse, idx, counts, stats."""
+    dec = Decoder(q, k_cache, v_cache, block_table, seq_lens, cfg, max_seq_len=max_seq_len,
+                  k_lowrank=k_lowrank, proj=proj, want_idx=want_idx)
+    return dec(stream)
+
+
+def project_keys(k_cache, proj, k_lowrank=None, stream=None):
+    """Low-rank key cache bf16(K P) for the low-rank predictor (as int16 bit patterns)."""
+    import torch
+    nb, Hkv, page, d = k_cache.shape
+    r = proj.shape[1]
+    if k_lowrank is None:
+        k_lowrank = torch.empty(nb, Hkv, page, r, dtype=torch.int16, device=k_cache.device)
+    rc = load().vattn_project_keys(_ptr(k_cache), _kv_dtype(k_cache), _ptr(proj), _ptr(k_lowrank),
+                                   nb, Hkv, d, r, _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_project_keys")
+    return k_lowrank
+
+
+def z_from_delta(delta: float) -> float:
+    return float(load().vattn_z_from_delta(float(delta)))

@@ -1,0 +1,241 @@
+// Host side of the C ABI declared in include/vattn.h: argument validation,
+// the launch plan, the workspace layout and z = Phi^-1(1 - delta/2).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "vattn.h"
+#include "vattn_plan.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kGatherChunk = 4 * vattn::kChunkThreads;  // one Philox quad per thread
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Upper-tail standard normal quantile: z with P(Z > z) = p, 0 < p < 1.
+// Start from the Abramowitz-Stegun 26.2.23 rational approximation and refine
+// with Newton steps on the exact tail 0.5 * erfc(z / sqrt 2).
+double normal_isf(double p) {
+    const bool upper = p <= 0.5;
+    const double pp = upper ? p : 1.0 - p;
+    const double t = std::sqrt(-2.0 * std::log(pp));
+    double z = t - (2.515517 + 0.802853 * t + 0.010328 * t * t) /
+                       (1.0 + 1.432788 * t + 0.189269 * t * t + 0.001308 * t * t * t);
+    const double inv_sqrt2 = 0.70710678118654752440;
+    const double inv_sqrt2pi = 0.39894228040143267794;
+    for (int it = 0; it < 8; ++it) {
+        const double tail = 0.5 * std::erfc(z * inv_sqrt2);
+        const double dens = inv_sqrt2pi * std::exp(-0.5 * z * z);
+        if (!(dens > 0.0)) break;
+        const double step = (tail - pp) / dens;
+        z += step;
+        if (std::fabs(step) <= 1e-17 * std::fabs(z)) break;
+    }
+    return upper ? z : -z;
+}
+
+struct Shape {
+    int G, cp, ncp, kcap, cg, ncg, words;
+};
+
+vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
+    if (!in || !cfg) return VATTN_E_NULL;
+    if (in->B < 1 || in->Hq < 1 || in->Hkv < 1 || in->Hq % in->Hkv != 0) return VATTN_E_SHAPE;
+    const int G = in->Hq / in->Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return VATTN_E_UNSUPPORTED;
+    if (in->d != 64 && in->d != 128) return VATTN_E_UNSUPPORTED;
+    if (in->max_seq_len < 1 || in->max_seq_len > VATTN_MAX_SEQ) return VATTN_E_SHAPE;
+    if (in->max_blocks < 1 || static_cast<long long>(in->max_blocks) * VATTN_PAGE < in->max_seq_len)
+        return VATTN_E_SHAPE;
+    if (in->num_blocks < 1) return VATTN_E_SHAPE;
+    if (static_cast<long long>(in->B) * in->Hkv > 65535) return VATTN_E_SHAPE;
+    if (in->kv_dtype != VATTN_F32 && in->kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (cfg->sinks < 0 || cfg->window < 0 || cfg->topk_abs < -1) return VATTN_E_CFG;
+    if (cfg->topk_ppm < 0 || cfg->topk_ppm > 1000000) return VATTN_E_CFG;
+    if (cfg->base_ppm < 1 || cfg->base_ppm > 1000000) return VATTN_E_CFG;
+    if (cfg->force_budget < -1) return VATTN_E_CFG;
+    if (cfg->predictor != VATTN_PRED_EXACT && cfg->predictor != VATTN_PRED_LOWRANK) return VATTN_E_CFG;
+    if (cfg->predictor == VATTN_PRED_LOWRANK) {
+        if (cfg->rank != 16 && cfg->rank != 32 && cfg->rank != 64) return VATTN_E_UNSUPPORTED;
+        if (cfg->rank > in->d) return VATTN_E_CFG;
+    }
+    if (!(cfg->eps > 0.0) || !std::isfinite(cfg->eps)) return VATTN_E_CFG;
+    if (!(cfg->delta > 0.0 && cfg->delta < 1.0)) return VATTN_E_CFG;
+    if (sh) {
+        sh->G = G;
+        sh->cp = vattn::kPredKeys / G;
+        sh->ncp = (in->max_seq_len + sh->cp - 1) / sh->cp;
+        const long long kmax = cfg->topk_abs >= 0
+                                   ? static_cast<long long>(cfg->topk_abs)
+                                   : (static_cast<long long>(in->max_seq_len) * cfg->topk_ppm + 999999) / 1000000;
+        long long kc = kmax < sh->cp ? kmax : sh->cp;
+        sh->kcap = static_cast<int>(kc < 1 ? 1 : kc);
+        sh->cg = kGatherChunk;
+        sh->ncg = (in->max_seq_len + sh->cg - 1) / sh->cg;
+        sh->words = (in->max_seq_len + 31) / 32;
+    }
+    return VATTN_OK;
+}
+
+struct Layout {
+    size_t cand, bits, hs, sc, cmax, part, total;
+};
+
+Layout layout(const vattn_inputs* in, const Shape& s) {
+    const size_t BHq = static_cast<size_t>(in->B) * in->Hq;
+    const size_t BHkv = static_cast<size_t>(in->B) * in->Hkv;
+    Layout L{};
+    size_t off = 0;
+    L.cand = off;
+    off += align_up(BHq * s.ncp * s.kcap * sizeof(uint64_t));
+    L.bits = off;
+    off += align_up(BHq * s.words * sizeof(uint32_t));
+    L.hs = off;
+    off += align_up(BHq * sizeof(vattn::HeadState));
+    L.sc = off;
+    off += align_up(BHkv * static_cast<size_t>(in->max_seq_len) * s.G * sizeof(float));
+    L.cmax = off;
+    off += align_up(BHq * s.ncg * sizeof(float));
+    L.part = off;
+    off += align_up(BHq * s.ncg * static_cast<size_t>(in->d + 2) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+double vattn_z_from_delta(double delta) {
+    if (!(delta > 0.0 && delta < 1.0)) return NAN;
+    return static_cast<double>(static_cast<float>(normal_isf(delta / 2.0)));
+}
+
+size_t vattn_workspace_size(const vattn_inputs* in, const vattn_cfg* cfg) {
+    Shape s{};
+    if (check(in, cfg, &s) != VATTN_OK) return 0;
+    return layout(in, s).total;
+}
+
+static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
+                                void* workspace, size_t ws_bytes, void* hip_stream,
+                                void* const* events) {
+    Shape s{};
+    vattn_status st = check(in, cfg, &s);
+    if (st != VATTN_OK) return st;
+    if (!out || !out->out || !out->lse) return VATTN_E_NULL;
+    if (!in->q || !in->k_cache || !in->v_cache || !in->block_table || !in->seq_lens) return VATTN_E_NULL;
+    if (cfg->predictor == VATTN_PRED_LOWRANK && (!in->k_lowrank || !in->proj)) return VATTN_E_NULL;
+    if (!aligned(in->q, 16) || !aligned(in->k_cache, 16) || !aligned(in->v_cache, 16) ||
+        (in->k_lowrank && !aligned(in->k_lowrank, 16)) || (in->proj && !aligned(in->proj, 4)))
+        return VATTN_E_SHAPE;
+    if (out->idx && out->idx_cap < in->max_seq_len) return VATTN_E_SHAPE;
+    const Layout L = layout(in, s);
+    if (!workspace || !aligned(workspace, kAlign) || ws_bytes < L.total) return VATTN_E_WORKSPACE;
+
+    vattn::Plan p{};
+    p.B = in->B;
+    p.Hq = in->Hq;
+    p.Hkv = in->Hkv;
+    p.G = s.G;
+    p.d = in->d;
+    p.r = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+    p.max_blocks = in->max_blocks;
+    p.max_seq_len = in->max_seq_len;
+    p.words = s.words;
+    p.sinks = cfg->sinks;
+    p.window = cfg->window;
+    p.topk_abs = cfg->topk_abs;
+    p.topk_ppm = cfg->topk_ppm;
+    p.base_ppm = cfg->base_ppm;
+    p.force_budget = cfg->force_budget;
+    p.predictor = cfg->predictor;
+    p.kv_bf16 = in->kv_dtype == VATTN_BF16;
+    p.scale32 = static_cast<float>(1.0 / std::sqrt(static_cast<double>(in->d)));
+    p.z32 = vattn_z_from_delta(cfg->delta);
+    p.eps = cfg->eps;
+    p.seed_lo = static_cast<uint32_t>(cfg->seed);
+    p.seed_hi = static_cast<uint32_t>(cfg->seed >> 32);
+    p.cp = s.cp;
+    p.ncp = s.ncp;
+    p.kcap = s.kcap;
+    p.cg = s.cg;
+    p.ncg = s.ncg;
+    p.q = in->q;
+    p.k = in->k_cache;
+    p.v = in->v_cache;
+    p.kt = in->k_lowrank;
+    p.proj = in->proj;
+    p.bt = in->block_table;
+    p.seq_lens = in->seq_lens;
+    char* ws = static_cast<char*>(workspace);
+    p.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+    p.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+    p.hs = reinterpret_cast<vattn::HeadState*>(ws + L.hs);
+    p.sc = reinterpret_cast<float*>(ws + L.sc);
+    p.cmax = reinterpret_cast<float*>(ws + L.cmax);
+    p.part = reinterpret_cast<float*>(ws + L.part);
+    p.out = out->out;
+    p.lse = out->lse;
+    p.idx = out->idx;
+    p.idx_cap = out->idx_cap;
+    p.counts = out->counts;
+    p.stats = out->stats;
+    p.gcounts = out->group_counts;
+    out->z_used = p.z32;
+    const int rc = vattn::launch_decode(p, hip_stream, events);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
+vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
+                          void* workspace, size_t ws_bytes, void* hip_stream) {
+    return decode_impl(in, cfg, out, workspace, ws_bytes, hip_stream, nullptr);
+}
+
+vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
+                                   vattn_outputs* out, void* workspace, size_t ws_bytes,
+                                   void* hip_stream, void* const* events, int32_t n_events) {
+    if (!events) return VATTN_E_NULL;
+    if (n_events != VATTN_NUM_STAGES + 1) return VATTN_E_SHAPE;
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return VATTN_E_NULL;
+    return decode_impl(in, cfg, out, workspace, ws_bytes, hip_stream, events);
+}
+
+vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const float* proj,
+                                uint16_t* k_lowrank, int32_t num_blocks, int32_t Hkv, int32_t d,
+                                int32_t r, void* hip_stream) {
+    if (!k_cache || !proj || !k_lowrank) return VATTN_E_NULL;
+    if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
+    if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
+    if (r != 16 && r != 32 && r != 64) return VATTN_E_UNSUPPORTED;
+    if (r > d) return VATTN_E_SHAPE;
+    const long long rows = static_cast<long long>(num_blocks) * Hkv * VATTN_PAGE;
+    if ((rows + 3) / 4 > 0x7FFFFFFFLL) return VATTN_E_SHAPE;
+    const int rc = vattn::launch_project(k_cache, kv_dtype == VATTN_BF16, proj, k_lowrank, num_blocks, Hkv,
+                                         d, r, hip_stream);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
+const char* vattn_status_string(vattn_status s) {
+    switch (s) {
+        case VATTN_OK: return "VATTN_OK";
+        case VATTN_E_NULL: return "VATTN_E_NULL: a required pointer is NULL";
+        case VATTN_E_SHAPE: return "VATTN_E_SHAPE: a size or alignment is outside the supported range";
+        case VATTN_E_DTYPE: return "VATTN_E_DTYPE: unknown kv dtype";
+        case VATTN_E_CFG: return "VATTN_E_CFG: a configuration field is out of range";
+        case VATTN_E_WORKSPACE: return "VATTN_E_WORKSPACE: workspace NULL, misaligned or too small";
+        case VATTN_E_UNSUPPORTED: return "VATTN_E_UNSUPPORTED: combination not implemented";
+        case VATTN_E_HIP: return "VATTN_E_HIP: a HIP launch failed";
+    }
+    return "unknown vattn_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal launch plan shared by the host C ABI and the kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vattn {
+
+constexpr int kPage = 16;
+constexpr int kPredThreads = 1024;   // predictor + chunk top-k
+constexpr int kGroupThreads = 1024;  // per-(b, KV head) selection / budget
+constexpr int kChunkThreads = 256;   // base scores and gather
+constexpr int kEmitThreads = 1024;   // index-set emission
+constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
+
+// Per (sequence, query head) state handed from kernel to kernel.
+struct HeadState {
+    int32_t L, k, n_fixed, NT, nb, n, flags, pad;
+    uint64_t thr_b;  // base sample  = tail tokens with sample key >= thr_b (nb > 0)
+    uint64_t thr_n;  // final sample = tail tokens with sample key >= thr_n (n > 0)
+    float m;         // max pinned score over I_f and the base sample
+    float wsamp;     // N_t / n as fp32
+    uint64_t SF, S1, S2hi, S2lo;
+};
+
+struct Plan {
+    // shapes
+    int B, Hq, Hkv, G, d, r, max_blocks, max_seq_len, words;
+    // configuration
+    int sinks, window, topk_abs, topk_ppm, base_ppm, force_budget, predictor, kv_bf16;
+    float scale32;
+    double z32, eps;
+    uint32_t seed_lo, seed_hi;
+    // chunking
+    int cp, ncp, kcap;  // predictor chunk (tokens), chunks per sequence, candidate slots
+    int cg, ncg;        // gather chunk (tokens), chunks per sequence
+    // inputs
+    const float* q;
+    const void* k;
+    const void* v;
+    const uint16_t* kt;
+    const float* proj;
+    const int32_t* bt;
+    const int32_t* seq_lens;
+    // workspace
+    uint64_t* cand;  // [B*Hq][ncp][kcap] composite (score key, ~index)
+    uint32_t* bits;  // [B*Hq][words] fixed-set membership bitmap
+    HeadState* hs;   // [B*Hq]
+    float* sc;       // [B*Hkv][max_seq_len][G] pinned exact scores (base-sample union)
+    float* cmax;     // [B*Hq][ncg] chunk max of pinned scores
+    float* part;     // [B*Hq][ncg][d + 2] online-softmax partials (m, l, acc[d])
+    // outputs
+    float* out;
+    float* lse;
+    int32_t* idx;
+    int32_t idx_cap;
+    int32_t* counts;
+    uint64_t* stats;
+    int32_t* gcounts;  // [B*Hkv][2] optional
+};
+
+// Launches one decode step.  Returns 0 or a hipError_t value.
+int launch_decode(const Plan& p, void* stream, void* const* events = nullptr);
+int launch_project(const void* k_cache, int kv_bf16, const float* proj, uint16_t* kt,
+                   int num_blocks, int Hkv, int d, int r, void* stream);
+size_t predict_lds_bytes(int G, int d, int row, int cp);
+
+}  // namespace vattn
