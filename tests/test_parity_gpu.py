@@ -85,6 +85,10 @@ SMALL_CASES = {
         name="flat_small", B=1, Hq=8, Hkv=2, d=128, seq_lens=(6000,), kv_dtype="bf16",
         recipe="flat", q_std=0.3, k_std=0.3, predictor=1, rank=32, sinks=128, window=128,
         topk_ppm=10000, eps=0.02, data_seed=16),
+    "flat_crowded_bucket": lambda: synthetic.make(
+        name="flat_crowded_bucket", B=1, Hq=8, Hkv=2, d=128, seq_lens=(20000,), kv_dtype="bf16",
+        recipe="flat", q_std=0.3, k_std=0.3, predictor=1, rank=32, sinks=16, window=16,
+        topk_ppm=25000, eps=0.02, data_seed=18),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,

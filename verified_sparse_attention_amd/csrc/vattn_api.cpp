@@ -12,7 +12,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kGatherChunk = 4 * vattn::kChunkThreads;  // one Philox quad per thread
+static_assert(VATTN_MAX_SEQ == VATTN_MAX_SEQ_TOKENS, "sequence bound differs from the kernels'");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -69,14 +69,27 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
     if (!(cfg->delta > 0.0 && cfg->delta < 1.0)) return VATTN_E_CFG;
     if (sh) {
         sh->G = G;
-        sh->cp = vattn::kPredKeys / G;
+        // Predictor chunk: the keys of G heads stay in LDS (at most kPredKeys
+        // and within the workgroup LDS limit).  Below that bound, aim for one
+        // chunk per compute unit over the whole batch, but keep chunks of at
+        // least 2048 tokens so the chunk top-k stays a small fraction of them.
+        const int prow = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+        int cpmax = vattn::kPredKeys / G;
+        while (cpmax > vattn::kPage &&
+               vattn::predict_lds_bytes(G, in->d, prow, cpmax) > static_cast<size_t>(vattn::kMaxLds))
+            cpmax -= vattn::kPage;
+        const long long spread = (static_cast<long long>(in->max_seq_len) * in->B * in->Hkv + 255) / 256;
+        long long cp = (spread + vattn::kPage - 1) / vattn::kPage * vattn::kPage;
+        if (cp < 2048) cp = 2048;
+        if (cp > cpmax) cp = cpmax;
+        sh->cp = static_cast<int>(cp);
         sh->ncp = (in->max_seq_len + sh->cp - 1) / sh->cp;
         const long long kmax = cfg->topk_abs >= 0
                                    ? static_cast<long long>(cfg->topk_abs)
                                    : (static_cast<long long>(in->max_seq_len) * cfg->topk_ppm + 999999) / 1000000;
         long long kc = kmax < sh->cp ? kmax : sh->cp;
         sh->kcap = static_cast<int>(kc < 1 ? 1 : kc);
-        sh->cg = kGatherChunk;
+        sh->cg = vattn::kGatherChunk;
         sh->ncg = (in->max_seq_len + sh->cg - 1) / sh->cg;
         sh->words = (in->max_seq_len + 31) / 32;
     }
@@ -84,7 +97,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, total;
+    size_t cand, bits, hs, sc, cmax, part, shist, hh, btok, bmeta, bcnt, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -104,6 +117,16 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHq * s.ncg * sizeof(float));
     L.part = off;
     off += align_up(BHq * s.ncg * static_cast<size_t>(in->d + 2) * sizeof(float));
+    L.shist = off;
+    off += align_up(BHkv * s.ncp * vattn::kSampBins * sizeof(uint32_t));
+    L.hh = off;
+    off += align_up(BHq * vattn::kSampBins * sizeof(uint32_t));
+    L.btok = off;
+    off += align_up(BHkv * s.ncg * s.cg * sizeof(int32_t));
+    L.bmeta = off;
+    off += align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t));
+    L.bcnt = off;
+    off += align_up(BHkv * s.ncg * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -138,6 +161,9 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     if (out->idx && out->idx_cap < in->max_seq_len) return VATTN_E_SHAPE;
     const Layout L = layout(in, s);
     if (!workspace || !aligned(workspace, kAlign) || ws_bytes < L.total) return VATTN_E_WORKSPACE;
+    const int prow = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+    if (vattn::predict_lds_bytes(s.G, in->d, prow, s.cp) > static_cast<size_t>(vattn::kMaxLds))
+        return VATTN_E_UNSUPPORTED;  // unreachable: the chunk is sized to fit
 
     vattn::Plan p{};
     p.B = in->B;
@@ -181,6 +207,11 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.sc = reinterpret_cast<float*>(ws + L.sc);
     p.cmax = reinterpret_cast<float*>(ws + L.cmax);
     p.part = reinterpret_cast<float*>(ws + L.part);
+    p.shist = reinterpret_cast<uint32_t*>(ws + L.shist);
+    p.hh = reinterpret_cast<uint32_t*>(ws + L.hh);
+    p.btok = reinterpret_cast<int32_t*>(ws + L.btok);
+    p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);
+    p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.out = out->out;
     p.lse = out->lse;
     p.idx = out->idx;

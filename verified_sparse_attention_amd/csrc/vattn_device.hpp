@@ -252,8 +252,12 @@ struct SelShared {
     uint32_t active;
 };
 
+// With `exact`, thr[h] is raised to the smallest selected key itself: needed
+// when `items` enumerates only part of a larger population (one bucket of it),
+// where a prefix threshold could also admit keys that were never visited.
 template <int NH, class Items>
-__device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items&& items) {
+__device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items&& items,
+                             bool exact = false) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     if (tid == 0) {
@@ -320,6 +324,324 @@ __device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items
                 }
             }
         }
+        __syncthreads();
+    }
+    if (exact) {
+        uint64_t lo_thr[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) lo_thr[h] = S.thr[h];
+        __syncthreads();
+        if (tid < NH) S.thr[tid] = ~0ull;
+        __syncthreads();
+        items([&](int h, uint64_t key) {
+            if (want[h] > 0 && key >= lo_thr[h]) atomicMin(&S.thr[h], key);
+        });
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wavefront finds the bin holding the rank-th element (1-based) when the
+// NBINS bins are visited in ascending order, or descending when `desc`.
+// bin_out = -1 when the histogram holds fewer than `rank` elements.
+// ---------------------------------------------------------------------------
+template <int NBINS>
+__device__ __forceinline__ void wave_rank_bin(const uint32_t* hist, uint32_t rank, bool desc,
+                                              int& bin_out, uint32_t& before_out) {
+    constexpr int PER = NBINS / 64;
+    const int lane = threadIdx.x & 63;
+    uint32_t c[PER];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int pos = lane * PER + e;
+        c[e] = hist[desc ? NBINS - 1 - pos : pos];
+        sum += c[e];
+    }
+    const uint32_t inc = wave_incl_scan(sum);
+    const unsigned long long ball = __ballot(inc >= rank);
+    if (ball == 0ull) {
+        bin_out = -1;
+        before_out = 0;
+        return;
+    }
+    const int owner = __ffsll(static_cast<long long>(ball)) - 1;
+    int bin = -1;
+    uint32_t before = 0;
+    if (lane == owner) {
+        uint32_t acc = inc - sum;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            if (bin < 0 && acc + c[e] >= rank) {
+                const int pos = lane * PER + e;
+                bin = desc ? NBINS - 1 - pos : pos;
+                before = acc;
+            }
+            acc += c[e];
+        }
+    }
+    bin_out = __shfl(bin, owner, 64);
+    before_out = __shfl(before, owner, 64);
+}
+
+// Element x of list[0, n) is the r-th largest (1-based) iff exactly r - 1
+// elements exceed it (keys are unique).  One thread per element.
+__device__ __forceinline__ void list_rank_pick(const uint64_t* list, int n, uint32_t r, int x,
+                                               uint64_t* out) {
+    if (x >= n) return;
+    const uint64_t v = list[x];
+    uint32_t above = 0;
+    for (int y = 0; y < n; ++y) above += list[y] > v ? 1u : 0u;
+    if (above + 1 == r) *out = v;
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exact top-k threshold for NH heads at once, without contended
+// atomics: (A) range of the order keys, (B) histogram over kTopBuckets
+// value-range buckets (a monotone map of the key, so bucket order is key
+// order), (C) the boundary bucket's keys listed and ranked exactly.  Only a
+// boundary bucket larger than kListCap falls back to the radix select.
+// items(f) calls f(h, okey, index) for every key of head h on this thread.
+// Result: thr[h] with exactly want[h] keys topk_key(okey, index) >= thr[h]
+// (thr 0 when want >= total; unused when want == 0).
+// ---------------------------------------------------------------------------
+template <int NH>
+struct TopkShared {
+    SelShared<NH> S;  // S.hist doubles as the bucket histogram
+    uint64_t list[NH][kListCap];
+    uint64_t thr[NH];
+    uint32_t lo[NH], hi[NH], above[NH], cnt[NH], aux[NH];
+    float vmin[NH], scale[NH];
+    int bstar[NH];
+};
+
+// Score back from its order key.
+__device__ __forceinline__ float okey_value(uint32_t ok) {
+    return __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
+}
+
+// Bucket linear in the score: (s - s_min) * 256 / (s_max - s_min), clamped.
+// Each step (fp32 subtract, multiply by a positive constant, truncate) is
+// monotone non-decreasing, so bucket order never contradicts key order.
+__device__ __forceinline__ int topk_bucket(uint32_t ok, float vmin, float scale) {
+    const int bk = static_cast<int>((okey_value(ok) - vmin) * scale);
+    return bk < kTopBuckets - 1 ? bk : kTopBuckets - 1;
+}
+
+template <int NH, class Items>
+__device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
+                           Items&& items) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+    bool act[NH];
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        act[h] = want[h] > 0 && want[h] < total[h];
+        any |= act[h];
+    }
+    if (tid < NH) {
+        T.lo[tid] = 0xFFFFFFFFu;
+        T.hi[tid] = 0;
+        T.cnt[tid] = 0;
+        T.thr[tid] = 0;
+        T.bstar[tid] = -1;
+        T.above[tid] = 0;
+    }
+    for (int x = tid; x < NH * kTopBuckets; x += nthr) (&T.S.hist[0][0])[x] = 0;
+    __syncthreads();
+    if (!any) return;
+    // (A) key range per head
+    uint32_t lo[NH], hi[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        lo[h] = 0xFFFFFFFFu;
+        hi[h] = 0;
+    }
+    items([&](int h, uint32_t ok, uint32_t) {
+        lo[h] = min(lo[h], ok);
+        hi[h] = max(hi[h], ok);
+    });
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        uint32_t a = lo[h], b = hi[h];
+        for (int o = 1; o < 64; o <<= 1) {
+            a = min(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
+            b = max(b, static_cast<uint32_t>(__shfl_xor(b, o, 64)));
+        }
+        if (lane == 0 && act[h]) {
+            atomicMin(&T.lo[h], a);
+            atomicMax(&T.hi[h], b);
+        }
+    }
+    __syncthreads();
+    if (tid < NH) {
+        const float vmin = okey_value(T.lo[tid]), vmax = okey_value(T.hi[tid]);
+        const float range = vmax - vmin;
+        const float scale = static_cast<float>(kTopBuckets) / range;
+        // a zero or non-finite range puts every key in bucket 0
+        const bool ok = range > 0.0f && range < __builtin_inff() && scale < __builtin_inff();
+        T.vmin[tid] = vmin;
+        T.scale[tid] = ok ? scale : 0.0f;
+    }
+    __syncthreads();
+    float vm[NH], sc[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        vm[h] = T.vmin[h];
+        sc[h] = T.scale[h];
+    }
+    // (B) bucket histogram
+    items([&](int h, uint32_t ok, uint32_t) {
+        if (act[h]) atomicAdd(&T.S.hist[h][topk_bucket(ok, vm[h], sc[h])], 1u);
+    });
+    __syncthreads();
+    for (int h = wave; h < NH; h += nwaves) {
+        if (!act[h]) continue;
+        int bin;
+        uint32_t before;
+        wave_rank_bin<kTopBuckets>(T.S.hist[h], want[h], true, bin, before);
+        if (lane == 0) {
+            T.bstar[h] = bin;
+            T.above[h] = before;
+        }
+    }
+    __syncthreads();
+    int bs[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) bs[h] = T.bstar[h];
+    // (C) boundary bucket list
+    items([&](int h, uint32_t ok, uint32_t idx) {
+        if (act[h] && topk_bucket(ok, vm[h], sc[h]) == bs[h]) {
+            const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
+            if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
+        }
+    });
+    __syncthreads();
+    uint32_t fmask = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+        if (act[h] && bs[h] >= 0 && T.cnt[h] > static_cast<uint32_t>(kListCap)) fmask |= 1u << h;
+    for (int x = tid; x < NH * kListCap; x += nthr) {
+        const int h = x / kListCap, e = x - h * kListCap;
+        if (act[h] && bs[h] >= 0 && !((fmask >> h) & 1u))
+            list_rank_pick(T.list[h], static_cast<int>(T.cnt[h]), want[h] - T.above[h], e, &T.thr[h]);
+    }
+    __syncthreads();
+    if (fmask) {  // rare: a crowded boundary bucket, ranked by the radix select
+        uint32_t fw[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? want[h] - T.above[h] : 0u;
+        block_select<NH>(T.S, fw, [&](auto&& visit) {
+            items([&](int h, uint32_t ok, uint32_t idx) {
+                if (((fmask >> h) & 1u) && topk_bucket(ok, vm[h], sc[h]) == bs[h]) visit(h, topk_key(ok, idx));
+            });
+        }, true);
+        if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = T.S.thr[tid];
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sampler thresholds from the histogram of the Philox words' top kSampBits.
+// hist[h] holds the tail histogram of head h.  For rank[h] > 0 the result
+// thr[h] = sample_key of the rank-th smallest (word, index) of the tail, so
+// the first rank[h] tail tokens of the sample order are exactly those with
+// sample_key >= thr[h].  One Philox pass over the middle collects the tokens
+// of the boundary bin; `in_fixed(h, i)` tells whether token i is in head h's
+// fixed set (those are not in the tail).
+// ---------------------------------------------------------------------------
+template <int NH>
+struct SampShared {
+    uint32_t hist[NH][kSampBins];
+    uint64_t list[NH][kListCap];
+    uint64_t thr[NH];
+    uint32_t before[NH], cnt[NH];
+    int bin[NH];
+};
+
+template <int NH, class InFixed>
+__device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions& R, int b, int g,
+                                       uint32_t seed_lo, uint32_t seed_hi, const uint32_t (&rank)[NH],
+                                       InFixed&& in_fixed) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+    constexpr int kShift = 32 - kSampBits;
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) any |= rank[h] > 0;
+    if (tid < NH) {
+        S.cnt[tid] = 0;
+        S.thr[tid] = 0;
+    }
+    if (!any) {
+        __syncthreads();
+        return;
+    }
+    for (int h = wave; h < NH; h += nwaves) {
+        if (rank[h] == 0) continue;
+        int bin;
+        uint32_t before;
+        wave_rank_bin<kSampBins>(S.hist[h], rank[h], false, bin, before);
+        if (lane == 0) {
+            S.bin[h] = bin;
+            S.before[h] = before;
+        }
+    }
+    __syncthreads();
+    int bn[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) bn[h] = rank[h] > 0 ? S.bin[h] : -1;
+    const int q0 = R.lo >> 2, q1 = (R.hi - 1) >> 2;
+    for (int qd = q0 + tid; qd <= q1; qd += nthr) {
+        const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, seed_lo, seed_hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * qd + e;
+            if (i < R.lo || i >= R.hi) continue;
+            const uint32_t u = word_of(w, e);
+            const int bi = static_cast<int>(u >> kShift);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                if (bi == bn[h] && !in_fixed(h, i)) {
+                    const uint32_t pos = atomicAdd(&S.cnt[h], 1u);
+                    if (pos < static_cast<uint32_t>(kListCap)) S.list[h][pos] = sample_key(u, static_cast<uint32_t>(i));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t fmask = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+        if (bn[h] >= 0 && S.cnt[h] > static_cast<uint32_t>(kListCap)) fmask |= 1u << h;
+    for (int x = tid; x < NH * kListCap; x += nthr) {
+        const int h = x / kListCap, e = x - h * kListCap;
+        if (bn[h] >= 0 && !((fmask >> h) & 1u))
+            list_rank_pick(S.list[h], static_cast<int>(S.cnt[h]), rank[h] - S.before[h], e, &S.thr[h]);
+    }
+    __syncthreads();
+    if (fmask) {  // rare: a crowded bin, ranked by the radix select over its tokens
+        uint32_t fw[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? rank[h] - S.before[h] : 0u;
+        block_select<NH>(F, fw, [&](auto&& visit) {
+            for (int qd = q0 + tid; qd <= q1; qd += nthr) {
+                const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, seed_lo, seed_hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * qd + e;
+                    if (i < R.lo || i >= R.hi) continue;
+                    const uint32_t u = word_of(w, e);
+                    const int bi = static_cast<int>(u >> kShift);
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        if (((fmask >> h) & 1u) && bi == bn[h] && !in_fixed(h, i))
+                            visit(h, sample_key(u, static_cast<uint32_t>(i)));
+                }
+            }
+        }, true);
+        if (tid < NH && ((fmask >> tid) & 1u)) S.thr[tid] = F.thr[tid];
         __syncthreads();
     }
 }

@@ -1,17 +1,18 @@
 // gfx950 kernels of the verified sparse-attention decode step.
 //
-// Pipeline for one step (one workgroup grid each, all on the caller's stream):
-//   predict  (chunk, b*Hkv)  stream predictor keys of one context chunk, score
-//                            the G query heads of the KV group, keep the chunk's
-//                            top-k candidates per head (radix select in LDS)
-//   select   (b*Hkv)         merge candidates into the exact top-k, write the
-//                            fixed-set bitmap (sinks, window, top-k), pick the
-//                            base sample threshold in the Philox order
-//   base     (chunk, b*Hkv)  pinned exact scores of every token in the union of
-//                            the group's fixed sets and base samples -> score
-//                            cache; chunk maxima
-//   budget   (b*Hkv)         exact fixed-point denominator statistics, CLT
-//                            budget, final sample threshold
+// Pipeline for one step (all on the caller's stream):
+//   predict  (chunk, b*Hkv)  stream the predictor keys of one context chunk,
+//                            score the G query heads of the KV group, keep the
+//                            chunk's top-k candidates per head; histogram of the
+//                            chunk's sample words
+//   select   (b*Hkv)         exact top-k from the candidates, fixed-set bitmap
+//                            (sinks, window, top-k), per-head tail histograms,
+//                            base-sample threshold in the sample order
+//   base     (chunk, b*Hkv)  pinned exact scores of the union of the group's
+//                            fixed sets and base samples -> score cache, chunk
+//                            maxima, member lists
+//   budget   (b*Hkv)         exact fixed-point denominator statistics from the
+//                            member lists, CLT budget, final-sample threshold
 //   gather   (chunk, b*Hkv)  one pass over the union of the group's index sets:
 //                            K row (unless its score is cached) and V row per
 //                            token, weighted online softmax for each member head
@@ -31,6 +32,8 @@
 
 namespace vattn {
 
+constexpr int kUnroll = 4;  // token rows in flight per lane group in the streaming loops
+
 __device__ __forceinline__ bool bit_of(const uint32_t* row, int i) {
     return (row[i >> 5] >> (i & 31)) & 1u;
 }
@@ -42,37 +45,45 @@ __device__ __forceinline__ bool bit_of_coherent(const uint32_t* row, int i) {
     return (w >> (i & 31)) & 1u;
 }
 
-__device__ __forceinline__ const void* row_ptr(const void* base, size_t esize, int page, int Hkv,
-                                               int g, int slot, int width) {
-    const size_t off = ((static_cast<size_t>(page) * Hkv + g) * kPage + slot) * static_cast<size_t>(width);
-    return static_cast<const char*>(base) + off * esize;
+__device__ __forceinline__ size_t row_index(int page, int Hkv, int g, int slot, int width) {
+    return ((static_cast<size_t>(page) * Hkv + g) * kPage + slot) * static_cast<size_t>(width);
 }
 
+__device__ __forceinline__ uint32_t token_word(const Plan& P, int b, int g, int i) {
+    const uint4 w = philox4x32_10(static_cast<uint32_t>(i >> 2), g, b, 0, P.seed_lo, P.seed_hi);
+    return word_of(w, i & 3);
+}
+
+__host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
+
 // ===========================================================================
-// predict: chunk-local top-k candidates
+// predict: chunk-local top-k candidates and the chunk's sample-word histogram
 // ===========================================================================
 size_t predict_lds_bytes(int G, int d, int row, int cp) {
-    size_t sel = 0;
+    size_t ts = 0;
     switch (G) {
-        case 1: sel = sizeof(SelShared<1>); break;
-        case 2: sel = sizeof(SelShared<2>); break;
-        case 4: sel = sizeof(SelShared<4>); break;
-        default: sel = sizeof(SelShared<8>); break;
+        case 1: ts = sizeof(TopkShared<1>); break;
+        case 2: ts = sizeof(TopkShared<2>); break;
+        case 4: ts = sizeof(TopkShared<4>); break;
+        default: ts = sizeof(TopkShared<8>); break;
     }
-    sel = (sel + 15) & ~static_cast<size_t>(15);
-    return sel + sizeof(float) * (static_cast<size_t>(G) * d + static_cast<size_t>(G) * row) +
-           sizeof(uint32_t) * (static_cast<size_t>(G) * cp + 8);
+    return align16(ts) + sizeof(uint32_t) * kSampBins + sizeof(int32_t) * (cp / kPage + 2) +
+           sizeof(float) * (static_cast<size_t>(G) * d + static_cast<size_t>(G) * row) +
+           sizeof(uint32_t) * static_cast<size_t>(G) * cp;
 }
 
 template <int ROW, typename T, int G>
 __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     extern __shared__ __align__(16) unsigned char smem[];
-    SelShared<G>& S = *reinterpret_cast<SelShared<G>*>(smem);
-    const size_t sel = (sizeof(SelShared<G>) + 15) & ~static_cast<size_t>(15);
-    float* qs = reinterpret_cast<float*>(smem + sel);  // [G][d]
+    TopkShared<G>& TS = *reinterpret_cast<TopkShared<G>*>(smem);
+    size_t off = align16(sizeof(TopkShared<G>));
+    uint32_t* shist = reinterpret_cast<uint32_t*>(smem + off);
+    off += sizeof(uint32_t) * kSampBins;
+    int32_t* pages = reinterpret_cast<int32_t*>(smem + off);  // the chunk's page ids
+    off += sizeof(int32_t) * (P.cp / kPage + 2);
+    float* qs = reinterpret_cast<float*>(smem + off);  // [G][d]
     float* qv = qs + G * P.d;                           // [G][ROW]
     uint32_t* keys = reinterpret_cast<uint32_t*>(qv + G * ROW);  // [G][cp]
-    uint32_t* wcnt = keys + G * P.cp;                            // [G] output counters
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -80,85 +91,114 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
     const int t0 = max(c * P.cp, R.lo), t1 = min((c + 1) * P.cp, R.hi);
-    if (t0 >= t1 || R.k == 0) return;
-    const int kp = min(R.k, t1 - t0);
+    if (t0 >= t1) return;
     const int d = P.d;
 
-    // 1) query vectors: q_s = fl32(q * fl32(1/sqrt(d))); low-rank q~ = pdot(q_s, P[:, j])
-    for (int x = tid; x < G * d; x += nthr) {
-        const int h = x / d, cc = x - h * d;
-        qs[x] = P.q[(static_cast<size_t>(b) * P.Hq + g * G + h) * d + cc] * P.scale32;
-    }
-    if (tid < G) wcnt[tid] = 0;
-    __syncthreads();
-    if (P.predictor == 1) {
-        for (int x = tid; x < G * ROW; x += nthr) {
-            const int h = x / ROW, j = x - h * ROW;
-            qv[x] = (d == 128) ? pdot_serial<128>(qs + h * d, 1, P.proj + j, ROW)
-                               : pdot_serial<64>(qs + h * d, 1, P.proj + j, ROW);
-        }
-    } else {
-        for (int x = tid; x < G * ROW; x += nthr) qv[x] = qs[x];
-    }
-    __syncthreads();
-
-    // 2) scores: LPT lanes per token row, 8 elements per lane
-    constexpr int LPT = ROW / 8, TPW = 64 / LPT;
-    const int j = lane % LPT, slot = lane / LPT;
-    float qreg[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[h][e] = qv[h * ROW + 8 * j + e];
-    const T* src = static_cast<const T*>(P.predictor == 1 ? static_cast<const void*>(P.kt) : P.k);
+    // sample-word histogram of the chunk's middle tokens (the top-k tokens are
+    // taken out per head once they are known)
     const int tb = (t0 / kPage) * kPage;
     const int ntok = ((t1 - 1) / kPage + 1) * kPage - tb;
-    const int cbase = c * P.cp;
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
-    for (int base = wave * TPW; base < ntok; base += nwaves * TPW) {
-        // rows past the chunk's last page (TPW > 16) reread the last row and are not stored
-        const int t = tb + min(base + slot, ntok - 1);
-        const int page = btrow[t / kPage];
-        const T* rowp = static_cast<const T*>(row_ptr(src, sizeof(T), page, P.Hkv, g, t % kPage, ROW)) + 8 * j;
-        float kf[8];
-        load8(rowp, kf);
+    for (int x = tid; x < kSampBins; x += nthr) shist[x] = 0;
+    for (int x = tid; x < ntok / kPage; x += nthr) pages[x] = btrow[tb / kPage + x];
+    __syncthreads();
+    for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
+        const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float s = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-            if (j == 0 && t >= t0 && t < t1) keys[h * P.cp + (t - cbase)] = okey(s);
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * qd + e;
+            if (i >= t0 && i < t1) atomicAdd(&shist[word_of(w, e) >> (32 - kSampBits)], 1u);
         }
     }
-    __syncthreads();
 
-    // 3) chunk top-kp per head
-    uint32_t want[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) want[h] = static_cast<uint32_t>(kp);
-    block_select<G>(S, want, [&](auto&& visit) {
-        for (int t = t0 + tid; t < t1; t += nthr)
-#pragma unroll
-            for (int h = 0; h < G; ++h) visit(h, topk_key(keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t)));
-    });
+    if (R.k > 0) {
+        // 1) query vectors: q_s = fl32(q * fl32(1/sqrt(d))); low-rank q~ = pdot(q_s, P[:, j])
+        for (int x = tid; x < G * d; x += nthr) {
+            const int h = x / d, cc = x - h * d;
+            qs[x] = P.q[(static_cast<size_t>(b) * P.Hq + g * G + h) * d + cc] * P.scale32;
+        }
+        __syncthreads();
+        if (P.predictor == 1) {
+            for (int x = tid; x < G * ROW; x += nthr) {
+                const int h = x / ROW, j = x - h * ROW;
+                qv[x] = (d == 128) ? pdot_serial<128>(qs + h * d, 1, P.proj + j, ROW)
+                                   : pdot_serial<64>(qs + h * d, 1, P.proj + j, ROW);
+            }
+        } else {
+            for (int x = tid; x < G * ROW; x += nthr) qv[x] = qs[x];
+        }
+        __syncthreads();
 
-    // 4) write the kp candidates of each head (any order)
-    uint64_t thr[G];
+        // 2) scores: LPT lanes per token row, 8 elements per lane, kUnroll rows in flight
+        constexpr int LPT = ROW / 8, TPW = 64 / LPT;
+        const int j = lane % LPT, slot = lane / LPT;
+        float qreg[G][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) thr[h] = S.thr[h];
-    for (int t = t0 + tid; t < t1; t += nthr) {
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qreg[h][e] = qv[h * ROW + 8 * j + e];
+        const T* src = static_cast<const T*>(P.predictor == 1 ? static_cast<const void*>(P.kt) : P.k);
+        const int cbase = c * P.cp;
+        for (int base = wave * TPW * kUnroll; base < ntok; base += nwaves * TPW * kUnroll) {
+            float kf[kUnroll][8];
+            int tt[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                // rows past the chunk's last page reread its last row and are not stored
+                const int tl = min(base + u * TPW + slot, ntok - 1);
+                tt[u] = tb + tl;
+                load8(src + row_index(pages[tl / kPage], P.Hkv, g, tt[u] % kPage, ROW) + 8 * j, kf[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float s = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
+                    if (j == 0 && tt[u] >= t0 && tt[u] < t1) keys[h * P.cp + (tt[u] - cbase)] = okey(s);
+                }
+            }
+        }
+        __syncthreads();
+
+        // 3) chunk top-kp per head
+        const int kp = min(R.k, t1 - t0);
+        uint32_t want[G], total[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const uint64_t key = topk_key(keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
-            if (key >= thr[h]) {
-                const uint32_t pos = atomicAdd(&wcnt[h], 1u);
-                const size_t bh = static_cast<size_t>(b) * P.Hq + g * G + h;
-                if (pos < static_cast<uint32_t>(kp)) P.cand[(bh * P.ncp + c) * P.kcap + pos] = key;
+            want[h] = static_cast<uint32_t>(kp);
+            total[h] = static_cast<uint32_t>(t1 - t0);
+        }
+        block_topk<G>(TS, want, total, [&](auto&& f) {
+            for (int t = t0 + tid; t < t1; t += nthr)
+#pragma unroll
+                for (int h = 0; h < G; ++h) f(h, keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
+        });
+
+        // 4) write the kp candidates of each head (any order)
+        uint64_t thr[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) thr[h] = TS.thr[h];
+        if (tid < G) TS.aux[tid] = 0;
+        __syncthreads();
+        for (int t = t0 + tid; t < t1; t += nthr) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const uint64_t key = topk_key(keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
+                if (key >= thr[h]) {
+                    const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
+                    const size_t bh = static_cast<size_t>(b) * P.Hq + g * G + h;
+                    if (pos < static_cast<uint32_t>(kp)) P.cand[(bh * P.ncp + c) * P.kcap + pos] = key;
+                }
             }
         }
     }
+    __syncthreads();
+    uint32_t* dst = P.shist + (static_cast<size_t>(bg) * P.ncp + c) * kSampBins;
+    for (int x = tid; x < kSampBins; x += nthr) dst[x] = shist[x];
 }
 
 // ===========================================================================
-// select: exact top-k, fixed-set bitmap, base-sample threshold
+// select: exact top-k, fixed-set bitmap, tail histograms, base threshold
 // ===========================================================================
 __device__ __forceinline__ int chunk_candidates(const Plan& P, const Regions& R, int c) {
     const int a = max(c * P.cp, R.lo), e = min((c + 1) * P.cp, R.hi);
@@ -167,33 +207,46 @@ __device__ __forceinline__ int chunk_candidates(const Plan& P, const Regions& R,
 
 template <int G>
 __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
-    __shared__ SelShared<G> S;
+    __shared__ TopkShared<G> TS;
+    __shared__ SampShared<G> SS;
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int bg = blockIdx.x, b = bg / P.Hkv, g = bg % P.Hkv;
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    if (tid == 0 && P.gcounts) {
+        P.gcounts[2 * bg] = 0;
+        P.gcounts[2 * bg + 1] = 0;
+    }
+    const int slots = P.ncp * P.kcap;
 
-    // 1) merge the chunk candidates into the exact top-k of each head
+    // 1) exact top-k of each head from its chunk candidates
     uint64_t thrT[G];
     if (R.k > 0) {
-        uint32_t want[G];
+        uint32_t want[G], total[G];
+        uint32_t tot = 0;
+        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(P, R, c));
 #pragma unroll
-        for (int h = 0; h < G; ++h) want[h] = static_cast<uint32_t>(R.k);
-        const int slots = P.ncp * P.kcap;
-        block_select<G>(S, want, [&](auto&& visit) {
+        for (int h = 0; h < G; ++h) {
+            want[h] = static_cast<uint32_t>(R.k);
+            total[h] = tot;
+        }
+        block_topk<G>(TS, want, total, [&](auto&& f) {
             for (int x = tid; x < slots; x += nthr) {
                 const int c = x / P.kcap, p = x - c * P.kcap;
                 if (p >= chunk_candidates(P, R, c)) continue;
 #pragma unroll
-                for (int h = 0; h < G; ++h) visit(h, P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p]);
+                for (int h = 0; h < G; ++h) {
+                    const uint64_t key = P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p];
+                    f(h, static_cast<uint32_t>(key >> 32), ~static_cast<uint32_t>(key));
+                }
             }
         });
 #pragma unroll
-        for (int h = 0; h < G; ++h) thrT[h] = S.thr[h];
+        for (int h = 0; h < G; ++h) thrT[h] = TS.thr[h];
     }
 
-    // 2) bitmap: sinks [0, sp), window [hi, L), then the top-k bits
+    // 2) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
     const int wl = (L + 31) >> 5;
     for (int x = tid; x < G * wl; x += nthr) {
         const int h = x / wl, w = x - h * wl;
@@ -204,9 +257,18 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
         }
         P.bits[(bh0 + h) * P.words + w] = word;
     }
+    for (int x = tid; x < kSampBins; x += nthr) {
+        uint32_t sum = 0;
+        for (int c = 0; c < P.ncp; ++c) {
+            const int a = max(c * P.cp, R.lo), e = min((c + 1) * P.cp, R.hi);
+            if (a < e) sum += P.shist[(static_cast<size_t>(bg) * P.ncp + c) * kSampBins + x];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) SS.hist[h][x] = sum;
+    }
     __syncthreads();
+    // top-k bits; top-k tokens leave the tail histogram
     if (R.k > 0) {
-        const int slots = P.ncp * P.kcap;
         for (int x = tid; x < slots; x += nthr) {
             const int c = x / P.kcap, p = x - c * P.kcap;
             if (p >= chunk_candidates(P, R, c)) continue;
@@ -216,41 +278,25 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
                 if (key >= thrT[h]) {
                     const uint32_t i = ~static_cast<uint32_t>(key);
                     atomicOr(&P.bits[(bh0 + h) * P.words + (i >> 5)], 1u << (i & 31));
+                    atomicSub(&SS.hist[h][token_word(P, b, g, static_cast<int>(i)) >> (32 - kSampBits)], 1u);
                 }
             }
         }
     }
     __syncthreads();
-
-    // 3) base sample: first nb tail tokens in (Philox word, index) order
-    uint64_t thrB[G];
-    if (R.nb > 0) {
-        uint32_t want[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) want[h] = static_cast<uint32_t>(R.nb);
-        const int q0 = R.lo >> 2, q1 = (R.hi - 1) >> 2;
-        block_select<G>(S, want, [&](auto&& visit) {
-            for (int qd = q0 + tid; qd <= q1; qd += nthr) {
-                const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * qd + e;
-                    if (i < R.lo || i >= R.hi) continue;
-                    const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        if (!bit_of_coherent(P.bits + (bh0 + h) * P.words, i)) visit(h, key);
-                }
-            }
-        });
-#pragma unroll
-        for (int h = 0; h < G; ++h) thrB[h] = S.thr[h];
+    for (int x = tid; x < G * kSampBins; x += nthr) {
+        const int h = x / kSampBins, e = x - h * kSampBins;
+        P.hh[(bh0 + h) * kSampBins + e] = SS.hist[h][e];
     }
 
-    if (tid == 0 && P.gcounts) {
-        P.gcounts[2 * bg] = 0;
-        P.gcounts[2 * bg + 1] = 0;
-    }
+    // 3) base sample: first nb tail tokens in (word, index) order
+    uint32_t rank[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) rank[h] = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
+    block_sample_threshold<G>(SS, TS.S, R, b, g, P.seed_lo, P.seed_hi, rank, [&](int h, int i) {
+        return bit_of_coherent(P.bits + (bh0 + h) * P.words, i);
+    });
+
     if (tid < G) {
         HeadState hs{};
         hs.L = L;
@@ -258,13 +304,13 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
         hs.n_fixed = R.sp + R.wp + R.k;
         hs.NT = R.NT;
         hs.nb = R.nb;
-        hs.thr_b = R.nb > 0 ? thrB[tid] : 0;
+        hs.thr_b = (R.nb > 0 && R.nb < R.NT) ? SS.thr[tid] : 0;  // nb == N_t: the whole tail
         P.hs[bh0 + tid] = hs;
     }
 }
 
 // ===========================================================================
-// Membership of one token for the G heads of its group.
+// base: pinned exact scores of the union of fixed sets and base samples
 // ===========================================================================
 struct HeadView {
     uint64_t thr_b, thr_n;
@@ -272,13 +318,11 @@ struct HeadView {
     float wsamp;
 };
 
-// ===========================================================================
-// base: pinned exact scores of the union of fixed sets and base samples
-// ===========================================================================
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
-    __shared__ int tok[1024];
-    __shared__ uint32_t tmask[1024];
+    __shared__ int tok[kGatherChunk];
+    __shared__ uint32_t tmeta[kGatherChunk];
+    __shared__ uint32_t trow[kGatherChunk];
     __shared__ uint32_t wsum[kChunkThreads / 64];
     __shared__ float wmax[kChunkThreads / 64][G];
     __shared__ HeadView hv[G];
@@ -296,11 +340,13 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     }
     __syncthreads();
 
-    // membership (one Philox call per 4 tokens)
+    // membership (one Philox call per 4 tokens): meta = base mask | fixed mask << 8
     const int T1 = min(T0 + P.cg, L);
     uint32_t m4[4] = {0, 0, 0, 0};
     uint32_t mine = 0;
     const int qd = (T0 >> 2) + tid;
+    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
         uint4 w = make_uint4(0, 0, 0, 0);
         if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
@@ -311,27 +357,36 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
             if (i >= T1) continue;
             const bool inM = i >= R.lo && i < R.hi;
             const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
-            uint32_t mask = 0;
+            uint32_t bm = 0, fm = 0;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const bool fx = bit_of(P.bits + (bh0 + h) * P.words, i);
                 const bool bs = inM && !fx && hv[h].nb > 0 && key >= hv[h].thr_b;
-                mask |= (fx || bs) ? (1u << h) : 0u;
+                bm |= (fx || bs) ? (1u << h) : 0u;
+                fm |= fx ? (1u << h) : 0u;
             }
-            m4[e] = mask;
-            mine += mask ? 1u : 0u;
+            m4[e] = bm ? (bm | (fm << 8)) : 0u;
+            mine += bm ? 1u : 0u;
         }
     }
     uint32_t cnt;
     uint32_t pos = block_excl_scan(mine, wsum, cnt);
+    int32_t* ltok = P.btok + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
+    uint32_t* lmeta = P.bmeta + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (m4[e]) {
             tok[pos] = 4 * qd + e;
-            tmask[pos] = m4[e];
+            tmeta[pos] = m4[e];
+            trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
+            ltok[pos] = 4 * qd + e;
+            lmeta[pos] = m4[e];
             ++pos;
         }
-    if (tid == 0 && P.gcounts && cnt) atomicAdd(&P.gcounts[2 * bg + 1], static_cast<int>(cnt));
+    if (tid == 0) {
+        P.bcnt[static_cast<size_t>(bg) * P.ncg + c] = static_cast<int32_t>(cnt);
+        if (P.gcounts && cnt) atomicAdd(&P.gcounts[2 * bg + 1], static_cast<int>(cnt));
+    }
     __syncthreads();
 
     // pinned scores for all G heads of each listed token
@@ -341,34 +396,40 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
+        for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
     float lmax[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) lmax[h] = -__builtin_inff();
-    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const KVT* kbase = static_cast<const KVT*>(P.k);
     float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    for (int base = 0; base < static_cast<int>(cnt); base += nwaves * TPW) {
-        const int x = base + wave * TPW + slot;
-        const bool act = x < static_cast<int>(cnt);
-        const int i = act ? tok[x] : tok[0];
-        const uint32_t mask = act ? tmask[x] : 0u;
-        const int page = btrow[i / kPage];
-        const KVT* rowp = static_cast<const KVT*>(row_ptr(P.k, sizeof(KVT), page, P.Hkv, g, i % kPage, D)) + 8 * j;
-        float kf[8];
-        load8(rowp, kf);
-        float s[G];
+    const int n = static_cast<int>(cnt);
+    for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
+        float kf[kUnroll][8];
+        int tk[kUnroll];
+        uint32_t mk[kUnroll];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-            if ((mask >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int x = base + u * TPW + slot;
+            const bool act = x < n;
+            const int xs = act ? x : 0;
+            tk[u] = tok[xs];
+            mk[u] = act ? tmeta[xs] : 0u;
+            load8(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kf[u]);
         }
-        if (act && j == 0) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) scrow[static_cast<size_t>(i) * G + h] = s[h];
+        for (int u = 0; u < kUnroll; ++u) {
+            float s[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
+                if ((mk[u] >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
+            }
+            if (mk[u] && j == 0) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) scrow[static_cast<size_t>(tk[u]) * G + h] = s[h];
+            }
         }
     }
-    // block max per head
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float v = lmax[h];
@@ -388,11 +449,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 // ===========================================================================
 template <int G>
 __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
-    __shared__ SelShared<G> S;
+    __shared__ SampShared<G> SS;
+    __shared__ SelShared<G> FS;
     __shared__ float smax[G];
     __shared__ uint64_t red[kGroupThreads / 64][G][4];
-    __shared__ HeadView hv[G];
-    __shared__ int nsel[G];
+    __shared__ int nsel[G], nfin[G];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     const int bg = blockIdx.x, b = bg / P.Hkv, g = bg % P.Hkv;
@@ -406,17 +467,20 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
         }
         return;
     }
+    const int nc = (L + P.cg - 1) / P.cg;
     if (tid < G) {
-        const HeadState& s = P.hs[bh0 + tid];
-        hv[tid] = HeadView{s.thr_b, 0, s.nb, 0, 0.f};
-        const int nc = (L + P.cg - 1) / P.cg;
         float m = -__builtin_inff();
         for (int c = 0; c < nc; ++c) m = fmaxf(m, P.cmax[(bh0 + tid) * P.ncg + c]);
         smax[tid] = m;
     }
+    for (int x = tid; x < G * kSampBins; x += nthr) {
+        const int h = x / kSampBins, e = x - h * kSampBins;
+        SS.hist[h][e] = P.hh[(bh0 + h) * kSampBins + e];
+    }
     __syncthreads();
 
-    // fixed-point sums: SF over I_f, S1 and S2 over the base sample
+    // fixed-point sums over the base pass's member lists: SF over I_f, S1 and
+    // S2 over the base sample
     uint64_t sf[G], s1[G];
     unsigned __int128 s2[G];
 #pragma unroll
@@ -426,29 +490,21 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
         s2[h] = 0;
     }
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    const int nq = (L + 3) >> 2;
-    for (int qd = tid; qd < nq; qd += nthr) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
-            w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * qd + e;
-            if (i >= L) continue;
-            const bool inM = i >= R.lo && i < R.hi;
-            const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
+    for (int c = wave; c < nc; c += nwaves) {
+        const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
+        const int cnt = P.bcnt[static_cast<size_t>(bg) * P.ncg + c];
+        for (int x = lane; x < cnt; x += 64) {
+            const int i = P.btok[lb + x];
+            const uint32_t meta = P.bmeta[lb + x];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const bool fx = bit_of(P.bits + (bh0 + h) * P.words, i);
-                const bool bs = inM && !fx && hv[h].nb > 0 && key >= hv[h].thr_b;
-                if (fx || bs) {
-                    const uint64_t E = fixed_weight(scrow[static_cast<size_t>(i) * G + h] - smax[h]);
-                    if (fx) {
-                        sf[h] += E;
-                    } else {
-                        s1[h] += E;
-                        s2[h] += static_cast<unsigned __int128>(E) * E;
-                    }
+                if (!((meta >> h) & 1u)) continue;
+                const uint64_t E = fixed_weight(scrow[static_cast<size_t>(i) * G + h] - smax[h]);
+                if ((meta >> (8 + h)) & 1u) {
+                    sf[h] += E;
+                } else {
+                    s1[h] += E;
+                    s2[h] += static_cast<unsigned __int128>(E) * E;
                 }
             }
         }
@@ -524,43 +580,25 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
         hs.S1 = S1;
         hs.S2hi = static_cast<uint64_t>(S2 >> 64);
         hs.S2lo = static_cast<uint64_t>(S2);
-        // a new selection unless the sample is empty, the whole tail or the base sample
+        // a new threshold unless the sample is empty, the whole tail or the base sample
         nsel[h] = (n > 0 && n < NT && n != nb) ? n : 0;
-        hv[h].n = n;
+        nfin[h] = n;
     }
     __syncthreads();
 
-    uint32_t want[G];
-    bool any = false;
+    uint32_t rank[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        want[h] = static_cast<uint32_t>(nsel[h]);
-        any |= nsel[h] > 0;
-    }
-    if (any) {
-        const int q0 = R.lo >> 2, q1 = (R.hi - 1) >> 2;
-        block_select<G>(S, want, [&](auto&& visit) {
-            for (int qd = q0 + tid; qd <= q1; qd += nthr) {
-                const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * qd + e;
-                    if (i < R.lo || i >= R.hi) continue;
-                    const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        if (!bit_of(P.bits + (bh0 + h) * P.words, i)) visit(h, key);
-                }
-            }
-        });
-    }
+    for (int h = 0; h < G; ++h) rank[h] = static_cast<uint32_t>(nsel[h]);
+    block_sample_threshold<G>(SS, FS, R, b, g, P.seed_lo, P.seed_hi, rank, [&](int h, int i) {
+        return bit_of(P.bits + (bh0 + h) * P.words, i);
+    });
     if (tid < G) {
-        const int h = tid, n = hv[h].n;
-        uint64_t thr = 0;
-        if (nsel[h] > 0) thr = S.thr[h];
-        else if (n > 0 && n == hv[h].nb) thr = hv[h].thr_b;
-        else thr = 0;  // n == N_t: the whole tail (or n == 0: unused)
-        P.hs[bh0 + h].thr_n = thr;
+        const int h = tid, n = nfin[h];
+        HeadState& hs = P.hs[bh0 + h];
+        uint64_t thr = 0;  // n == N_t: the whole tail (n == 0: unused)
+        if (nsel[h] > 0) thr = SS.thr[h];
+        else if (n > 0 && n == R.nb) thr = hs.thr_b;
+        hs.thr_n = thr;
     }
 }
 
@@ -570,8 +608,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     constexpr int NW = kChunkThreads / 64;
-    __shared__ int tok[1024];
-    __shared__ uint32_t tmeta[1024];
+    __shared__ int tok[kGatherChunk];
+    __shared__ uint32_t tmeta[kGatherChunk];
+    __shared__ uint32_t trow[kGatherChunk];
     __shared__ uint32_t wsum[NW];
     __shared__ HeadView hv[G];
     __shared__ float wm[NW][G], wl[NW][G];
@@ -590,11 +629,13 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     }
     __syncthreads();
 
-    // membership: meta = final mask | fixed mask << 8 | cached << 16
+    // membership: meta = final mask | fixed mask << 8 | score cached << 16
     const int T1 = min(T0 + P.cg, L);
     uint32_t m4[4] = {0, 0, 0, 0};
     uint32_t mine = 0;
     const int qd = (T0 >> 2) + tid;
+    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
         uint4 w = make_uint4(0, 0, 0, 0);
         if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
@@ -616,8 +657,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
                 fxm |= fx ? (1u << h) : 0u;
                 cached |= (fx || sb) ? 1u : 0u;
             }
-            const uint32_t meta = fin | (fxm << 8) | (cached << 16);
-            m4[e] = fin ? meta : 0u;
+            m4[e] = fin ? (fin | (fxm << 8) | (cached << 16)) : 0u;
             mine += fin ? 1u : 0u;
         }
     }
@@ -628,6 +668,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
         if (m4[e]) {
             tok[pos] = 4 * qd + e;
             tmeta[pos] = m4[e];
+            trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
             ++pos;
         }
     if (tid == 0 && P.gcounts && cnt) atomicAdd(&P.gcounts[2 * bg], static_cast<int>(cnt));
@@ -639,8 +680,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
+        for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
     float ws[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) ws[h] = hv[h].wsamp;
@@ -652,41 +692,62 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
-    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const KVT* kbase = static_cast<const KVT*>(P.k);
+    const KVT* vbase = static_cast<const KVT*>(P.v);
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    for (int base = 0; base < static_cast<int>(cnt); base += nwaves * TPW) {
-        const int x = base + wave * TPW + slot;
-        const bool act = x < static_cast<int>(cnt);
-        const int i = act ? tok[x] : tok[0];
-        const uint32_t meta = act ? tmeta[x] : 0u;
-        const bool cached = (meta >> 16) & 1u;
-        const int page = btrow[i / kPage];
-        const size_t roff = ((static_cast<size_t>(page) * P.Hkv + g) * kPage + (i % kPage)) * D + 8 * j;
-        float vf[8], kf[8];
-        load8(static_cast<const KVT*>(P.v) + roff, vf);
-        if (!cached) {
-            load8(static_cast<const KVT*>(P.k) + roff, kf);
-        } else {
+    const int n = static_cast<int>(cnt);
+    for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
+        float vf[kUnroll][8], kf[kUnroll][8];
+        uint32_t mk[kUnroll];
+        int tk[kUnroll];
+        // issue every row load of the batch first
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kf[e] = 0.f;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int x = base + u * TPW + slot;
+            const bool act = x < n;
+            const int xs = act ? x : 0;
+            tk[u] = tok[xs];
+            mk[u] = act ? tmeta[xs] : 0u;
+            const size_t roff = static_cast<size_t>(trow[xs]) * D + 8 * j;
+            load8(vbase + roff, vf[u]);
+            if (!((mk[u] >> 16) & 1u)) {
+                load8(kbase + roff, kf[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kf[u][e] = 0.f;
+            }
         }
-        float s[G];
+        float s[kUnroll][G];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool cached = (mk[u] >> 16) & 1u;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float st = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
+                s[u][h] = cached ? scrow[static_cast<size_t>(tk[u]) * G + h] : st;
+            }
+        }
+        // one max update per batch and head, then the weighted accumulation
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float st = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-            s[h] = cached ? scrow[static_cast<size_t>(i) * G + h] : st;
-        }
+            float mx = m[h];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const bool on = act && ((meta >> h) & 1u);
-            const float w = ((meta >> (8 + h)) & 1u) ? 1.0f : ws[h];
-            const float mn = on ? fmaxf(m[h], s[h]) : m[h];
-            const float alpha = (mn == -__builtin_inff()) ? 1.0f : __expf(m[h] - mn);
-            const float p = on ? w * __expf(s[h] - mn) : 0.0f;
-            l[h] = l[h] * alpha + p;
+            for (int u = 0; u < kUnroll; ++u)
+                if ((mk[u] >> h) & 1u) mx = fmaxf(mx, s[u][h]);
+            const float alpha = (mx == -__builtin_inff()) ? 1.0f : __expf(m[h] - mx);
+            l[h] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * alpha + p * vf[e];
-            m[h] = mn;
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const bool on = (mk[u] >> h) & 1u;
+                const float w = ((mk[u] >> (8 + h)) & 1u) ? 1.0f : ws[h];
+                const float p = on ? w * __expf(s[u][h] - mx) : 0.0f;
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, vf[u][e], acc[h][e]);
+            }
+            m[h] = mx;
         }
     }
     // merge the TPW token slots of the wave (lanes with equal j)
@@ -739,33 +800,53 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
 // ===========================================================================
 // combine: merge chunk partials; counts and statistics
 // ===========================================================================
-__global__ __launch_bounds__(256) void k_combine(Plan P) {
+constexpr int kCombineThreads = 128;
+constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
+
+__global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
+    __shared__ float wsh[kMaxChunks];
+    __shared__ float rm[kCombineThreads / 64], rl[kCombineThreads / 64];
+    const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq;
     const int L = P.seq_lens[b];
     const int D = P.d;
     const int nc = (L + P.cg - 1) / P.cg;
     const float* pp = P.part + static_cast<size_t>(bh) * P.ncg * (D + 2);
+    float mloc = -__builtin_inff();
+    for (int c = tid; c < nc; c += nthr) mloc = fmaxf(mloc, pp[static_cast<size_t>(c) * (D + 2)]);
+    for (int o = 1; o < 64; o <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+    if (lane == 0) rm[wave] = mloc;
+    __syncthreads();
     float M = -__builtin_inff();
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, pp[static_cast<size_t>(c) * (D + 2)]);
-    float l = 0.f;
-    if (M != -__builtin_inff())
-        for (int c = 0; c < nc; ++c) {
-            const float* q = pp + static_cast<size_t>(c) * (D + 2);
-            l += q[1] * __expf(q[0] - M);
-        }
-    for (int e = threadIdx.x; e < D; e += blockDim.x) {
-        float a = 0.f;
-        if (M != -__builtin_inff() && l > 0.f) {
-            for (int c = 0; c < nc; ++c) {
-                const float* q = pp + static_cast<size_t>(c) * (D + 2);
-                a += q[2 + e] * __expf(q[0] - M);
-            }
-            a = a / l;
-        }
-        P.out[static_cast<size_t>(bh) * D + e] = a;
+    for (int w = 0; w < nthr / 64; ++w) M = fmaxf(M, rm[w]);
+    float lloc = 0.f;
+    for (int c = tid; c < nc; c += nthr) {
+        const float* q = pp + static_cast<size_t>(c) * (D + 2);
+        const float wgt = (M == -__builtin_inff()) ? 0.0f : __expf(q[0] - M);
+        wsh[c] = wgt;
+        lloc += wgt * q[1];
     }
-    if (threadIdx.x == 0) {
-        P.lse[bh] = (M != -__builtin_inff() && l > 0.f) ? M + __logf(l) : -__builtin_inff();
+    for (int o = 1; o < 64; o <<= 1) lloc += __shfl_xor(lloc, o, 64);
+    if (lane == 0) rl[wave] = lloc;
+    __syncthreads();
+    float l = 0.f;
+    for (int w = 0; w < nthr / 64; ++w) l += rl[w];
+    const bool ok = M != -__builtin_inff() && l > 0.f;
+    for (int e = tid; e < D; e += nthr) {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        int c = 0;
+        for (; c + 4 <= nc; c += 4) {
+            a0 += wsh[c] * pp[static_cast<size_t>(c) * (D + 2) + 2 + e];
+            a1 += wsh[c + 1] * pp[static_cast<size_t>(c + 1) * (D + 2) + 2 + e];
+            a2 += wsh[c + 2] * pp[static_cast<size_t>(c + 2) * (D + 2) + 2 + e];
+            a3 += wsh[c + 3] * pp[static_cast<size_t>(c + 3) * (D + 2) + 2 + e];
+        }
+        for (; c < nc; ++c) a0 += wsh[c] * pp[static_cast<size_t>(c) * (D + 2) + 2 + e];
+        const float a = (a0 + a1) + (a2 + a3);
+        P.out[static_cast<size_t>(bh) * D + e] = ok ? a / l : 0.0f;
+    }
+    if (tid == 0) {
+        P.lse[bh] = ok ? M + __logf(l) : -__builtin_inff();
         const HeadState& hs = P.hs[bh];
         if (P.counts) {
             int32_t* ct = P.counts + static_cast<size_t>(bh) * 6;
@@ -897,9 +978,13 @@ template <int ROW, typename T, int G>
 static int launch_predict(const Plan& p, hipStream_t st) {
     const size_t lds = predict_lds_bytes(G, p.d, ROW, p.cp);
     auto kern = k_predict<ROW, T, G>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return static_cast<int>(e);
+    static bool attr_set = false;  // per kernel instance; the limit never changes
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (e != hipSuccess) return static_cast<int>(e);
+        attr_set = true;
+    }
     hipLaunchKernelGGL(kern, dim3(p.ncp, p.B * p.Hkv), dim3(kPredThreads), lds, st, p);
     return 0;
 }
@@ -945,7 +1030,7 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
         default: rc = launch_g<8>(p, st, mk); break;
     }
     if (rc) return rc;
-    hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(p.d), 0, st, p);
+    hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
     if ((rc = mk.mark(6))) return rc;
     if (p.idx) hipLaunchKernelGGL(k_emit, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
     if ((rc = mk.mark(7))) return rc;

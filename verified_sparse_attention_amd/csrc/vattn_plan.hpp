@@ -11,6 +11,13 @@ constexpr int kGroupThreads = 1024;  // per-(b, KV head) selection / budget
 constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
 constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
+constexpr int kSampBits = 11;        // sampler histogram: top bits of the Philox word
+constexpr int kSampBins = 1 << kSampBits;
+constexpr int kTopBuckets = 256;     // value-range buckets of the top-k select
+constexpr int kListCap = 128;        // boundary-bucket list capacity per head
+constexpr int kGatherChunk = 4 * kChunkThreads;  // tokens per base/gather block
+constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+#define VATTN_MAX_SEQ_TOKENS (1 << 20)
 
 // Per (sequence, query head) state handed from kernel to kernel.
 struct HeadState {
@@ -48,6 +55,11 @@ struct Plan {
     float* sc;       // [B*Hkv][max_seq_len][G] pinned exact scores (base-sample union)
     float* cmax;     // [B*Hq][ncg] chunk max of pinned scores
     float* part;     // [B*Hq][ncg][d + 2] online-softmax partials (m, l, acc[d])
+    uint32_t* shist; // [B*Hkv][ncp][kSampBins] sampler-word histogram of each chunk's middle
+    uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
+    int32_t* btok;   // [B*Hkv][ncg][cg] base-pass member tokens, ascending
+    uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
+    int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     // outputs
     float* out;
     float* lse;
