@@ -97,7 +97,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, shist, hh, btok, bmeta, bcnt, total;
+    size_t cand, bits, hs, sc, cmax, part, shist, hh, btok, bmeta, bcnt, uw, crange, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -127,6 +127,10 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t));
     L.bcnt = off;
     off += align_up(BHkv * s.ncg * sizeof(int32_t));
+    L.uw = off;
+    off += align_up(BHkv * (static_cast<size_t>(s.ncg) * s.cg) * sizeof(uint32_t));
+    L.crange = off;
+    off += align_up(BHq * s.ncp * 2 * sizeof(uint32_t));
     L.total = off;
     return L;
 }
@@ -212,6 +216,8 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.btok = reinterpret_cast<int32_t*>(ws + L.btok);
     p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
+    p.uw = reinterpret_cast<uint32_t*>(ws + L.uw);
+    p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
     p.out = out->out;
     p.lse = out->lse;
     p.idx = out->idx;

@@ -67,10 +67,24 @@ __device__ __forceinline__ float chain8(const float (&a)[8], const float (&b)[8]
     return acc;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The pairwise tree over the LPT lane partials of a row, adjacent pairs first,
+// with DPP lane moves: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 2k/2k+1
+// and the two halves of each quad; row_ror:4 then adds quad q-1 to quad q and
+// row_ror:8 adds lanes 4-7 to lanes 12-15 of each 16-lane row.  IEEE addition
+// commutes, so each sum equals the tree's.  The result is valid in the lanes
+// with lane % LPT == LPT - 1 (in every lane when LPT <= 4).
 template <int LPT>
 __device__ __forceinline__ float tree_across_lanes(float v) {
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) v = v + __shfl_xor(v, m, 64);
+    static_assert(LPT == 1 || LPT == 2 || LPT == 4 || LPT == 8 || LPT == 16, "row of 8..128 elements");
+    if constexpr (LPT >= 2) v = v + dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (LPT >= 4) v = v + dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (LPT >= 8) v = dpp<0x124>(v) + v;  // row_ror:4
+    if constexpr (LPT >= 16) v = dpp<0x128>(v) + v; // row_ror:8
     return v;
 }
 
@@ -159,6 +173,32 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&f)[8]) {
     for (int k = 0; k < 4; ++k) {
         f[2 * k] = __uint_as_float(ws[k] << 16);
         f[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+    }
+}
+struct Raw8 {  // one lane's 8 elements as loaded (bf16: one uint4; fp32: two float4)
+    uint4 a, b;
+};
+__device__ __forceinline__ void load_raw(const uint16_t* p, Raw8& r) {
+    r.a = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void load_raw(const float* p, Raw8& r) {
+    r.a = *reinterpret_cast<const uint4*>(p);
+    r.b = *reinterpret_cast<const uint4*>(p + 4);
+}
+template <typename T>
+__device__ __forceinline__ void widen(const Raw8& r, float (&f)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t ws[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = __uint_as_float(ws[k] << 16);
+            f[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+        }
+    } else {
+        f[0] = __uint_as_float(r.a.x); f[1] = __uint_as_float(r.a.y);
+        f[2] = __uint_as_float(r.a.z); f[3] = __uint_as_float(r.a.w);
+        f[4] = __uint_as_float(r.b.x); f[5] = __uint_as_float(r.b.y);
+        f[6] = __uint_as_float(r.b.z); f[7] = __uint_as_float(r.b.w);
     }
 }
 __device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
@@ -396,22 +436,24 @@ __device__ __forceinline__ void list_rank_pick(const uint64_t* list, int n, uint
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exact top-k threshold for NH heads at once, without contended
-// atomics: (A) range of the order keys, (B) histogram over kTopBuckets
-// value-range buckets (a monotone map of the key, so bucket order is key
-// order), (C) the boundary bucket's keys listed and ranked exactly.  Only a
-// boundary bucket larger than kListCap falls back to the radix select.
-// items(f) calls f(h, okey, index) for every key of head h on this thread.
-// Result: thr[h] with exactly want[h] keys topk_key(okey, index) >= thr[h]
-// (thr 0 when want >= total; unused when want == 0).
+// Block-wide exact top-k for NH heads at once, without contended atomics:
+// (B) histogram over kTopBuckets value-range buckets of the score (a
+// monotone map of the key, so bucket order is key order) between the given
+// bracket [lo_ok, hi_ok] of the heads' order keys, (C) one pass that emits
+// every key above the boundary bucket and lists the boundary bucket's keys,
+// which are then ranked exactly.  Only a boundary bucket larger than
+// kListCap falls back to the radix select.  items(f) calls f(h, okey, index)
+// for every key of head h on this thread; emit(h, key) is called exactly once
+// for each of the want[h] largest keys topk_key(okey, index) of head h (for
+// every key when want[h] >= total[h]).  On return thr[h] is the smallest
+// emitted key (0 when everything was emitted).
 // ---------------------------------------------------------------------------
 template <int NH>
 struct TopkShared {
     SelShared<NH> S;  // S.hist doubles as the bucket histogram
     uint64_t list[NH][kListCap];
     uint64_t thr[NH];
-    uint32_t lo[NH], hi[NH], above[NH], cnt[NH], aux[NH];
-    float vmin[NH], scale[NH];
+    uint32_t above[NH], cnt[NH], aux[NH], lo[NH], hi[NH];
     int bstar[NH];
 };
 
@@ -420,29 +462,38 @@ __device__ __forceinline__ float okey_value(uint32_t ok) {
     return __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
 }
 
-// Bucket linear in the score: (s - s_min) * 256 / (s_max - s_min), clamped.
+// Bucket linear in the score: (s - s_lo) * 256 / (s_hi - s_lo), clamped.
 // Each step (fp32 subtract, multiply by a positive constant, truncate) is
 // monotone non-decreasing, so bucket order never contradicts key order.
 __device__ __forceinline__ int topk_bucket(uint32_t ok, float vmin, float scale) {
-    const int bk = static_cast<int>((okey_value(ok) - vmin) * scale);
+    const float f = (okey_value(ok) - vmin) * scale;
+    const int bk = f > 0.0f ? static_cast<int>(f) : 0;
     return bk < kTopBuckets - 1 ? bk : kTopBuckets - 1;
 }
 
-template <int NH, class Items>
+template <int NH, class Items, class Emit>
 __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
-                           Items&& items) {
+                           const uint32_t (&lo_ok)[NH], const uint32_t (&hi_ok)[NH], Items&& items,
+                           Emit&& emit) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    bool act[NH];
+    bool act[NH], all[NH];
+    float vm[NH], sc[NH];
     bool any = false;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
         act[h] = want[h] > 0 && want[h] < total[h];
+        all[h] = want[h] > 0 && want[h] >= total[h];
         any |= act[h];
+        const float vmin = okey_value(lo_ok[h]), vmax = okey_value(hi_ok[h]);
+        const float range = vmax - vmin;
+        const float scale = static_cast<float>(kTopBuckets) / range;
+        // a zero or non-finite range puts every key in bucket 0
+        const bool ok = range > 0.0f && range < __builtin_inff() && scale < __builtin_inff();
+        vm[h] = vmin;
+        sc[h] = ok ? scale : 0.0f;
     }
     if (tid < NH) {
-        T.lo[tid] = 0xFFFFFFFFu;
-        T.hi[tid] = 0;
         T.cnt[tid] = 0;
         T.thr[tid] = 0;
         T.bstar[tid] = -1;
@@ -450,73 +501,45 @@ __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const 
     }
     for (int x = tid; x < NH * kTopBuckets; x += nthr) (&T.S.hist[0][0])[x] = 0;
     __syncthreads();
-    if (!any) return;
-    // (A) key range per head
-    uint32_t lo[NH], hi[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        lo[h] = 0xFFFFFFFFu;
-        hi[h] = 0;
-    }
-    items([&](int h, uint32_t ok, uint32_t) {
-        lo[h] = min(lo[h], ok);
-        hi[h] = max(hi[h], ok);
-    });
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        uint32_t a = lo[h], b = hi[h];
-        for (int o = 1; o < 64; o <<= 1) {
-            a = min(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
-            b = max(b, static_cast<uint32_t>(__shfl_xor(b, o, 64)));
+    if (any) {
+        // (B) bucket histogram
+        items([&](int h, uint32_t ok, uint32_t) {
+            if (act[h]) atomicAdd(&T.S.hist[h][topk_bucket(ok, vm[h], sc[h])], 1u);
+        });
+        __syncthreads();
+        for (int h = wave; h < NH; h += nwaves) {
+            if (!act[h]) continue;
+            int bin;
+            uint32_t before;
+            wave_rank_bin<kTopBuckets>(T.S.hist[h], want[h], true, bin, before);
+            if (lane == 0) {
+                T.bstar[h] = bin;
+                T.above[h] = before;
+            }
         }
-        if (lane == 0 && act[h]) {
-            atomicMin(&T.lo[h], a);
-            atomicMax(&T.hi[h], b);
-        }
+        __syncthreads();
     }
-    __syncthreads();
-    if (tid < NH) {
-        const float vmin = okey_value(T.lo[tid]), vmax = okey_value(T.hi[tid]);
-        const float range = vmax - vmin;
-        const float scale = static_cast<float>(kTopBuckets) / range;
-        // a zero or non-finite range puts every key in bucket 0
-        const bool ok = range > 0.0f && range < __builtin_inff() && scale < __builtin_inff();
-        T.vmin[tid] = vmin;
-        T.scale[tid] = ok ? scale : 0.0f;
-    }
-    __syncthreads();
-    float vm[NH], sc[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        vm[h] = T.vmin[h];
-        sc[h] = T.scale[h];
-    }
-    // (B) bucket histogram
-    items([&](int h, uint32_t ok, uint32_t) {
-        if (act[h]) atomicAdd(&T.S.hist[h][topk_bucket(ok, vm[h], sc[h])], 1u);
-    });
-    __syncthreads();
-    for (int h = wave; h < NH; h += nwaves) {
-        if (!act[h]) continue;
-        int bin;
-        uint32_t before;
-        wave_rank_bin<kTopBuckets>(T.S.hist[h], want[h], true, bin, before);
-        if (lane == 0) {
-            T.bstar[h] = bin;
-            T.above[h] = before;
-        }
-    }
-    __syncthreads();
     int bs[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) bs[h] = T.bstar[h];
-    // (C) boundary bucket list
+    // (C) emit the keys above the boundary bucket, list the boundary bucket
     items([&](int h, uint32_t ok, uint32_t idx) {
-        if (act[h] && topk_bucket(ok, vm[h], sc[h]) == bs[h]) {
-            const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
-            if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
+        if (all[h]) {
+            emit(h, topk_key(ok, idx));
+        } else if (act[h]) {
+            const int bk = topk_bucket(ok, vm[h], sc[h]);
+            if (bk > bs[h]) {
+                emit(h, topk_key(ok, idx));
+            } else if (bk == bs[h]) {
+                const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
+                if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
+            }
         }
     });
+    if (!any) {
+        __syncthreads();
+        return;
+    }
     __syncthreads();
     uint32_t fmask = 0;
 #pragma unroll
@@ -528,18 +551,32 @@ __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const 
             list_rank_pick(T.list[h], static_cast<int>(T.cnt[h]), want[h] - T.above[h], e, &T.thr[h]);
     }
     __syncthreads();
+    for (int x = tid; x < NH * kListCap; x += nthr) {
+        const int h = x / kListCap, e = x - h * kListCap;
+        if (act[h] && bs[h] >= 0 && !((fmask >> h) & 1u) && e < static_cast<int>(T.cnt[h]) &&
+            T.list[h][e] >= T.thr[h])
+            emit(h, T.list[h][e]);
+    }
     if (fmask) {  // rare: a crowded boundary bucket, ranked by the radix select
         uint32_t fw[NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? want[h] - T.above[h] : 0u;
+        __syncthreads();
         block_select<NH>(T.S, fw, [&](auto&& visit) {
             items([&](int h, uint32_t ok, uint32_t idx) {
                 if (((fmask >> h) & 1u) && topk_bucket(ok, vm[h], sc[h]) == bs[h]) visit(h, topk_key(ok, idx));
             });
         }, true);
-        if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = T.S.thr[tid];
-        __syncthreads();
+        uint64_t ft[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) ft[h] = T.S.thr[h];
+        items([&](int h, uint32_t ok, uint32_t idx) {
+            if (((fmask >> h) & 1u) && topk_bucket(ok, vm[h], sc[h]) == bs[h] && topk_key(ok, idx) >= ft[h])
+                emit(h, topk_key(ok, idx));
+        });
+        if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = ft[tid];
     }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -547,9 +584,9 @@ __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const 
 // hist[h] holds the tail histogram of head h.  For rank[h] > 0 the result
 // thr[h] = sample_key of the rank-th smallest (word, index) of the tail, so
 // the first rank[h] tail tokens of the sample order are exactly those with
-// sample_key >= thr[h].  One Philox pass over the middle collects the tokens
-// of the boundary bin; `in_fixed(h, i)` tells whether token i is in head h's
-// fixed set (those are not in the tail).
+// sample_key >= thr[h].  One pass over the middle's cached words uw[i]
+// collects the tokens of the boundary bin; `in_fixed(h, i)` tells whether
+// token i is in head h's fixed set (those are not in the tail).
 // ---------------------------------------------------------------------------
 template <int NH>
 struct SampShared {
@@ -561,8 +598,8 @@ struct SampShared {
 };
 
 template <int NH, class InFixed>
-__device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions& R, int b, int g,
-                                       uint32_t seed_lo, uint32_t seed_hi, const uint32_t (&rank)[NH],
+__device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions& R,
+                                       const uint32_t* __restrict__ uw, const uint32_t (&rank)[NH],
                                        InFixed&& in_fixed) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -593,19 +630,30 @@ __device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, cons
 #pragma unroll
     for (int h = 0; h < NH; ++h) bn[h] = rank[h] > 0 ? S.bin[h] : -1;
     const int q0 = R.lo >> 2, q1 = (R.hi - 1) >> 2;
-    for (int qd = q0 + tid; qd <= q1; qd += nthr) {
-        const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, seed_lo, seed_hi);
+    constexpr int kBatch = 8;  // quads loaded before any is examined
+    for (int qb = q0 + tid; qb <= q1; qb += kBatch * nthr) {
+        uint4 wb[kBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * qd + e;
-            if (i < R.lo || i >= R.hi) continue;
-            const uint32_t u = word_of(w, e);
-            const int bi = static_cast<int>(u >> kShift);
+        for (int t = 0; t < kBatch; ++t) {
+            const int qd = qb + t * nthr;
+            wb[t] = qd <= q1 ? *reinterpret_cast<const uint4*>(uw + 4 * qd) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                if (bi == bn[h] && !in_fixed(h, i)) {
-                    const uint32_t pos = atomicAdd(&S.cnt[h], 1u);
-                    if (pos < static_cast<uint32_t>(kListCap)) S.list[h][pos] = sample_key(u, static_cast<uint32_t>(i));
+        for (int t = 0; t < kBatch; ++t) {
+            const int qd = qb + t * nthr;
+            if (qd > q1) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * qd + e;
+                if (i < R.lo || i >= R.hi) continue;
+                const uint32_t u = word_of(wb[t], e);
+                const int bi = static_cast<int>(u >> kShift);
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    if (bi == bn[h] && !in_fixed(h, i)) {
+                        const uint32_t pos = atomicAdd(&S.cnt[h], 1u);
+                        if (pos < static_cast<uint32_t>(kListCap)) S.list[h][pos] = sample_key(u, static_cast<uint32_t>(i));
+                    }
                 }
             }
         }
@@ -627,7 +675,7 @@ __device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, cons
         for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? rank[h] - S.before[h] : 0u;
         block_select<NH>(F, fw, [&](auto&& visit) {
             for (int qd = q0 + tid; qd <= q1; qd += nthr) {
-                const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, seed_lo, seed_hi);
+                const uint4 w = *reinterpret_cast<const uint4*>(uw + 4 * qd);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * qd + e;

@@ -49,9 +49,9 @@ __device__ __forceinline__ size_t row_index(int page, int Hkv, int g, int slot, 
     return ((static_cast<size_t>(page) * Hkv + g) * kPage + slot) * static_cast<size_t>(width);
 }
 
-__device__ __forceinline__ uint32_t token_word(const Plan& P, int b, int g, int i) {
-    const uint4 w = philox4x32_10(static_cast<uint32_t>(i >> 2), g, b, 0, P.seed_lo, P.seed_hi);
-    return word_of(w, i & 3);
+// Cached sample words of group bg (written by the predictor pass for the middle).
+__device__ __forceinline__ const uint32_t* group_words(const Plan& P, int bg) {
+    return P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
 }
 
 __host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
@@ -102,8 +102,10 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     for (int x = tid; x < kSampBins; x += nthr) shist[x] = 0;
     for (int x = tid; x < ntok / kPage; x += nthr) pages[x] = btrow[tb / kPage + x];
     __syncthreads();
+    uint32_t* uwg = P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
     for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
         const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+        *reinterpret_cast<uint4*>(uwg + 4 * qd) = w;  // chunks are disjoint at quad granularity
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
@@ -139,6 +141,17 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             for (int e = 0; e < 8; ++e) qreg[h][e] = qv[h * ROW + 8 * j + e];
         const T* src = static_cast<const T*>(P.predictor == 1 ? static_cast<const void*>(P.kt) : P.k);
         const int cbase = c * P.cp;
+        uint32_t klo[G], khi[G];  // order-key range of the stored scores
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            klo[h] = 0xFFFFFFFFu;
+            khi[h] = 0;
+        }
+        if (tid < G) {
+            TS.lo[tid] = 0xFFFFFFFFu;
+            TS.hi[tid] = 0;
+            TS.aux[tid] = 0;
+        }
         for (int base = wave * TPW * kUnroll; base < ntok; base += nwaves * TPW * kUnroll) {
             float kf[kUnroll][8];
             int tt[kUnroll];
@@ -154,42 +167,53 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float s = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
-                    if (j == 0 && tt[u] >= t0 && tt[u] < t1) keys[h * P.cp + (tt[u] - cbase)] = okey(s);
+                    if (j == LPT - 1 && tt[u] >= t0 && tt[u] < t1) {
+                        const uint32_t ok = okey(s);
+                        keys[h * P.cp + (tt[u] - cbase)] = ok;
+                        klo[h] = min(klo[h], ok);
+                        khi[h] = max(khi[h], ok);
+                    }
                 }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            uint32_t a = klo[h], bb = khi[h];
+            for (int o = 1; o < 64; o <<= 1) {
+                a = min(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
+                bb = max(bb, static_cast<uint32_t>(__shfl_xor(bb, o, 64)));
+            }
+            if (lane == 0) {
+                atomicMin(&TS.lo[h], a);
+                atomicMax(&TS.hi[h], bb);
             }
         }
         __syncthreads();
 
-        // 3) chunk top-kp per head
+        // 3) chunk top-kp per head, written as candidates (any order)
         const int kp = min(R.k, t1 - t0);
-        uint32_t want[G], total[G];
+        uint32_t want[G], total[G], lo[G], hi[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             want[h] = static_cast<uint32_t>(kp);
             total[h] = static_cast<uint32_t>(t1 - t0);
+            lo[h] = TS.lo[h];
+            hi[h] = TS.hi[h];
         }
-        block_topk<G>(TS, want, total, [&](auto&& f) {
+        const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) {
             for (int t = t0 + tid; t < t1; t += nthr)
 #pragma unroll
                 for (int h = 0; h < G; ++h) f(h, keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
+        }, [&](int h, uint64_t key) {
+            const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
+            if (pos < static_cast<uint32_t>(kp)) P.cand[((bh0 + h) * P.ncp + c) * P.kcap + pos] = key;
         });
-
-        // 4) write the kp candidates of each head (any order)
-        uint64_t thr[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) thr[h] = TS.thr[h];
-        if (tid < G) TS.aux[tid] = 0;
-        __syncthreads();
-        for (int t = t0 + tid; t < t1; t += nthr) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const uint64_t key = topk_key(keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
-                if (key >= thr[h]) {
-                    const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
-                    const size_t bh = static_cast<size_t>(b) * P.Hq + g * G + h;
-                    if (pos < static_cast<uint32_t>(kp)) P.cand[(bh * P.ncp + c) * P.kcap + pos] = key;
-                }
-            }
+        // order-key bracket of the candidates for the merge: [threshold key, chunk max]
+        if (tid < G) {
+            uint32_t* cr = P.crange + ((bh0 + tid) * P.ncp + c) * 2;
+            cr[0] = TS.thr[tid] ? static_cast<uint32_t>(TS.thr[tid] >> 32) : lo[tid];
+            cr[1] = hi[tid];
         }
     }
     __syncthreads();
@@ -214,46 +238,22 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    const uint32_t* uwg = group_words(P, bg);
     if (tid == 0 && P.gcounts) {
         P.gcounts[2 * bg] = 0;
         P.gcounts[2 * bg + 1] = 0;
     }
-    const int slots = P.ncp * P.kcap;
 
-    // 1) exact top-k of each head from its chunk candidates
-    uint64_t thrT[G];
-    if (R.k > 0) {
-        uint32_t want[G], total[G];
-        uint32_t tot = 0;
-        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(P, R, c));
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            want[h] = static_cast<uint32_t>(R.k);
-            total[h] = tot;
-        }
-        block_topk<G>(TS, want, total, [&](auto&& f) {
-            for (int x = tid; x < slots; x += nthr) {
-                const int c = x / P.kcap, p = x - c * P.kcap;
-                if (p >= chunk_candidates(P, R, c)) continue;
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint64_t key = P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p];
-                    f(h, static_cast<uint32_t>(key >> 32), ~static_cast<uint32_t>(key));
-                }
-            }
-        });
-#pragma unroll
-        for (int h = 0; h < G; ++h) thrT[h] = TS.thr[h];
-    }
-
-    // 2) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
+    // 1) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
     const int wl = (L + 31) >> 5;
     for (int x = tid; x < G * wl; x += nthr) {
         const int h = x / wl, w = x - h * wl;
         uint32_t word = 0;
-        for (int e = 0; e < 32; ++e) {
-            const int i = 32 * w + e;
-            if (i < L && (i < R.sp || i >= R.hi)) word |= 1u << e;
+        const int i0 = 32 * w;
+        if (i0 < R.sp) word |= (R.sp - i0 >= 32) ? 0xFFFFFFFFu : ((1u << (R.sp - i0)) - 1u);
+        if (i0 + 32 > R.hi) {
+            const int a = max(R.hi - i0, 0), e = min(L - i0, 32);  // bits [a, e)
+            if (e > a) word |= (e - a >= 32 ? 0xFFFFFFFFu : ((1u << (e - a)) - 1u)) << a;
         }
         P.bits[(bh0 + h) * P.words + w] = word;
     }
@@ -266,24 +266,45 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
 #pragma unroll
         for (int h = 0; h < G; ++h) SS.hist[h][x] = sum;
     }
-    __syncthreads();
-    // top-k bits; top-k tokens leave the tail histogram
+
+    // 2) exact top-k of each head from its chunk candidates: set the bit and
+    //    take the token out of the tail histogram (block_topk starts with a barrier)
     if (R.k > 0) {
-        for (int x = tid; x < slots; x += nthr) {
-            const int c = x / P.kcap, p = x - c * P.kcap;
-            if (p >= chunk_candidates(P, R, c)) continue;
+        uint32_t want[G], total[G], lo[G], hi[G];
+        uint32_t tot = 0;
+        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(P, R, c));
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const uint64_t key = P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p];
-                if (key >= thrT[h]) {
-                    const uint32_t i = ~static_cast<uint32_t>(key);
-                    atomicOr(&P.bits[(bh0 + h) * P.words + (i >> 5)], 1u << (i & 31));
-                    atomicSub(&SS.hist[h][token_word(P, b, g, static_cast<int>(i)) >> (32 - kSampBits)], 1u);
-                }
+        for (int h = 0; h < G; ++h) {
+            want[h] = static_cast<uint32_t>(R.k);
+            total[h] = tot;
+            lo[h] = 0xFFFFFFFFu;
+            hi[h] = 0;
+            for (int c = 0; c < P.ncp; ++c) {
+                if (chunk_candidates(P, R, c) == 0) continue;
+                const uint32_t* cr = P.crange + ((bh0 + h) * P.ncp + c) * 2;
+                lo[h] = min(lo[h], cr[0]);
+                hi[h] = max(hi[h], cr[1]);
             }
         }
+        const int slots = P.ncp * P.kcap;
+        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) {
+            for (int x = tid; x < slots; x += nthr) {
+                const int c = x / P.kcap, p = x - c * P.kcap;
+                if (p >= chunk_candidates(P, R, c)) continue;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint64_t key = P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p];
+                    f(h, static_cast<uint32_t>(key >> 32), ~static_cast<uint32_t>(key));
+                }
+            }
+        }, [&](int h, uint64_t key) {
+            const uint32_t i = ~static_cast<uint32_t>(key);
+            atomicOr(&P.bits[(bh0 + h) * P.words + (i >> 5)], 1u << (i & 31));
+            atomicSub(&SS.hist[h][uwg[i] >> (32 - kSampBits)], 1u);
+        });
+    } else {
+        __syncthreads();
     }
-    __syncthreads();
     for (int x = tid; x < G * kSampBins; x += nthr) {
         const int h = x / kSampBins, e = x - h * kSampBins;
         P.hh[(bh0 + h) * kSampBins + e] = SS.hist[h][e];
@@ -293,7 +314,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
     uint32_t rank[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) rank[h] = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
-    block_sample_threshold<G>(SS, TS.S, R, b, g, P.seed_lo, P.seed_hi, rank, [&](int h, int i) {
+    block_sample_threshold<G>(SS, TS.S, R, uwg, rank, [&](int h, int i) {
         return bit_of_coherent(P.bits + (bh0 + h) * P.words, i);
     });
 
@@ -349,8 +370,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
         uint4 w = make_uint4(0, 0, 0, 0);
-        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
-            w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi) w = *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
@@ -420,13 +440,15 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
         for (int u = 0; u < kUnroll; ++u) {
             float s[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
-                if ((mk[u] >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
-            }
-            if (mk[u] && j == 0) {
+            for (int h = 0; h < G; ++h) s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
+            if (j == LPT - 1) {  // the lane holding the pinned sums
 #pragma unroll
-                for (int h = 0; h < G; ++h) scrow[static_cast<size_t>(tk[u]) * G + h] = s[h];
+                for (int h = 0; h < G; ++h)
+                    if ((mk[u] >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
+                if (mk[u]) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) scrow[static_cast<size_t>(tk[u]) * G + h] = s[h];
+                }
             }
         }
     }
@@ -490,22 +512,45 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
         s2[h] = 0;
     }
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    for (int c = wave; c < nc; c += nwaves) {
-        const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
-        const int cnt = P.bcnt[static_cast<size_t>(bg) * P.ncg + c];
-        for (int x = lane; x < cnt; x += 64) {
-            const int i = P.btok[lb + x];
-            const uint32_t meta = P.bmeta[lb + x];
+    // each wave takes every nwaves-th chunk; all of a lane's loads are issued
+    // before its first use
+    const int32_t* cnts = P.bcnt + static_cast<size_t>(bg) * P.ncg;
+    for (int c0 = wave; c0 < nc; c0 += nwaves * 4) {
+        int cn[4];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                if (!((meta >> h) & 1u)) continue;
-                const uint64_t E = fixed_weight(scrow[static_cast<size_t>(i) * G + h] - smax[h]);
-                if ((meta >> (8 + h)) & 1u) {
-                    sf[h] += E;
-                } else {
-                    s1[h] += E;
-                    s2[h] += static_cast<unsigned __int128>(E) * E;
+        for (int t = 0; t < 4; ++t) cn[t] = c0 + t * nwaves < nc ? cnts[c0 + t * nwaves] : 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = c0 + t * nwaves;
+            const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
+            for (int x0 = lane; x0 < cn[t]; x0 += 4 * 64) {
+                int ti[4];
+                uint32_t tm[4];
+                float sv[4][G];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int x = x0 + 64 * v;
+                    ti[v] = x < cn[t] ? P.btok[lb + x] : -1;
+                    tm[v] = x < cn[t] ? P.bmeta[lb + x] : 0u;
                 }
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+                        sv[v][h] = ((tm[v] >> h) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + h] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        if (!((tm[v] >> h) & 1u)) continue;
+                        const uint64_t E = fixed_weight(sv[v][h] - smax[h]);
+                        if ((tm[v] >> (8 + h)) & 1u) {
+                            sf[h] += E;
+                        } else {
+                            s1[h] += E;
+                            s2[h] += static_cast<unsigned __int128>(E) * E;
+                        }
+                    }
             }
         }
     }
@@ -589,7 +634,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
     uint32_t rank[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) rank[h] = static_cast<uint32_t>(nsel[h]);
-    block_sample_threshold<G>(SS, FS, R, b, g, P.seed_lo, P.seed_hi, rank, [&](int h, int i) {
+    block_sample_threshold<G>(SS, FS, R, group_words(P, bg), rank, [&](int h, int i) {
         return bit_of(P.bits + (bh0 + h) * P.words, i);
     });
     if (tid < G) {
@@ -603,17 +648,24 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
 }
 
 // ===========================================================================
-// gather: weighted online softmax over the union of the group's index sets
+// gather: weighted softmax over the union of the group's index sets, in two
+// passes over the listed tokens: (1) scores (score cache or K row) into LDS,
+// then per head the block max and the weights p = w exp(s - max); (2) a pure
+// stream of V rows accumulating sum_i p_i V_i.  Every weight is computed once.
 // ===========================================================================
+constexpr int kGatherUnrollV = 8;  // V rows in flight per lane group
+
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     constexpr int NW = kChunkThreads / 64;
     __shared__ int tok[kGatherChunk];
     __shared__ uint32_t tmeta[kGatherChunk];
     __shared__ uint32_t trow[kGatherChunk];
+    __shared__ float sp[G][kGatherChunk];  // scores, then weights
     __shared__ uint32_t wsum[NW];
     __shared__ HeadView hv[G];
-    __shared__ float wm[NW][G], wl[NW][G];
+    __shared__ float wred[NW][G];
+    __shared__ float hmax[G], hsum[G];
     __shared__ float wacc[NW][G][D];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -638,8 +690,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
         uint4 w = make_uint4(0, 0, 0, 0);
-        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
-            w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi) w = *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
@@ -673,125 +724,195 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
         }
     if (tid == 0 && P.gcounts && cnt) atomicAdd(&P.gcounts[2 * bg], static_cast<int>(cnt));
     __syncthreads();
+    const int n = static_cast<int>(cnt);
 
+    // (1) scores into LDS (-inf for heads the token does not belong to); K rows
+    // double-buffered: the next batch is in flight while this one is scored
     constexpr int LPT = D / 8, TPW = 64 / LPT;
     const int j = lane % LPT, slot = lane / LPT;
-    float qreg[G][8];
+    {
+        float qreg[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
+        const KVT* kbase = static_cast<const KVT*>(P.k);
+        const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
+        struct Batch {
+            Raw8 kr[kUnroll];
+            uint32_t mk[kUnroll];
+            int xs[kUnroll];
+        };
+        auto issue = [&](Batch& bt, int b0) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int x = b0 + u * TPW + slot;
+                bt.xs[u] = x < n ? x : -1;
+                bt.mk[u] = x < n ? tmeta[x] : 0u;
+                if (bt.mk[u] && !((bt.mk[u] >> 16) & 1u))
+                    load_raw(kbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.kr[u]);
+            }
+        };
+        auto score = [&](const Batch& bt) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const bool cached = (bt.mk[u] >> 16) & 1u;
+                float kf[8];
+                widen<KVT>(bt.kr[u], kf);
+                float sv[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) sv[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
+                if (j == LPT - 1 && bt.xs[u] >= 0) {
+                    const int x = bt.xs[u];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float v = cached ? scrow[static_cast<size_t>(tok[x]) * G + h] : sv[h];
+                        sp[h][x] = ((bt.mk[u] >> h) & 1u) ? v : -__builtin_inff();
+                    }
+                }
+            }
+        };
+        const int stride = nwaves * TPW * kUnroll;
+        int base = wave * TPW * kUnroll;
+        Batch A, B;
+        if (base < n) issue(A, base);
+        while (base < n) {
+            if (base + stride < n) issue(B, base + stride);
+            score(A);
+            base += stride;
+            if (base >= n) break;
+            if (base + stride < n) issue(A, base + stride);
+            score(B);
+            base += stride;
+        }
+    }
+    __syncthreads();
+    // per-head block max, then weights and their sum
+    {
+        float mx[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) mx[h] = -__builtin_inff();
+        for (int x = tid; x < n; x += nthr)
+#pragma unroll
+            for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], sp[h][x]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float v = mx[h];
+            for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+            if (lane == 0) wred[wave][h] = v;
+        }
+        __syncthreads();
+        if (tid < G) {
+            float v = -__builtin_inff();
+            for (int w = 0; w < NW; ++w) v = fmaxf(v, wred[w][tid]);
+            hmax[tid] = v;
+        }
+        __syncthreads();
+        float hm[G], ls[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            hm[h] = hmax[h];
+            ls[h] = 0.f;
+        }
+        for (int x = tid; x < n; x += nthr) {
+            const uint32_t meta = tmeta[x];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float sv = sp[h][x];
+                const float w = ((meta >> (8 + h)) & 1u) ? 1.0f : hv[h].wsamp;
+                const float p = (sv == -__builtin_inff()) ? 0.0f : w * __expf(sv - hm[h]);
+                sp[h][x] = p;
+                ls[h] += p;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float v = ls[h];
+            for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (lane == 0) wred[wave][h] = v;
+        }
+        __syncthreads();
+        if (tid < G) {
+            float v = 0.f;
+            for (int w = 0; w < NW; ++w) v += wred[w][tid];
+            hsum[tid] = v;
+        }
+    }
+    __syncthreads();
+
+    // (2) sum_i p_i V_i, V rows streamed kGatherUnrollV deep and double-buffered
+    float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
-    float ws[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) ws[h] = hv[h].wsamp;
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -__builtin_inff();
-        l[h] = 0.f;
-#pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
-    const KVT* kbase = static_cast<const KVT*>(P.k);
-    const KVT* vbase = static_cast<const KVT*>(P.v);
-    const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    const int n = static_cast<int>(cnt);
-    for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
-        float vf[kUnroll][8], kf[kUnroll][8];
-        uint32_t mk[kUnroll];
-        int tk[kUnroll];
-        // issue every row load of the batch first
+    {
+        const KVT* vbase = static_cast<const KVT*>(P.v);
+        struct VBatch {
+            Raw8 vr[kGatherUnrollV];
+            int x0;
+        };
+        auto issue = [&](VBatch& bt, int b0) {
+            bt.x0 = b0;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int x = base + u * TPW + slot;
-            const bool act = x < n;
-            const int xs = act ? x : 0;
-            tk[u] = tok[xs];
-            mk[u] = act ? tmeta[xs] : 0u;
-            const size_t roff = static_cast<size_t>(trow[xs]) * D + 8 * j;
-            load8(vbase + roff, vf[u]);
-            if (!((mk[u] >> 16) & 1u)) {
-                load8(kbase + roff, kf[u]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kf[u][e] = 0.f;
+            for (int u = 0; u < kGatherUnrollV; ++u) {
+                const int x = b0 + u * TPW + slot;
+                if (x < n) load_raw(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
             }
-        }
-        float s[kUnroll][G];
+        };
+        auto accumulate = [&](const VBatch& bt) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool cached = (mk[u] >> 16) & 1u;
+            for (int u = 0; u < kGatherUnrollV; ++u) {
+                const int x = bt.x0 + u * TPW + slot;
+                if (x >= n) continue;
+                float vf[8];
+                widen<KVT>(bt.vr[u], vf);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float st = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
-                s[u][h] = cached ? scrow[static_cast<size_t>(tk[u]) * G + h] : st;
+                for (int h = 0; h < G; ++h) {
+                    const float pw = sp[h][x];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(pw, vf[e], acc[h][e]);
+                }
             }
-        }
-        // one max update per batch and head, then the weighted accumulation
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = m[h];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if ((mk[u] >> h) & 1u) mx = fmaxf(mx, s[u][h]);
-            const float alpha = (mx == -__builtin_inff()) ? 1.0f : __expf(m[h] - mx);
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const bool on = (mk[u] >> h) & 1u;
-                const float w = ((mk[u] >> (8 + h)) & 1u) ? 1.0f : ws[h];
-                const float p = on ? w * __expf(s[u][h] - mx) : 0.0f;
-                l[h] += p;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, vf[u][e], acc[h][e]);
-            }
-            m[h] = mx;
+        };
+        const int stride = nwaves * TPW * kGatherUnrollV;
+        int base = wave * TPW * kGatherUnrollV;
+        VBatch A, B;
+        if (base < n) issue(A, base);
+        while (base < n) {
+            if (base + stride < n) issue(B, base + stride);
+            accumulate(A);
+            base += stride;
+            if (base >= n) break;
+            if (base + stride < n) issue(A, base + stride);
+            accumulate(B);
+            base += stride;
         }
     }
-    // merge the TPW token slots of the wave (lanes with equal j)
+    // token slots of the wave hold the same dims: plain sums
 #pragma unroll
-    for (int o = LPT; o < 64; o <<= 1) {
+    for (int o = LPT; o < 64; o <<= 1)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(m[h], o, 64), lo = __shfl_xor(l[h], o, 64);
-            const float mn = fmaxf(m[h], mo);
-            const float a = (mn == -__builtin_inff()) ? 0.0f : __expf(m[h] - mn);
-            const float bo = (mn == -__builtin_inff()) ? 0.0f : __expf(mo - mn);
-            l[h] = l[h] * a + lo * bo;
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ao = __shfl_xor(acc[h][e], o, 64);
-                acc[h][e] = acc[h][e] * a + ao * bo;
-            }
-            m[h] = mn;
-        }
-    }
+            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
     if (slot == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (j == 0) {
-                wm[wave][h] = m[h];
-                wl[wave][h] = l[h];
-            }
+        for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) wacc[wave][h][8 * j + e] = acc[h][e];
-        }
     }
     __syncthreads();
     for (int x = tid; x < G * (D + 2); x += nthr) {
         const int h = x / (D + 2), e = x - h * (D + 2);
-        float M = -__builtin_inff();
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][h]);
-        float v = 0.f;
+        float v;
         if (e == 0) {
-            v = M;
-        } else if (M != -__builtin_inff()) {
-            for (int w = 0; w < NW; ++w) {
-                const float sc = __expf(wm[w][h] - M);
-                v += (e == 1 ? wl[w][h] : wacc[w][h][e - 2]) * sc;
-            }
+            v = hmax[h];
+        } else if (e == 1) {
+            v = hsum[h];
+        } else {
+            v = 0.f;
+            for (int w = 0; w < NW; ++w) v += wacc[w][h][e - 2];
         }
         P.part[((bh0 + h) * P.ncg + c) * (D + 2) + e] = v;
     }
@@ -891,7 +1012,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(Plan P) {
         if (4 * qd < L) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
-                w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+                w = *reinterpret_cast<const uint4*>(group_words(P, b * P.Hkv + g) + 4 * qd);
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * qd + e;
                 if (i >= L) continue;

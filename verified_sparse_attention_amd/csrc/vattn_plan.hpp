@@ -60,6 +60,8 @@ struct Plan {
     int32_t* btok;   // [B*Hkv][ncg][cg] base-pass member tokens, ascending
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
+    uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
+    uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
     // outputs
     float* out;
     float* lse;
