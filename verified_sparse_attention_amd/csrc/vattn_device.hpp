@@ -175,6 +175,16 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&f)[8]) {
         f[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
     }
 }
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// fp32 rounded to the nearest bf16 (ties to even), returned as fp32.
+__device__ __forceinline__ float bf16_round(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __uint_as_float(u & 0xFFFF0000u);
+}
+
 struct Raw8 {  // one lane's 8 elements as loaded (bf16: one uint4; fp32: two float4)
     uint4 a, b;
 };
@@ -296,7 +306,7 @@ struct SelShared {
 // when `items` enumerates only part of a larger population (one bucket of it),
 // where a prefix threshold could also admit keys that were never visited.
 template <int NH, class Items>
-__device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items&& items,
+__device__ __forceinline__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items&& items,
                              bool exact = false) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -320,7 +330,7 @@ __device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items
 #pragma unroll
         for (int h = 0; h < NH; ++h) pre[h] = S.prefix[h];
         __syncthreads();
-        items([&](int h, uint64_t key) {
+        items([&](int h, uint64_t key) __attribute__((always_inline)) {
             if (!((act >> h) & 1u)) return;
             if (pass > 0 && ((key ^ pre[h]) >> (shift + 8)) != 0) return;
             atomicAdd(&S.hist[h][static_cast<uint32_t>(key >> shift) & 255u], 1u);
@@ -367,14 +377,15 @@ __device__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items
         __syncthreads();
     }
     if (exact) {
-        uint64_t lo_thr[NH];
+        uint32_t wmask = 0;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) lo_thr[h] = S.thr[h];
+        for (int h = 0; h < NH; ++h) wmask |= want[h] > 0 ? (1u << h) : 0u;
+        if (tid < NH) S.prefix[tid] = S.thr[tid];  // the prefix threshold, kept for the pass
         __syncthreads();
         if (tid < NH) S.thr[tid] = ~0ull;
         __syncthreads();
-        items([&](int h, uint64_t key) {
-            if (want[h] > 0 && key >= lo_thr[h]) atomicMin(&S.thr[h], key);
+        items([&](int h, uint64_t key) __attribute__((always_inline)) {
+            if (((wmask >> h) & 1u) && key >= S.prefix[h]) atomicMin(&S.thr[h], key);
         });
         __syncthreads();
     }
@@ -455,6 +466,9 @@ struct TopkShared {
     uint64_t thr[NH];
     uint32_t above[NH], cnt[NH], aux[NH], lo[NH], hi[NH];
     int bstar[NH];
+    float vmin[NH], scale[NH];  // per-head bucket map, read by the visitors
+    uint32_t mode[NH];          // 0 idle, 1 select, 2 emit everything
+    uint32_t want[NH];
 };
 
 // Score back from its order key.
@@ -472,46 +486,48 @@ __device__ __forceinline__ int topk_bucket(uint32_t ok, float vmin, float scale)
 }
 
 template <int NH, class Items, class Emit>
-__device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
+__device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
                            const uint32_t (&lo_ok)[NH], const uint32_t (&hi_ok)[NH], Items&& items,
                            Emit&& emit) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    bool act[NH], all[NH];
-    float vm[NH], sc[NH];
-    bool any = false;
+    // per-head parameters live in LDS: the visitors index them by a head number
+    // that need not be a compile-time constant after inlining
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        act[h] = want[h] > 0 && want[h] < total[h];
-        all[h] = want[h] > 0 && want[h] >= total[h];
-        any |= act[h];
+    for (int h = 0; h < NH; ++h) {  // compile-time head numbers: no indexing of the caller's arrays
+        if (tid != h) continue;
+        const bool act = want[h] > 0 && want[h] < total[h];
+        const bool all = want[h] > 0 && want[h] >= total[h];
+        T.want[h] = want[h];
         const float vmin = okey_value(lo_ok[h]), vmax = okey_value(hi_ok[h]);
         const float range = vmax - vmin;
         const float scale = static_cast<float>(kTopBuckets) / range;
         // a zero or non-finite range puts every key in bucket 0
         const bool ok = range > 0.0f && range < __builtin_inff() && scale < __builtin_inff();
-        vm[h] = vmin;
-        sc[h] = ok ? scale : 0.0f;
+        T.vmin[h] = vmin;
+        T.scale[h] = ok ? scale : 0.0f;
+        T.mode[h] = act ? 1u : all ? 2u : 0u;
+        T.cnt[h] = 0;
+        T.thr[h] = 0;
+        T.bstar[h] = -1;
+        T.above[h] = 0;
     }
-    if (tid < NH) {
-        T.cnt[tid] = 0;
-        T.thr[tid] = 0;
-        T.bstar[tid] = -1;
-        T.above[tid] = 0;
-    }
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) any |= want[h] > 0 && want[h] < total[h];
     for (int x = tid; x < NH * kTopBuckets; x += nthr) (&T.S.hist[0][0])[x] = 0;
     __syncthreads();
     if (any) {
         // (B) bucket histogram
-        items([&](int h, uint32_t ok, uint32_t) {
-            if (act[h]) atomicAdd(&T.S.hist[h][topk_bucket(ok, vm[h], sc[h])], 1u);
+        items([&](int h, uint32_t ok, uint32_t) __attribute__((always_inline)) {
+            if (T.mode[h] == 1u) atomicAdd(&T.S.hist[h][topk_bucket(ok, T.vmin[h], T.scale[h])], 1u);
         });
         __syncthreads();
         for (int h = wave; h < NH; h += nwaves) {
-            if (!act[h]) continue;
+            if (T.mode[h] != 1u) continue;
             int bin;
             uint32_t before;
-            wave_rank_bin<kTopBuckets>(T.S.hist[h], want[h], true, bin, before);
+            wave_rank_bin<kTopBuckets>(T.S.hist[h], T.want[h], true, bin, before);
             if (lane == 0) {
                 T.bstar[h] = bin;
                 T.above[h] = before;
@@ -519,18 +535,17 @@ __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const 
         }
         __syncthreads();
     }
-    int bs[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) bs[h] = T.bstar[h];
     // (C) emit the keys above the boundary bucket, list the boundary bucket
-    items([&](int h, uint32_t ok, uint32_t idx) {
-        if (all[h]) {
+    items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+        const uint32_t md = T.mode[h];
+        if (md == 2u) {
             emit(h, topk_key(ok, idx));
-        } else if (act[h]) {
-            const int bk = topk_bucket(ok, vm[h], sc[h]);
-            if (bk > bs[h]) {
+        } else if (md == 1u) {
+            const int bk = topk_bucket(ok, T.vmin[h], T.scale[h]);
+            const int bs = T.bstar[h];
+            if (bk > bs) {
                 emit(h, topk_key(ok, idx));
-            } else if (bk == bs[h]) {
+            } else if (bk == bs) {
                 const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
                 if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
             }
@@ -544,37 +559,37 @@ __device__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const 
     uint32_t fmask = 0;
 #pragma unroll
     for (int h = 0; h < NH; ++h)
-        if (act[h] && bs[h] >= 0 && T.cnt[h] > static_cast<uint32_t>(kListCap)) fmask |= 1u << h;
+        if (T.mode[h] == 1u && T.bstar[h] >= 0 && T.cnt[h] > static_cast<uint32_t>(kListCap)) fmask |= 1u << h;
     for (int x = tid; x < NH * kListCap; x += nthr) {
         const int h = x / kListCap, e = x - h * kListCap;
-        if (act[h] && bs[h] >= 0 && !((fmask >> h) & 1u))
-            list_rank_pick(T.list[h], static_cast<int>(T.cnt[h]), want[h] - T.above[h], e, &T.thr[h]);
+        if (T.mode[h] == 1u && T.bstar[h] >= 0 && !((fmask >> h) & 1u))
+            list_rank_pick(T.list[h], static_cast<int>(T.cnt[h]), T.want[h] - T.above[h], e, &T.thr[h]);
     }
     __syncthreads();
     for (int x = tid; x < NH * kListCap; x += nthr) {
         const int h = x / kListCap, e = x - h * kListCap;
-        if (act[h] && bs[h] >= 0 && !((fmask >> h) & 1u) && e < static_cast<int>(T.cnt[h]) &&
+        if (T.mode[h] == 1u && T.bstar[h] >= 0 && !((fmask >> h) & 1u) && e < static_cast<int>(T.cnt[h]) &&
             T.list[h][e] >= T.thr[h])
             emit(h, T.list[h][e]);
     }
     if (fmask) {  // rare: a crowded boundary bucket, ranked by the radix select
         uint32_t fw[NH];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? want[h] - T.above[h] : 0u;
+        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? T.want[h] - T.above[h] : 0u;
         __syncthreads();
-        block_select<NH>(T.S, fw, [&](auto&& visit) {
-            items([&](int h, uint32_t ok, uint32_t idx) {
-                if (((fmask >> h) & 1u) && topk_bucket(ok, vm[h], sc[h]) == bs[h]) visit(h, topk_key(ok, idx));
+        block_select<NH>(T.S, fw, [&](auto&& visit) __attribute__((always_inline)) {
+            items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+                if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h])
+                    visit(h, topk_key(ok, idx));
             });
         }, true);
-        uint64_t ft[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) ft[h] = T.S.thr[h];
-        items([&](int h, uint32_t ok, uint32_t idx) {
-            if (((fmask >> h) & 1u) && topk_bucket(ok, vm[h], sc[h]) == bs[h] && topk_key(ok, idx) >= ft[h])
+        __syncthreads();
+        items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+            if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h] &&
+                topk_key(ok, idx) >= T.S.thr[h])
                 emit(h, topk_key(ok, idx));
         });
-        if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = ft[tid];
+        if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = T.S.thr[tid];
     }
     __syncthreads();
 }
@@ -593,12 +608,12 @@ struct SampShared {
     uint32_t hist[NH][kSampBins];
     uint64_t list[NH][kListCap];
     uint64_t thr[NH];
-    uint32_t before[NH], cnt[NH];
+    uint32_t before[NH], cnt[NH], rank[NH];
     int bin[NH];
 };
 
 template <int NH, class InFixed>
-__device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions& R,
+__device__ __forceinline__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions R,
                                        const uint32_t* __restrict__ uw, const uint32_t (&rank)[NH],
                                        InFixed&& in_fixed) {
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -606,20 +621,21 @@ __device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, cons
     constexpr int kShift = 32 - kSampBits;
     bool any = false;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) any |= rank[h] > 0;
-    if (tid < NH) {
-        S.cnt[tid] = 0;
-        S.thr[tid] = 0;
+    for (int h = 0; h < NH; ++h) {
+        any |= rank[h] > 0;
+        if (tid == h) {  // compile-time head numbers: no indexing of the caller's array
+            S.cnt[h] = 0;
+            S.thr[h] = 0;
+            S.rank[h] = rank[h];
+        }
     }
-    if (!any) {
-        __syncthreads();
-        return;
-    }
+    __syncthreads();
+    if (!any) return;
     for (int h = wave; h < NH; h += nwaves) {
-        if (rank[h] == 0) continue;
+        if (S.rank[h] == 0) continue;
         int bin;
         uint32_t before;
-        wave_rank_bin<kSampBins>(S.hist[h], rank[h], false, bin, before);
+        wave_rank_bin<kSampBins>(S.hist[h], S.rank[h], false, bin, before);
         if (lane == 0) {
             S.bin[h] = bin;
             S.before[h] = before;
@@ -666,14 +682,14 @@ __device__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, cons
     for (int x = tid; x < NH * kListCap; x += nthr) {
         const int h = x / kListCap, e = x - h * kListCap;
         if (bn[h] >= 0 && !((fmask >> h) & 1u))
-            list_rank_pick(S.list[h], static_cast<int>(S.cnt[h]), rank[h] - S.before[h], e, &S.thr[h]);
+            list_rank_pick(S.list[h], static_cast<int>(S.cnt[h]), S.rank[h] - S.before[h], e, &S.thr[h]);
     }
     __syncthreads();
     if (fmask) {  // rare: a crowded bin, ranked by the radix select over its tokens
         uint32_t fw[NH];
 #pragma unroll
-        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? rank[h] - S.before[h] : 0u;
-        block_select<NH>(F, fw, [&](auto&& visit) {
+        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? S.rank[h] - S.before[h] : 0u;
+        block_select<NH>(F, fw, [&](auto&& visit) __attribute__((always_inline)) {
             for (int qd = q0 + tid; qd <= q1; qd += nthr) {
                 const uint4 w = *reinterpret_cast<const uint4*>(uw + 4 * qd);
 #pragma unroll

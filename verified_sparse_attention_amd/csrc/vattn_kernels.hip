@@ -33,6 +33,7 @@
 namespace vattn {
 
 constexpr int kUnroll = 4;  // token rows in flight per lane group in the streaming loops
+constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
 __device__ __forceinline__ bool bit_of(const uint32_t* row, int i) {
     return (row[i >> 5] >> (i & 31)) & 1u;
@@ -201,13 +202,15 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             hi[h] = TS.hi[h];
         }
         const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) {
+        const int cp = P.cp, ncp = P.ncp, kcap = P.kcap;
+        uint64_t* __restrict__ cand = P.cand;
+        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
             for (int t = t0 + tid; t < t1; t += nthr)
 #pragma unroll
-                for (int h = 0; h < G; ++h) f(h, keys[h * P.cp + (t - cbase)], static_cast<uint32_t>(t));
-        }, [&](int h, uint64_t key) {
+                for (int h = 0; h < G; ++h) f(h, keys[h * cp + (t - cbase)], static_cast<uint32_t>(t));
+        }, [&](int h, uint64_t key) __attribute__((always_inline)) {
             const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
-            if (pos < static_cast<uint32_t>(kp)) P.cand[((bh0 + h) * P.ncp + c) * P.kcap + pos] = key;
+            if (pos < static_cast<uint32_t>(kp)) cand[((bh0 + h) * ncp + c) * kcap + pos] = key;
         });
         // order-key bracket of the candidates for the merge: [threshold key, chunk max]
         if (tid < G) {
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
 // ===========================================================================
 // select: exact top-k, fixed-set bitmap, tail histograms, base threshold
 // ===========================================================================
-__device__ __forceinline__ int chunk_candidates(const Plan& P, const Regions& R, int c) {
-    const int a = max(c * P.cp, R.lo), e = min((c + 1) * P.cp, R.hi);
+__device__ __forceinline__ int chunk_candidates(int cp, const Regions R, int c) {
+    const int a = max(c * cp, R.lo), e = min((c + 1) * cp, R.hi);
     return a < e ? min(R.k, e - a) : 0;
 }
 
@@ -239,6 +242,10 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
     const uint32_t* uwg = group_words(P, bg);
+    // lambdas below capture these locals, never the kernel argument itself
+    const int cp = P.cp, ncp = P.ncp, kcap = P.kcap, words = P.words;
+    const uint64_t* __restrict__ cand = P.cand;
+    uint32_t* __restrict__ bits = P.bits;
     if (tid == 0 && P.gcounts) {
         P.gcounts[2 * bg] = 0;
         P.gcounts[2 * bg + 1] = 0;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
     if (R.k > 0) {
         uint32_t want[G], total[G], lo[G], hi[G];
         uint32_t tot = 0;
-        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(P, R, c));
+        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(cp, R, c));
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             want[h] = static_cast<uint32_t>(R.k);
@@ -280,26 +287,34 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
             lo[h] = 0xFFFFFFFFu;
             hi[h] = 0;
             for (int c = 0; c < P.ncp; ++c) {
-                if (chunk_candidates(P, R, c) == 0) continue;
+                if (chunk_candidates(cp, R, c) == 0) continue;
                 const uint32_t* cr = P.crange + ((bh0 + h) * P.ncp + c) * 2;
                 lo[h] = min(lo[h], cr[0]);
                 hi[h] = max(hi[h], cr[1]);
             }
         }
-        const int slots = P.ncp * P.kcap;
-        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) {
-            for (int x = tid; x < slots; x += nthr) {
-                const int c = x / P.kcap, p = x - c * P.kcap;
-                if (p >= chunk_candidates(P, R, c)) continue;
+        const int slots = ncp * kcap;
+        constexpr int kBatch = 8;  // candidate keys loaded before any is visited
+        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
+            for (int x0 = tid; x0 < G * slots; x0 += kBatch * nthr) {
+                uint64_t kk[kBatch];
+                int hh[kBatch];
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint64_t key = P.cand[((bh0 + h) * P.ncp + c) * P.kcap + p];
-                    f(h, static_cast<uint32_t>(key >> 32), ~static_cast<uint32_t>(key));
+                for (int t = 0; t < kBatch; ++t) {
+                    const int x = x0 + t * nthr;
+                    const int h = x / slots, sl = x - h * slots;
+                    const int c = sl / kcap, p = sl - c * kcap;
+                    const bool ok = x < G * slots && p < chunk_candidates(cp, R, c);
+                    hh[t] = ok ? h : -1;
+                    kk[t] = ok ? cand[((bh0 + h) * ncp + c) * kcap + p] : 0ull;
                 }
+#pragma unroll
+                for (int t = 0; t < kBatch; ++t)
+                    if (hh[t] >= 0) f(hh[t], static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
             }
-        }, [&](int h, uint64_t key) {
+        }, [&](int h, uint64_t key) __attribute__((always_inline)) {
             const uint32_t i = ~static_cast<uint32_t>(key);
-            atomicOr(&P.bits[(bh0 + h) * P.words + (i >> 5)], 1u << (i & 31));
+            atomicOr(&bits[(bh0 + h) * words + (i >> 5)], 1u << (i & 31));
             atomicSub(&SS.hist[h][uwg[i] >> (32 - kSampBits)], 1u);
         });
     } else {
@@ -314,8 +329,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
     uint32_t rank[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) rank[h] = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
-    block_sample_threshold<G>(SS, TS.S, R, uwg, rank, [&](int h, int i) {
-        return bit_of_coherent(P.bits + (bh0 + h) * P.words, i);
+    block_sample_threshold<G>(SS, TS.S, R, uwg, rank, [&](int h, int i) __attribute__((always_inline)) {
+        return bit_of_coherent(bits + (bh0 + h) * words, i);
     });
 
     if (tid < G) {
@@ -476,6 +491,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
     __shared__ float smax[G];
     __shared__ uint64_t red[kGroupThreads / 64][G][4];
     __shared__ int nsel[G], nfin[G];
+    __shared__ int coff[kMaxChunks + 1];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     const int bg = blockIdx.x, b = bg / P.Hkv, g = bg % P.Hkv;
@@ -512,46 +528,62 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
         s2[h] = 0;
     }
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    // each wave takes every nwaves-th chunk; all of a lane's loads are issued
-    // before its first use
-    const int32_t* cnts = P.bcnt + static_cast<size_t>(bg) * P.ncg;
-    for (int c0 = wave; c0 < nc; c0 += nwaves * 4) {
-        int cn[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cn[t] = c0 + t * nwaves < nc ? cnts[c0 + t * nwaves] : 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int c = c0 + t * nwaves;
-            const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
-            for (int x0 = lane; x0 < cn[t]; x0 += 4 * 64) {
-                int ti[4];
-                uint32_t tm[4];
-                float sv[4][G];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int x = x0 + 64 * v;
-                    ti[v] = x < cn[t] ? P.btok[lb + x] : -1;
-                    tm[v] = x < cn[t] ? P.bmeta[lb + x] : 0u;
-                }
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        sv[v][h] = ((tm[v] >> h) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + h] : 0.0f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        if (!((tm[v] >> h) & 1u)) continue;
-                        const uint64_t E = fixed_weight(sv[v][h] - smax[h]);
-                        if ((tm[v] >> (8 + h)) & 1u) {
-                            sf[h] += E;
-                        } else {
-                            s1[h] += E;
-                            s2[h] += static_cast<unsigned __int128>(E) * E;
-                        }
-                    }
+    // members of all base chunks as one flat range: a prefix over the chunk
+    // counts, then every thread loads its members' tokens and scores before use
+    {
+        const int32_t* cnts = P.bcnt + static_cast<size_t>(bg) * P.ncg;
+        for (int c = tid; c < nc; c += nthr) coff[c] = cnts[c];
+        __syncthreads();
+        if (wave == 0) {  // exclusive prefix over nc <= kMaxChunks counts, 64 at a time
+            uint32_t carry = 0;
+            for (int c0 = 0; c0 < nc; c0 += 64) {
+                const uint32_t v = c0 + lane < nc ? static_cast<uint32_t>(coff[c0 + lane]) : 0u;
+                const uint32_t inc = wave_incl_scan(v);
+                if (c0 + lane < nc) coff[c0 + lane] = static_cast<int>(carry + inc - v);
+                carry += __shfl(inc, 63, 64);
             }
+            if (lane == 0) coff[nc] = static_cast<int>(carry);
+        }
+        __syncthreads();
+        const int total = coff[nc];
+        constexpr int kMemBatch = G <= 4 ? 4 : 2;
+        for (int y0 = tid; y0 < total; y0 += kMemBatch * nthr) {
+            int ti[kMemBatch];
+            uint32_t tm[kMemBatch];
+#pragma unroll
+            for (int v = 0; v < kMemBatch; ++v) {
+                const int y = y0 + v * nthr;
+                ti[v] = -1;
+                tm[v] = 0u;
+                if (y < total) {
+                    int lo = 0, hi = nc - 1;  // chunk c with coff[c] <= y < coff[c + 1]
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (coff[mid] <= y) lo = mid; else hi = mid - 1;
+                    }
+                    const size_t at = (static_cast<size_t>(bg) * P.ncg + lo) * P.cg + (y - coff[lo]);
+                    ti[v] = P.btok[at];
+                    tm[v] = P.bmeta[at];
+                }
+            }
+            float sv[kMemBatch][G];
+#pragma unroll
+            for (int v = 0; v < kMemBatch; ++v)
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    sv[v][h] = ((tm[v] >> h) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + h] : 0.0f;
+#pragma unroll
+            for (int v = 0; v < kMemBatch; ++v)
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint64_t E = ((tm[v] >> h) & 1u) ? fixed_weight(sv[v][h] - smax[h]) : 0ull;
+                    if ((tm[v] >> (8 + h)) & 1u) {
+                        sf[h] += E;
+                    } else {
+                        s1[h] += E;
+                        s2[h] += static_cast<unsigned __int128>(E) * E;
+                    }
+                }
         }
     }
     // exact reduction (integer sums are order independent)
@@ -634,8 +666,10 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
     uint32_t rank[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) rank[h] = static_cast<uint32_t>(nsel[h]);
-    block_sample_threshold<G>(SS, FS, R, group_words(P, bg), rank, [&](int h, int i) {
-        return bit_of(P.bits + (bh0 + h) * P.words, i);
+    const uint32_t* __restrict__ bits = P.bits;
+    const int words = P.words;
+    block_sample_threshold<G>(SS, FS, R, group_words(P, bg), rank, [&](int h, int i) __attribute__((always_inline)) {
+        return bit_of(bits + (bh0 + h) * words, i);
     });
     if (tid < G) {
         const int h = tid, n = nfin[h];
@@ -653,7 +687,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
 // then per head the block max and the weights p = w exp(s - max); (2) a pure
 // stream of V rows accumulating sum_i p_i V_i.  Every weight is computed once.
 // ===========================================================================
-constexpr int kGatherUnrollV = 8;  // V rows in flight per lane group
+constexpr int kGatherUnrollV = 4;  // V rows per batch and lane group (two batches in flight)
 
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
@@ -726,64 +760,130 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     __syncthreads();
     const int n = static_cast<int>(cnt);
 
-    // (1) scores into LDS (-inf for heads the token does not belong to); K rows
-    // double-buffered: the next batch is in flight while this one is scored
+    // (1) scores into LDS (-inf for heads the token does not belong to).
+    // Tokens of the base pass take their cached pinned scores (independent
+    // loads, one pass); the others are scored from their K rows below.
     constexpr int LPT = D / 8, TPW = 64 / LPT;
     const int j = lane % LPT, slot = lane / LPT;
-    {
+    const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
+    const KVT* kbase = static_cast<const KVT*>(P.k);
+    for (int x = tid; x < n; x += nthr) {
+        const uint32_t m = tmeta[x];
+        if ((m >> 16) & 1u) {
+            float v[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) v[h] = scrow[static_cast<size_t>(tok[x]) * G + h];
+#pragma unroll
+            for (int h = 0; h < G; ++h) sp[h][x] = ((m >> h) & 1u) ? v[h] : -__builtin_inff();
+        }
+    }
+    if constexpr (sizeof(KVT) == 2) {
+        // bf16 keys: 16-token tiles on the matrix cores.  A = K rows (16 x D),
+        // B = the scaled query split into three bf16 terms q_hi + q_lo + q_lo2
+        // (residual ~2^-25 |q|), three columns per head, four heads per column
+        // block; bf16 x bf16 products are exact and accumulate in fp32.
+        constexpr int KB = D / 32, NCB = (G + 3) / 4;
+        const int col = lane & 15, kq = lane >> 4;
+        bf16x8 qb[NCB][KB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int hh = cb * 4 + col / 3, term = col % 3;
+            const bool live = col < 12 && hh < G;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float part = 0.0f;
+                    if (live) {
+                        const float qsv = P.q[(bh0 + hh) * D + 32 * kb + 8 * kq + e] * P.scale32;
+                        const float hi = bf16_round(qsv);
+                        const float lo = bf16_round(qsv - hi);
+                        part = term == 0 ? hi : term == 1 ? lo : bf16_round((qsv - hi) - lo);
+                    }
+                    qb[cb][kb][e] = static_cast<__bf16>(part);
+                }
+        }
+        const int ntile = (n + 15) / 16;
+        auto tile_row = [&](int x0) __attribute__((always_inline)) {
+            // row of this lane's token; cached or absent tokens read a row that
+            // is already needed (their result is not used)
+            const int x = x0 + col;
+            const int xr = x < n ? x : x0;
+            const uint32_t m = tmeta[xr];
+            return ((m >> 16) & 1u) ? trow[x0] : trow[xr];
+        };
+        struct KTile {
+            uint4 a[KB];
+        };
+        auto issue = [&](KTile& t, int x0) __attribute__((always_inline)) {
+            const KVT* rp = kbase + static_cast<size_t>(tile_row(x0)) * D + 8 * kq;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) t.a[kb] = *reinterpret_cast<const uint4*>(rp + 32 * kb);
+        };
+        auto score = [&](const KTile& t, int x0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.a[kb]), qb[cb][kb],
+                                                                 acc, 0, 0, 0);
+                const int hh = cb * 4 + col / 3;
+                const bool writer = col < 12 && col % 3 == 0 && hh < G;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = acc[r] + dpp<0x101>(acc[r]) + dpp<0x102>(acc[r]);  // row_shl:1, :2
+                    const int x = x0 + 4 * kq + r;
+                    if (writer && x < n) {
+                        const uint32_t m = tmeta[x];
+                        if (!((m >> 16) & 1u)) sp[hh][x] = ((m >> hh) & 1u) ? sv : -__builtin_inff();
+                    }
+                }
+            }
+        };
+        int tI = wave;
+        KTile A, B;
+        if (tI < ntile) issue(A, 16 * tI);
+        while (tI < ntile) {
+            if (tI + nwaves < ntile) issue(B, 16 * (tI + nwaves));
+            score(A, 16 * tI);
+            tI += nwaves;
+            if (tI >= ntile) break;
+            if (tI + nwaves < ntile) issue(A, 16 * (tI + nwaves));
+            score(B, 16 * tI);
+            tI += nwaves;
+        }
+    } else {
         float qreg[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
-        const KVT* kbase = static_cast<const KVT*>(P.k);
-        const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-        struct Batch {
+        for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
             Raw8 kr[kUnroll];
             uint32_t mk[kUnroll];
             int xs[kUnroll];
-        };
-        auto issue = [&](Batch& bt, int b0) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int x = b0 + u * TPW + slot;
-                bt.xs[u] = x < n ? x : -1;
-                bt.mk[u] = x < n ? tmeta[x] : 0u;
-                if (bt.mk[u] && !((bt.mk[u] >> 16) & 1u))
-                    load_raw(kbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.kr[u]);
+                const int x = base + u * TPW + slot;
+                xs[u] = x < n ? x : -1;
+                mk[u] = x < n ? tmeta[x] : 0u;
+                load_raw(kbase + static_cast<size_t>(trow[x < n ? x : 0]) * D + 8 * j, kr[u]);
             }
-        };
-        auto score = [&](const Batch& bt) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const bool cached = (bt.mk[u] >> 16) & 1u;
+                const bool cached = (mk[u] >> 16) & 1u;
                 float kf[8];
-                widen<KVT>(bt.kr[u], kf);
+                widen<KVT>(kr[u], kf);
                 float sv[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) sv[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-                if (j == LPT - 1 && bt.xs[u] >= 0) {
-                    const int x = bt.xs[u];
+                if (j == LPT - 1 && xs[u] >= 0 && !cached) {
+                    const int x = xs[u];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float v = cached ? scrow[static_cast<size_t>(tok[x]) * G + h] : sv[h];
-                        sp[h][x] = ((bt.mk[u] >> h) & 1u) ? v : -__builtin_inff();
-                    }
+                    for (int h = 0; h < G; ++h) sp[h][x] = ((mk[u] >> h) & 1u) ? sv[h] : -__builtin_inff();
                 }
             }
-        };
-        const int stride = nwaves * TPW * kUnroll;
-        int base = wave * TPW * kUnroll;
-        Batch A, B;
-        if (base < n) issue(A, base);
-        while (base < n) {
-            if (base + stride < n) issue(B, base + stride);
-            score(A);
-            base += stride;
-            if (base >= n) break;
-            if (base + stride < n) issue(A, base + stride);
-            score(B);
-            base += stride;
         }
     }
     __syncthreads();
@@ -852,24 +952,25 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
             Raw8 vr[kGatherUnrollV];
             int x0;
         };
-        auto issue = [&](VBatch& bt, int b0) {
+        // rows past the list end reread the last row with weight 0 (no branches)
+        auto issue = [&](VBatch& bt, int b0) __attribute__((always_inline)) {
             bt.x0 = b0;
 #pragma unroll
             for (int u = 0; u < kGatherUnrollV; ++u) {
-                const int x = b0 + u * TPW + slot;
-                if (x < n) load_raw(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
+                const int x = min(b0 + u * TPW + slot, n - 1);
+                load_raw(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
             }
         };
-        auto accumulate = [&](const VBatch& bt) {
+        auto accumulate = [&](const VBatch& bt) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < kGatherUnrollV; ++u) {
                 const int x = bt.x0 + u * TPW + slot;
-                if (x >= n) continue;
+                const int xc = min(x, n - 1);
                 float vf[8];
                 widen<KVT>(bt.vr[u], vf);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float pw = sp[h][x];
+                    const float pw = x < n ? sp[h][xc] : 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(pw, vf[e], acc[h][e]);
                 }
@@ -922,7 +1023,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
 // combine: merge chunk partials; counts and statistics
 // ===========================================================================
 constexpr int kCombineThreads = 128;
-constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
 __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
     __shared__ float wsh[kMaxChunks];
