@@ -15,7 +15,6 @@ fp32 reference, and the CPU oracle timed on the host cores.
 """
 import argparse
 import ctypes as C
-import hashlib
 import json
 import os
 import sys
@@ -68,14 +67,6 @@ class HipEvents:
             self.rt.hipEventDestroy(C.c_void_p(h))
 
 
-def source_hash():
-    h = hashlib.sha1()
-    for f in ("vattn_kernels.hip", "vattn_device.hpp", "vattn_plan.hpp"):
-        with open(os.path.join(ROOT, "verified_sparse_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:12]
-
-
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -124,8 +115,10 @@ def main():
 
     steps, warm = (min(args.steps, 5), min(args.warmup, 2)) if args.profile else (args.steps, args.warmup)
     if args.profile:
-        # a plain device copy of known size: calibrates the HBM byte counters
-        cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # a plain device copy of known size, the last copy before the decode steps:
+        # calibrates the HBM byte counters
+        from verified_sparse_attention_amd import profile_summary
+        cal_src = torch.empty(profile_summary.CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         cal_dst = torch.empty_like(cal_src)
         cal_dst.copy_(cal_src)
         torch.cuda.synchronize()
@@ -194,13 +187,16 @@ def main():
     dom_bytes = per_kernel_bytes.get(dom_name)
     achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9 if dom_bytes else None
 
+    # HBM bytes per launch from the committed counter summary, if it was taken
+    # with the current kernel sources
     traffic = None
-    pmc_file = os.path.join(ROOT, "profiles", "%s_%s.pmc.json" % (dom_name, w.name))
+    pmc_file = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % w.name)
     if os.path.exists(pmc_file):
+        from verified_sparse_attention_amd import build as vbuild
         with open(pmc_file) as f:
             pmc = json.load(f)
-        if pmc.get("source_hash") == source_hash():
-            traffic = pmc.get("hbm_bytes_per_launch")
+        if pmc.get("source_hash") == vbuild.source_hash():
+            traffic = pmc.get("kernels", {}).get("k_" + dom_name, {}).get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,

@@ -1,4 +1,5 @@
 """Builds libvattn.so (the gfx950 HIP library behind include/vattn.h) in-tree."""
+import hashlib
 import os
 import subprocess
 import sys
@@ -18,6 +19,16 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-I", os.path.join(PKG, "csrc"),
 ]
+
+
+def source_hash() -> str:
+    """Short digest of the kernel sources; hardware-counter summaries record it so a
+    summary taken before a kernel change is recognised as stale."""
+    h = hashlib.sha1()
+    for f in ("vattn_kernels.hip", "vattn_device.hpp", "vattn_plan.hpp"):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
 
 
 def build(verbose=False) -> str:

@@ -1,0 +1,162 @@
+"""Turns rocprofv3 output of a bench.py run into the short text summaries kept
+under profiles/.
+
+  python -m verified_sparse_attention_amd.profile_summary stats \
+      --trace DIR --workload NAME --cmd "rocprofv3 ... -- python3 bench.py" --out FILE.txt
+      kernel-trace statistics (rocprofv3 --kernel-trace --stats --output-format csv):
+      calls, mean / min / max duration per kernel.
+
+  python -m verified_sparse_attention_amd.profile_summary traffic \
+      --fetch CSV --write CSV --workload NAME --cmd-fetch "..." --cmd-write "..." --out FILE.json
+      HBM bytes per dispatch from two counter runs (FETCH_SIZE, then WRITE_SIZE,
+      both in KiB per dispatch).  Each counter is scaled by what it reads for the
+      plain device copy that `bench.py --profile` makes just before its decode
+      steps (a copy of a known size reads and writes that many bytes), so the
+      result is in bytes regardless of how the counter aggregates its channels.
+
+The traffic file carries the digest of the kernel sources it was taken with;
+bench.py reports `traffic` only while that digest matches the current sources.
+"""
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+from . import build as _build
+
+# must match the calibration copy in bench.py --profile
+CALIBRATION_BYTES = 256 << 20
+STAGE_KERNELS = ("k_predict", "k_select", "k_base", "k_budget", "k_gather", "k_combine", "k_emit",
+                 "k_project")
+
+
+def _demangle(name):
+    try:
+        out = subprocess.run(["c++filt", name], capture_output=True, text=True, check=True).stdout
+        return out.strip()
+    except (OSError, subprocess.CalledProcessError):
+        return name
+
+
+def _short(name):
+    dm = _demangle(name)
+    for k in STAGE_KERNELS:
+        if "vattn::%s" % k in dm or "vattn::%s<" % k in dm:
+            tmpl = dm.split("vattn::%s" % k, 1)[1]
+            tmpl = tmpl.split("(", 1)[0]
+            return k + tmpl
+    return dm[:60]
+
+
+def _stage(name):
+    dm = _demangle(name)
+    for k in STAGE_KERNELS:
+        if "vattn::%s" % k in dm:
+            return k
+    return None
+
+
+def _find(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit("no file matches %s" % pattern)
+    return hits[0]
+
+
+def stats(args):
+    path = _find(os.path.join(args.trace, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# rocprofv3 kernel-trace statistics, workload %s" % args.workload,
+             "# command: %s" % args.cmd,
+             "# kernel sources digest: %s" % _build.source_hash(),
+             "# durations in microseconds; every dispatch of the run is counted "
+             "(warm-up, timed, per-stage-timed and rate-check steps)",
+             "%-40s %7s %10s %10s %10s %7s" % ("kernel", "calls", "mean_us", "min_us", "max_us", "share")]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("%-40s %7d %10.2f %10.2f %10.2f %6.1f%%" % (
+            _short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / total))
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
+def _per_dispatch(path, counter):
+    """{dispatch id: (kernel name, summed counter value)} in dispatch order."""
+    acc = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = acc.get(d, (r["Kernel_Name"], 0.0))
+        acc[d] = (name, v + float(r["Counter_Value"]))
+    return acc
+
+
+def _calibration(disp):
+    """The copy just before the first decode-step kernel of the run."""
+    first = min((d for d, (n, _) in disp.items() if _stage(n) == "k_predict"), default=None)
+    if first is None:
+        raise SystemExit("no k_predict dispatch in the counter file")
+    cands = [d for d, (n, _) in disp.items() if "copyBuffer" in n and d < first]
+    if not cands:
+        raise SystemExit("no calibration copy before the first decode step")
+    return disp[max(cands)][1]
+
+
+def traffic(args):
+    fetch = _per_dispatch(args.fetch, "FETCH_SIZE")
+    write = _per_dispatch(args.write, "WRITE_SIZE")
+    cal_f, cal_w = _calibration(fetch), _calibration(write)
+    kib = CALIBRATION_BYTES / 1024.0
+    f_scale, w_scale = kib / cal_f, kib / cal_w
+    out = {"workload": args.workload, "source_hash": _build.source_hash(),
+           "commands": {"fetch": args.cmd_fetch, "write": args.cmd_write},
+           "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_kib": round(cal_f, 2),
+                           "write_kib": round(cal_w, 2), "fetch_scale": round(f_scale, 4),
+                           "write_scale": round(w_scale, 4)},
+           "kernels": {}}
+    for stage in STAGE_KERNELS:
+        fs = [v for n, v in fetch.values() if _stage(n) == stage]
+        ws = [v for n, v in write.values() if _stage(n) == stage]
+        if not fs or not ws:
+            continue
+        fk, wk = sum(fs) / len(fs), sum(ws) / len(ws)
+        out["kernels"][stage] = {
+            "dispatches": [len(fs), len(ws)],
+            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+            "hbm_bytes_per_launch": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("--trace", required=True)
+    a.add_argument("--workload", required=True)
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--out", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--cmd-fetch", required=True)
+    b.add_argument("--cmd-write", required=True)
+    b.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    (stats if args.mode == "stats" else traffic)(args)
+
+
+if __name__ == "__main__":
+    main()
