@@ -141,10 +141,14 @@ def test_z_matches_oracle_and_status_strings(lib):
 def test_profiled_entry_point_argument_checks(lib):
     inp, cfg = _inputs(), _cfg()
     outs = vsa.vattn_outputs(256, 256, None, 0, None, None, None, 0.0)
-    ev = (C.c_void_p * 8)(*([256] * 8))
+    ne = vsa.NUM_STAGES + 1
+    ev = (C.c_void_p * ne)(*([256] * ne))
     f = lib.vattn_decode_profiled
-    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, None, 8) == 1
-    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, 7) == 2
-    ev0 = (C.c_void_p * 8)(*([256] * 7 + [None]))
-    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev0, 8) == 1
-    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, 8) == 5
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, None, ne) == 1
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, ne - 1) == 2
+    ev0 = (C.c_void_p * ne)(*([256] * (ne - 1) + [None]))
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev0, ne) == 1
+    assert f(C.byref(inp), C.byref(cfg), C.byref(outs), None, 0, None, ev, ne) == 5
+    assert len(vsa.STAGES) == vsa.NUM_STAGES
+    text = open(HEADER).read()
+    assert re.search(r"#define VATTN_NUM_STAGES %d\b" % vsa.NUM_STAGES, text)

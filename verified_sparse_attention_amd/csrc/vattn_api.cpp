@@ -97,7 +97,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, shist, hh, btok, bmeta, bcnt, uw, crange, total;
+    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, btok, bmeta, bcnt, uw, crange, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -117,8 +117,10 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHq * s.ncg * sizeof(float));
     L.part = off;
     off += align_up(BHq * s.ncg * static_cast<size_t>(in->d + 2) * sizeof(float));
-    L.shist = off;
-    off += align_up(BHkv * s.ncp * vattn::kSampBins * sizeof(uint32_t));
+    L.soff = off;
+    off += align_up(BHkv * s.ncp * (vattn::kSampBins + 1) * sizeof(uint32_t));
+    L.slist = off;
+    off += align_up(BHkv * s.ncp * static_cast<size_t>(s.cp) * sizeof(int32_t));
     L.hh = off;
     off += align_up(BHq * vattn::kSampBins * sizeof(uint32_t));
     L.btok = off;
@@ -211,7 +213,8 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.sc = reinterpret_cast<float*>(ws + L.sc);
     p.cmax = reinterpret_cast<float*>(ws + L.cmax);
     p.part = reinterpret_cast<float*>(ws + L.part);
-    p.shist = reinterpret_cast<uint32_t*>(ws + L.shist);
+    p.soff = reinterpret_cast<uint32_t*>(ws + L.soff);
+    p.slist = reinterpret_cast<int32_t*>(ws + L.slist);
     p.hh = reinterpret_cast<uint32_t*>(ws + L.hh);
     p.btok = reinterpret_cast<int32_t*>(ws + L.btok);
     p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);

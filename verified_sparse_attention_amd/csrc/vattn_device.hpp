@@ -595,117 +595,87 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
 }
 
 // ---------------------------------------------------------------------------
-// Sampler thresholds from the histogram of the Philox words' top kSampBits.
-// hist[h] holds the tail histogram of head h.  For rank[h] > 0 the result
-// thr[h] = sample_key of the rank-th smallest (word, index) of the tail, so
-// the first rank[h] tail tokens of the sample order are exactly those with
-// sample_key >= thr[h].  One pass over the middle's cached words uw[i]
-// collects the tokens of the boundary bin; `in_fixed(h, i)` tells whether
-// token i is in head h's fixed set (those are not in the tail).
+// Sampler threshold of one head from the histogram of the Philox words' top
+// kSampBits.  S.hist holds the head's tail histogram.  For rank > 0 the result
+// S.thr = sample_key of the rank-th smallest (word, index) of the tail, so the
+// first `rank` tail tokens of the sample order are exactly those with
+// sample_key >= S.thr.  The tokens of the boundary bin come from the
+// predictor's bin-sorted chunk lists (BinLists); `in_fixed(i)` tells whether
+// token i is in the head's fixed set (those are not in the tail).
 // ---------------------------------------------------------------------------
-template <int NH>
-struct SampShared {
-    uint32_t hist[NH][kSampBins];
-    uint64_t list[NH][kListCap];
-    uint64_t thr[NH];
-    uint32_t before[NH], cnt[NH], rank[NH];
-    int bin[NH];
+struct HeadSamp {
+    uint32_t hist[kSampBins];
+    uint64_t list[kListCap];
+    uint64_t thr;
+    uint32_t before, cnt;
+    int bin;
 };
 
-template <int NH, class InFixed>
-__device__ __forceinline__ void block_sample_threshold(SampShared<NH>& S, SelShared<NH>& F, const Regions R,
-                                       const uint32_t* __restrict__ uw, const uint32_t (&rank)[NH],
-                                       InFixed&& in_fixed) {
+// Chunk c of the middle holds its tokens grouped by bin: bin x of chunk c is
+// slist[c * cp + soff[c][x] .. c * cp + soff[c][x + 1]).  Chunks are the
+// predictor's; only those overlapping the middle [lo, hi) were written.
+struct BinLists {
+    const uint32_t* soff;  // [nchunks][kSampBins + 1]
+    const int32_t* slist;  // [nchunks][cp]
+    int nchunks, cp, lo, hi;
+};
+
+template <class InFixed>
+__device__ __forceinline__ void head_sample_threshold(HeadSamp& S, SelShared<1>& F, const BinLists BL,
+                                                      const uint32_t* __restrict__ uw, uint32_t rank,
+                                                      InFixed&& in_fixed) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    constexpr int kShift = 32 - kSampBits;
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        any |= rank[h] > 0;
-        if (tid == h) {  // compile-time head numbers: no indexing of the caller's array
-            S.cnt[h] = 0;
-            S.thr[h] = 0;
-            S.rank[h] = rank[h];
-        }
+    if (tid == 0) {
+        S.cnt = 0;
+        S.thr = 0;
     }
-    __syncthreads();
-    if (!any) return;
-    for (int h = wave; h < NH; h += nwaves) {
-        if (S.rank[h] == 0) continue;
+    if (rank == 0) {  // block-uniform
+        __syncthreads();
+        return;
+    }
+    if (wave == 0) {
         int bin;
         uint32_t before;
-        wave_rank_bin<kSampBins>(S.hist[h], S.rank[h], false, bin, before);
+        wave_rank_bin<kSampBins>(S.hist, rank, false, bin, before);
         if (lane == 0) {
-            S.bin[h] = bin;
-            S.before[h] = before;
+            S.bin = bin;
+            S.before = before;
         }
     }
     __syncthreads();
-    int bn[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) bn[h] = rank[h] > 0 ? S.bin[h] : -1;
-    const int q0 = R.lo >> 2, q1 = (R.hi - 1) >> 2;
-    constexpr int kBatch = 8;  // quads loaded before any is examined
-    for (int qb = q0 + tid; qb <= q1; qb += kBatch * nthr) {
-        uint4 wb[kBatch];
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-            const int qd = qb + t * nthr;
-            wb[t] = qd <= q1 ? *reinterpret_cast<const uint4*>(uw + 4 * qd) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-            const int qd = qb + t * nthr;
-            if (qd > q1) break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * qd + e;
-                if (i < R.lo || i >= R.hi) continue;
-                const uint32_t u = word_of(wb[t], e);
-                const int bi = static_cast<int>(u >> kShift);
-#pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    if (bi == bn[h] && !in_fixed(h, i)) {
-                        const uint32_t pos = atomicAdd(&S.cnt[h], 1u);
-                        if (pos < static_cast<uint32_t>(kListCap)) S.list[h][pos] = sample_key(u, static_cast<uint32_t>(i));
-                    }
-                }
+    const int bn = S.bin;
+    if (bn < 0) return;  // fewer tail tokens than `rank`: excluded by the callers
+    const uint32_t r = rank - S.before;
+    // every tail token of the boundary bin, wave per chunk
+    auto each = [&](auto&& f) __attribute__((always_inline)) {
+        for (int c = wave; c < BL.nchunks; c += nwaves) {
+            if (max(c * BL.cp, BL.lo) >= min((c + 1) * BL.cp, BL.hi)) continue;
+            const uint32_t* off = BL.soff + static_cast<size_t>(c) * (kSampBins + 1) + bn;
+            const uint32_t a = off[0], e = off[1];
+            const int32_t* lst = BL.slist + static_cast<size_t>(c) * BL.cp;
+            for (uint32_t p = a + lane; p < e; p += 64) {
+                const int i = lst[p];
+                const uint32_t u = uw[i];
+                if (!in_fixed(i)) f(sample_key(u, static_cast<uint32_t>(i)));
             }
         }
-    }
+    };
+    each([&](uint64_t key) __attribute__((always_inline)) {
+        const uint32_t pos = atomicAdd(&S.cnt, 1u);
+        if (pos < static_cast<uint32_t>(kListCap)) S.list[pos] = key;
+    });
     __syncthreads();
-    uint32_t fmask = 0;
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-        if (bn[h] >= 0 && S.cnt[h] > static_cast<uint32_t>(kListCap)) fmask |= 1u << h;
-    for (int x = tid; x < NH * kListCap; x += nthr) {
-        const int h = x / kListCap, e = x - h * kListCap;
-        if (bn[h] >= 0 && !((fmask >> h) & 1u))
-            list_rank_pick(S.list[h], static_cast<int>(S.cnt[h]), S.rank[h] - S.before[h], e, &S.thr[h]);
-    }
-    __syncthreads();
-    if (fmask) {  // rare: a crowded bin, ranked by the radix select over its tokens
-        uint32_t fw[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? S.rank[h] - S.before[h] : 0u;
-        block_select<NH>(F, fw, [&](auto&& visit) __attribute__((always_inline)) {
-            for (int qd = q0 + tid; qd <= q1; qd += nthr) {
-                const uint4 w = *reinterpret_cast<const uint4*>(uw + 4 * qd);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * qd + e;
-                    if (i < R.lo || i >= R.hi) continue;
-                    const uint32_t u = word_of(w, e);
-                    const int bi = static_cast<int>(u >> kShift);
-#pragma unroll
-                    for (int h = 0; h < NH; ++h)
-                        if (((fmask >> h) & 1u) && bi == bn[h] && !in_fixed(h, i))
-                            visit(h, sample_key(u, static_cast<uint32_t>(i)));
-                }
-            }
+    const uint32_t cnt = S.cnt;
+    if (cnt <= static_cast<uint32_t>(kListCap)) {
+        for (int x = tid; x < static_cast<int>(cnt); x += nthr) list_rank_pick(S.list, static_cast<int>(cnt), r, x, &S.thr);
+        __syncthreads();
+    } else {  // rare: a crowded bin, ranked by the radix select over its tokens
+        const uint32_t fw[1] = {r};
+        block_select<1>(F, fw, [&](auto&& visit) __attribute__((always_inline)) {
+            each([&](uint64_t key) __attribute__((always_inline)) { visit(0, key); });
         }, true);
-        if (tid < NH && ((fmask >> tid) & 1u)) S.thr[tid] = F.thr[tid];
+        if (tid == 0) S.thr = F.thr[0];
         __syncthreads();
     }
 }

@@ -3,16 +3,17 @@
 // Pipeline for one step (all on the caller's stream):
 //   predict  (chunk, b*Hkv)  stream the predictor keys of one context chunk,
 //                            score the G query heads of the KV group, keep the
-//                            chunk's top-k candidates per head; histogram of the
-//                            chunk's sample words
-//   select   (b*Hkv)         exact top-k from the candidates, fixed-set bitmap
-//                            (sinks, window, top-k), per-head tail histograms,
+//                            chunk's top-k candidates per head; the chunk's
+//                            sample words, grouped by their top bits
+//   select   (b*Hq)          exact top-k from the candidates, fixed-set bitmap
+//                            (sinks, window, top-k), tail histogram,
 //                            base-sample threshold in the sample order
 //   base     (chunk, b*Hkv)  pinned exact scores of the union of the group's
 //                            fixed sets and base samples -> score cache, chunk
 //                            maxima, member lists
-//   budget   (b*Hkv)         exact fixed-point denominator statistics from the
-//                            member lists, CLT budget, final-sample threshold
+//   stats    (chunk, b*Hkv)  exact fixed-point denominator statistics of the
+//                            chunk's members, added to each head's totals
+//   budget   (b*Hq)          CLT budget, final-sample threshold
 //   gather   (chunk, b*Hkv)  one pass over the union of the group's index sets:
 //                            K row (unless its score is cached) and V row per
 //                            token, weighted online softmax for each member head
@@ -32,7 +33,8 @@
 
 namespace vattn {
 
-constexpr int kUnroll = 4;  // token rows in flight per lane group in the streaming loops
+constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
+constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
 __device__ __forceinline__ bool bit_of(const uint32_t* row, int i) {
@@ -68,7 +70,7 @@ size_t predict_lds_bytes(int G, int d, int row, int cp) {
         case 4: ts = sizeof(TopkShared<4>); break;
         default: ts = sizeof(TopkShared<8>); break;
     }
-    return align16(ts) + sizeof(uint32_t) * kSampBins + sizeof(int32_t) * (cp / kPage + 2) +
+    return align16(ts) + sizeof(uint32_t) * (kSampBins + kPredThreads / 64) + sizeof(int32_t) * (cp / kPage + 2) +
            sizeof(float) * (static_cast<size_t>(G) * d + static_cast<size_t>(G) * row) +
            sizeof(uint32_t) * static_cast<size_t>(G) * cp;
 }
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     TopkShared<G>& TS = *reinterpret_cast<TopkShared<G>*>(smem);
     size_t off = align16(sizeof(TopkShared<G>));
     uint32_t* shist = reinterpret_cast<uint32_t*>(smem + off);
-    off += sizeof(uint32_t) * kSampBins;
+    uint32_t* wsum = shist + kSampBins;  // scan scratch, one word per wave
+    off += sizeof(uint32_t) * (kSampBins + kPredThreads / 64);
     int32_t* pages = reinterpret_cast<int32_t*>(smem + off);  // the chunk's page ids
     off += sizeof(int32_t) * (P.cp / kPage + 2);
     float* qs = reinterpret_cast<float*>(smem + off);  // [G][d]
@@ -95,8 +98,9 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     if (t0 >= t1) return;
     const int d = P.d;
 
-    // sample-word histogram of the chunk's middle tokens (the top-k tokens are
-    // taken out per head once they are known)
+    // sample words of the chunk's middle tokens, their histogram over the top
+    // kSampBits, and the tokens grouped by that bin (a counting sort): the
+    // sampler later reads one bin's tokens instead of scanning the tail
     const int tb = (t0 / kPage) * kPage;
     const int ntok = ((t1 - 1) / kPage + 1) * kPage - tb;
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
@@ -112,6 +116,43 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             const int i = 4 * qd + e;
             if (i >= t0 && i < t1) atomicAdd(&shist[word_of(w, e) >> (32 - kSampBits)], 1u);
         }
+    }
+    __syncthreads();
+    {
+        static_assert(kSampBins % kPredThreads == 0, "bins per thread");
+        constexpr int PER = kSampBins / kPredThreads;
+        uint32_t v[PER], sum = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            v[e] = shist[PER * tid + e];
+            sum += v[e];
+        }
+        uint32_t total;
+        uint32_t run = block_excl_scan(sum, wsum, total);
+        uint32_t* so = P.soff + (static_cast<size_t>(bg) * P.ncp + c) * (kSampBins + 1);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            shist[PER * tid + e] = run;  // bin cursor for the scatter below
+            so[PER * tid + e] = run;
+            run += v[e];
+        }
+        if (tid == 0) so[kSampBins] = total;
+        __syncthreads();
+        // scatter into LDS (the score area is free until the stream), then one
+        // coalesced copy of the chunk's sorted list
+        int32_t* stage = reinterpret_cast<int32_t*>(keys);
+        for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
+            const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * qd + e;
+                if (i >= t0 && i < t1) stage[atomicAdd(&shist[word_of(w, e) >> (32 - kSampBits)], 1u)] = i;
+            }
+        }
+        __syncthreads();
+        int32_t* sl = P.slist + (static_cast<size_t>(bg) * P.ncp + c) * P.cp;
+        for (int x = tid; x < t1 - t0; x += nthr) sl[x] = stage[x];
+        __syncthreads();  // the score stream reuses the staging area
     }
 
     if (R.k > 0) {
@@ -153,24 +194,31 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             TS.hi[tid] = 0;
             TS.aux[tid] = 0;
         }
-        for (int base = wave * TPW * kUnroll; base < ntok; base += nwaves * TPW * kUnroll) {
-            float kf[kUnroll][8];
-            int tt[kUnroll];
+        // rows past the chunk's last page reread its last row and are not stored.
+        // Each iteration requests its whole batch before scoring any of it
+        // (no loads carried across iterations, so the waits stay exact).
+        const int Hkv = P.Hkv, cp = P.cp;
+        uint32_t* __restrict__ kst = keys;
+        // rows per lane group and batch: fewer when the G query registers are many
+        constexpr int PU = G * sizeof(T) >= 32 ? 2 : G * sizeof(T) >= 16 ? 4 : 2 * kUnroll;
+        for (int sb = wave * TPW * PU; sb < ntok; sb += nwaves * TPW * PU) {
+            Raw8 kr[PU];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                // rows past the chunk's last page reread its last row and are not stored
-                const int tl = min(base + u * TPW + slot, ntok - 1);
-                tt[u] = tb + tl;
-                load8(src + row_index(pages[tl / kPage], P.Hkv, g, tt[u] % kPage, ROW) + 8 * j, kf[u]);
+            for (int u = 0; u < PU; ++u) {
+                const int tl = min(sb + u * TPW + slot, ntok - 1);
+                load_raw(src + row_index(pages[tl / kPage], Hkv, g, (tb + tl) % kPage, ROW) + 8 * j, kr[u]);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < PU; ++u) {
+                const int tt = tb + min(sb + u * TPW + slot, ntok - 1);
+                float kf[8];
+                widen<T>(kr[u], kf);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float s = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
-                    if (j == LPT - 1 && tt[u] >= t0 && tt[u] < t1) {
-                        const uint32_t ok = okey(s);
-                        keys[h * P.cp + (tt[u] - cbase)] = ok;
+                    const float sc = tree_across_lanes<LPT>(chain8(qreg[h], kf));
+                    if (j == LPT - 1 && tt >= t0 && tt < t1) {
+                        const uint32_t ok = okey(sc);
+                        kst[h * cp + (tt - cbase)] = ok;
                         klo[h] = min(klo[h], ok);
                         khi[h] = max(khi[h], ok);
                     }
@@ -202,7 +250,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             hi[h] = TS.hi[h];
         }
         const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-        const int cp = P.cp, ncp = P.ncp, kcap = P.kcap;
+        const int ncp = P.ncp, kcap = P.kcap;
         uint64_t* __restrict__ cand = P.cand;
         block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
             for (int t = t0 + tid; t < t1; t += nthr)
@@ -219,9 +267,6 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             cr[1] = hi[tid];
         }
     }
-    __syncthreads();
-    uint32_t* dst = P.shist + (static_cast<size_t>(bg) * P.ncp + c) * kSampBins;
-    for (int x = tid; x < kSampBins; x += nthr) dst[x] = shist[x];
 }
 
 // ===========================================================================
@@ -232,29 +277,28 @@ __device__ __forceinline__ int chunk_candidates(int cp, const Regions R, int c) 
     return a < e ? min(R.k, e - a) : 0;
 }
 
-template <int G>
-__global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
-    __shared__ TopkShared<G> TS;
-    __shared__ SampShared<G> SS;
+__global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
+    __shared__ TopkShared<1> TS;
+    __shared__ HeadSamp SS;
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int bg = blockIdx.x, b = bg / P.Hkv, g = bg % P.Hkv;
+    const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
+    const int bg = b * P.Hkv + g;
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
-    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
     const uint32_t* uwg = group_words(P, bg);
     // lambdas below capture these locals, never the kernel argument itself
-    const int cp = P.cp, ncp = P.ncp, kcap = P.kcap, words = P.words;
-    const uint64_t* __restrict__ cand = P.cand;
-    uint32_t* __restrict__ bits = P.bits;
-    if (tid == 0 && P.gcounts) {
+    const int cp = P.cp, ncp = P.ncp, kcap = P.kcap;
+    const uint64_t* __restrict__ cand = P.cand + static_cast<size_t>(bh) * ncp * kcap;
+    uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
+    const uint32_t* soffg = P.soff + static_cast<size_t>(bg) * ncp * (kSampBins + 1);
+    if (tid == 0 && P.gcounts && h % P.G == 0) {
         P.gcounts[2 * bg] = 0;
         P.gcounts[2 * bg + 1] = 0;
     }
 
     // 1) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
     const int wl = (L + 31) >> 5;
-    for (int x = tid; x < G * wl; x += nthr) {
-        const int h = x / wl, w = x - h * wl;
+    for (int w = tid; w < wl; w += nthr) {
         uint32_t word = 0;
         const int i0 = 32 * w;
         if (i0 < R.sp) word |= (R.sp - i0 >= 32) ? 0xFFFFFFFFu : ((1u << (R.sp - i0)) - 1u);
@@ -262,86 +306,91 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
             const int a = max(R.hi - i0, 0), e = min(L - i0, 32);  // bits [a, e)
             if (e > a) word |= (e - a >= 32 ? 0xFFFFFFFFu : ((1u << (e - a)) - 1u)) << a;
         }
-        P.bits[(bh0 + h) * P.words + w] = word;
+        bits[w] = word;
     }
+    constexpr int kCB = 4;  // chunks whose loads are issued together
     for (int x = tid; x < kSampBins; x += nthr) {
         uint32_t sum = 0;
-        for (int c = 0; c < P.ncp; ++c) {
-            const int a = max(c * P.cp, R.lo), e = min((c + 1) * P.cp, R.hi);
-            if (a < e) sum += P.shist[(static_cast<size_t>(bg) * P.ncp + c) * kSampBins + x];
-        }
+        for (int c0 = 0; c0 < ncp; c0 += kCB) {
+            uint32_t a[kCB], e[kCB];
 #pragma unroll
-        for (int h = 0; h < G; ++h) SS.hist[h][x] = sum;
+            for (int t = 0; t < kCB; ++t) {
+                const int c = c0 + t;
+                const bool live = c < ncp && max(c * cp, R.lo) < min((c + 1) * cp, R.hi);
+                const uint32_t* off = soffg + static_cast<size_t>(live ? c : 0) * (kSampBins + 1) + x;
+                a[t] = live ? off[0] : 0u;
+                e[t] = live ? off[1] : 0u;
+            }
+#pragma unroll
+            for (int t = 0; t < kCB; ++t) sum += e[t] - a[t];
+        }
+        SS.hist[x] = sum;
     }
 
-    // 2) exact top-k of each head from its chunk candidates: set the bit and
-    //    take the token out of the tail histogram (block_topk starts with a barrier)
+    // 2) exact top-k from the chunk candidates: set the bit and take the token
+    //    out of the tail histogram (block_topk starts with a barrier)
     if (R.k > 0) {
-        uint32_t want[G], total[G], lo[G], hi[G];
-        uint32_t tot = 0;
-        for (int c = 0; c < P.ncp; ++c) tot += static_cast<uint32_t>(chunk_candidates(cp, R, c));
+        uint32_t tot = 0, lo = 0xFFFFFFFFu, hi = 0;
+        for (int c0 = 0; c0 < ncp; c0 += kCB) {
+            uint32_t clo[kCB], chi[kCB];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            want[h] = static_cast<uint32_t>(R.k);
-            total[h] = tot;
-            lo[h] = 0xFFFFFFFFu;
-            hi[h] = 0;
-            for (int c = 0; c < P.ncp; ++c) {
-                if (chunk_candidates(cp, R, c) == 0) continue;
-                const uint32_t* cr = P.crange + ((bh0 + h) * P.ncp + c) * 2;
-                lo[h] = min(lo[h], cr[0]);
-                hi[h] = max(hi[h], cr[1]);
+            for (int t = 0; t < kCB; ++t) {
+                const int c = c0 + t;
+                const int nc = c < ncp ? chunk_candidates(cp, R, c) : 0;
+                tot += static_cast<uint32_t>(nc);
+                const uint32_t* cr = P.crange + (static_cast<size_t>(bh) * ncp + (nc ? c : 0)) * 2;
+                clo[t] = nc ? cr[0] : 0xFFFFFFFFu;
+                chi[t] = nc ? cr[1] : 0u;
+            }
+#pragma unroll
+            for (int t = 0; t < kCB; ++t) {
+                lo = min(lo, clo[t]);
+                hi = max(hi, chi[t]);
             }
         }
+        const uint32_t want[1] = {static_cast<uint32_t>(R.k)}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
         const int slots = ncp * kcap;
         constexpr int kBatch = 8;  // candidate keys loaded before any is visited
-        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
-            for (int x0 = tid; x0 < G * slots; x0 += kBatch * nthr) {
+        block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
+            for (int x0 = tid; x0 < slots; x0 += kBatch * nthr) {
                 uint64_t kk[kBatch];
-                int hh[kBatch];
+                bool ok[kBatch];
 #pragma unroll
                 for (int t = 0; t < kBatch; ++t) {
                     const int x = x0 + t * nthr;
-                    const int h = x / slots, sl = x - h * slots;
-                    const int c = sl / kcap, p = sl - c * kcap;
-                    const bool ok = x < G * slots && p < chunk_candidates(cp, R, c);
-                    hh[t] = ok ? h : -1;
-                    kk[t] = ok ? cand[((bh0 + h) * ncp + c) * kcap + p] : 0ull;
+                    const int c = x / kcap, p = x - c * kcap;
+                    ok[t] = x < slots && p < chunk_candidates(cp, R, c);
+                    kk[t] = ok[t] ? cand[x] : 0ull;
                 }
 #pragma unroll
                 for (int t = 0; t < kBatch; ++t)
-                    if (hh[t] >= 0) f(hh[t], static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
+                    if (ok[t]) f(0, static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
             }
-        }, [&](int h, uint64_t key) __attribute__((always_inline)) {
+        }, [&](int, uint64_t key) __attribute__((always_inline)) {
             const uint32_t i = ~static_cast<uint32_t>(key);
-            atomicOr(&bits[(bh0 + h) * words + (i >> 5)], 1u << (i & 31));
-            atomicSub(&SS.hist[h][uwg[i] >> (32 - kSampBits)], 1u);
+            atomicOr(&bits[i >> 5], 1u << (i & 31));
+            atomicSub(&SS.hist[uwg[i] >> (32 - kSampBits)], 1u);
         });
     } else {
         __syncthreads();
     }
-    for (int x = tid; x < G * kSampBins; x += nthr) {
-        const int h = x / kSampBins, e = x - h * kSampBins;
-        P.hh[(bh0 + h) * kSampBins + e] = SS.hist[h][e];
-    }
+    for (int x = tid; x < kSampBins; x += nthr) P.hh[static_cast<size_t>(bh) * kSampBins + x] = SS.hist[x];
 
     // 3) base sample: first nb tail tokens in (word, index) order
-    uint32_t rank[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) rank[h] = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
-    block_sample_threshold<G>(SS, TS.S, R, uwg, rank, [&](int h, int i) __attribute__((always_inline)) {
-        return bit_of_coherent(bits + (bh0 + h) * words, i);
+    const uint32_t rank = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
+    const BinLists BL{soffg, P.slist + static_cast<size_t>(bg) * ncp * cp, ncp, cp, R.lo, R.hi};
+    head_sample_threshold(SS, TS.S, BL, uwg, rank, [&](int i) __attribute__((always_inline)) {
+        return bit_of_coherent(bits, i);
     });
-
-    if (tid < G) {
-        HeadState hs{};
+    if (tid == 0) {
+        HeadState hs{};  // the statistics start at zero for the stats pass
         hs.L = L;
         hs.k = R.k;
         hs.n_fixed = R.sp + R.wp + R.k;
         hs.NT = R.NT;
         hs.nb = R.nb;
-        hs.thr_b = (R.nb > 0 && R.nb < R.NT) ? SS.thr[tid] : 0;  // nb == N_t: the whole tail
-        P.hs[bh0 + tid] = hs;
+        hs.thr_b = rank ? SS.thr : 0;  // nb == N_t: the whole tail
+        P.hs[bh] = hs;
     }
 }
 
@@ -351,7 +400,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_select(Plan P) {
 struct HeadView {
     uint64_t thr_b, thr_n;
     int nb, n;
-    float wsamp;
+    float wsamp, m;
 };
 
 template <int D, typename KVT, int G>
@@ -364,7 +413,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     __shared__ HeadView hv[G];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
+    // KV heads fastest: the blocks of one (sequence, chunk) launch together and
+    // read the same pages, whose KV heads are adjacent in memory
+    const int g = blockIdx.x, c = blockIdx.y, b = blockIdx.z, bg = b * P.Hkv + g;
     const int L = P.seq_lens[b];
     const int T0 = c * P.cg;
     if (T0 >= L) return;
@@ -372,7 +423,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
     if (tid < G) {
         const HeadState& s = P.hs[bh0 + tid];
-        hv[tid] = HeadView{s.thr_b, 0, s.nb, 0, 0.f};
+        hv[tid] = HeadView{s.thr_b, 0, s.nb, 0, 0.f, 0.f};
     }
     __syncthreads();
 
@@ -384,24 +435,29 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
     const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi) w = *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd);
+        // the quad's sample words and each head's bitmap word (a quad never
+        // straddles a 32-token word), all requested before use
+        const bool anyM = 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
+        const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+        uint32_t fw[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) fw[h] = P.bits[(bh0 + h) * P.words + (qd >> 3)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
-            if (i >= T1) continue;
             const bool inM = i >= R.lo && i < R.hi;
             const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
             uint32_t bm = 0, fm = 0;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const bool fx = bit_of(P.bits + (bh0 + h) * P.words, i);
+                const bool fx = (fw[h] >> (i & 31)) & 1u;
                 const bool bs = inM && !fx && hv[h].nb > 0 && key >= hv[h].thr_b;
                 bm |= (fx || bs) ? (1u << h) : 0u;
                 fm |= fx ? (1u << h) : 0u;
             }
-            m4[e] = bm ? (bm | (fm << 8)) : 0u;
-            mine += bm ? 1u : 0u;
+            const bool live = i < T1 && bm;
+            m4[e] = live ? (bm | (fm << 8)) : 0u;
+            mine += live ? 1u : 0u;
         }
     }
     uint32_t cnt;
@@ -438,24 +494,27 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const KVT* kbase = static_cast<const KVT*>(P.k);
     float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
     const int n = static_cast<int>(cnt);
-    for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
-        float kf[kUnroll][8];
-        int tk[kUnroll];
-        uint32_t mk[kUnroll];
+    constexpr int kBU = kBaseUnroll;
+    for (int base = wave * TPW * kBU; base < n; base += nwaves * TPW * kBU) {
+        Raw8 kr[kBU];
+        int tk[kBU];
+        uint32_t mk[kBU];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kBU; ++u) {
             const int x = base + u * TPW + slot;
             const bool act = x < n;
             const int xs = act ? x : 0;
             tk[u] = tok[xs];
             mk[u] = act ? tmeta[xs] : 0u;
-            load8(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kf[u]);
+            load_raw(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kr[u]);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kBU; ++u) {
+            float kf[8];
+            widen<KVT>(kr[u], kf);
             float s[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf[u]));
+            for (int h = 0; h < G; ++h) s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
             if (j == LPT - 1) {  // the lane holding the pinned sums
 #pragma unroll
                 for (int h = 0; h < G; ++h)
@@ -482,115 +541,87 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 }
 
 // ===========================================================================
-// budget: exact fixed-point statistics, CLT budget, final-sample threshold
+// stats: exact fixed-point sums over one base chunk's member list, added to
+// the head's totals with integer atomics (exact, so order independent)
 // ===========================================================================
+constexpr int kStatsChunks = 4;  // base chunks per stats block
+
 template <int G>
-__global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
-    __shared__ SampShared<G> SS;
-    __shared__ SelShared<G> FS;
+__global__ __launch_bounds__(kChunkThreads) void k_stats(Plan P) {
+    constexpr int NW = kChunkThreads / 64, kBatch = 4;
     __shared__ float smax[G];
-    __shared__ uint64_t red[kGroupThreads / 64][G][4];
-    __shared__ int nsel[G], nfin[G];
-    __shared__ int coff[kMaxChunks + 1];
+    __shared__ uint64_t red[NW][G][4];
+    __shared__ int coff[kStatsChunks + 1];
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    const int bg = blockIdx.x, b = bg / P.Hkv, g = bg % P.Hkv;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv, c0 = blockIdx.x * kStatsChunks;
     const int L = P.seq_lens[b];
-    const Regions R = regions(P, L);
-    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-    if (L == 0) {
-        if (tid < G) {
-            HeadState hs{};
-            P.hs[bh0 + tid] = hs;
-        }
-        return;
-    }
+    if (c0 * P.cg >= L) return;
     const int nc = (L + P.cg - 1) / P.cg;
-    if (tid < G) {
-        float m = -__builtin_inff();
-        for (int c = 0; c < nc; ++c) m = fmaxf(m, P.cmax[(bh0 + tid) * P.ncg + c]);
-        smax[tid] = m;
+    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    if (wave == 0) {  // members of the block's chunks: counts -> offsets
+        const int cc = c0 + lane;
+        const uint32_t v = (lane < kStatsChunks && cc < nc) ? static_cast<uint32_t>(P.bcnt[static_cast<size_t>(bg) * P.ncg + cc]) : 0u;
+        const uint32_t inc = wave_incl_scan(v);
+        if (lane < kStatsChunks) coff[lane] = static_cast<int>(inc - v);
+        if (lane == kStatsChunks - 1) coff[kStatsChunks] = static_cast<int>(inc);
     }
-    for (int x = tid; x < G * kSampBins; x += nthr) {
-        const int h = x / kSampBins, e = x - h * kSampBins;
-        SS.hist[h][e] = P.hh[(bh0 + h) * kSampBins + e];
+    for (int hh = wave; hh < G; hh += NW) {  // m: max pinned score over I_f and the base sample
+        float m = -__builtin_inff();
+        for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, P.cmax[(bh0 + hh) * P.ncg + cc]);
+        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (lane == 0) smax[hh] = m;
     }
     __syncthreads();
-
-    // fixed-point sums over the base pass's member lists: SF over I_f, S1 and
-    // S2 over the base sample
-    uint64_t sf[G], s1[G];
-    unsigned __int128 s2[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        sf[h] = 0;
-        s1[h] = 0;
-        s2[h] = 0;
-    }
+    const int total = coff[kStatsChunks];
+    if (total == 0) return;
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    // members of all base chunks as one flat range: a prefix over the chunk
-    // counts, then every thread loads its members' tokens and scores before use
-    {
-        const int32_t* cnts = P.bcnt + static_cast<size_t>(bg) * P.ncg;
-        for (int c = tid; c < nc; c += nthr) coff[c] = cnts[c];
-        __syncthreads();
-        if (wave == 0) {  // exclusive prefix over nc <= kMaxChunks counts, 64 at a time
-            uint32_t carry = 0;
-            for (int c0 = 0; c0 < nc; c0 += 64) {
-                const uint32_t v = c0 + lane < nc ? static_cast<uint32_t>(coff[c0 + lane]) : 0u;
-                const uint32_t inc = wave_incl_scan(v);
-                if (c0 + lane < nc) coff[c0 + lane] = static_cast<int>(carry + inc - v);
-                carry += __shfl(inc, 63, 64);
+    uint64_t sf[G], s1[G], s2lo[G], s2hi[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sf[hh] = s1[hh] = s2lo[hh] = s2hi[hh] = 0;
+    for (int y0 = 0; y0 < total; y0 += kBatch * nthr) {
+        int ti[kBatch];
+        uint32_t tm[kBatch];
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            const int y = y0 + tid + v * nthr;
+            ti[v] = 0;
+            tm[v] = 0u;
+            if (y < total) {
+                int cc = 0;
+#pragma unroll
+                for (int t = 1; t < kStatsChunks; ++t) cc += y >= coff[t] ? 1 : 0;
+                const size_t at = (static_cast<size_t>(bg) * P.ncg + c0 + cc) * P.cg + (y - coff[cc]);
+                ti[v] = P.btok[at];
+                tm[v] = P.bmeta[at];
             }
-            if (lane == 0) coff[nc] = static_cast<int>(carry);
         }
-        __syncthreads();
-        const int total = coff[nc];
-        constexpr int kMemBatch = G <= 4 ? 4 : 2;
-        for (int y0 = tid; y0 < total; y0 += kMemBatch * nthr) {
-            int ti[kMemBatch];
-            uint32_t tm[kMemBatch];
+        float sv[kBatch][G];
 #pragma unroll
-            for (int v = 0; v < kMemBatch; ++v) {
-                const int y = y0 + v * nthr;
-                ti[v] = -1;
-                tm[v] = 0u;
-                if (y < total) {
-                    int lo = 0, hi = nc - 1;  // chunk c with coff[c] <= y < coff[c + 1]
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (coff[mid] <= y) lo = mid; else hi = mid - 1;
-                    }
-                    const size_t at = (static_cast<size_t>(bg) * P.ncg + lo) * P.cg + (y - coff[lo]);
-                    ti[v] = P.btok[at];
-                    tm[v] = P.bmeta[at];
-                }
+        for (int v = 0; v < kBatch; ++v)
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh)
+                sv[v][hh] = ((tm[v] >> hh) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + hh] : 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float m = smax[hh];
+#pragma unroll
+            for (int v = 0; v < kBatch; ++v) {
+                const bool mem = (tm[v] >> hh) & 1u, fx = (tm[v] >> (8 + hh)) & 1u;
+                const uint64_t E = mem ? fixed_weight(sv[v][hh] - m) : 0ull;
+                const uint64_t Ef = fx ? E : 0ull, Es = fx ? 0ull : E;
+                sf[hh] += Ef;
+                s1[hh] += Es;
+                const unsigned __int128 e2 = static_cast<unsigned __int128>(Es) * Es;
+                const uint64_t lo = static_cast<uint64_t>(e2);
+                s2hi[hh] += static_cast<uint64_t>(e2 >> 64) + ((s2lo[hh] + lo < s2lo[hh]) ? 1u : 0u);
+                s2lo[hh] += lo;
             }
-            float sv[kMemBatch][G];
-#pragma unroll
-            for (int v = 0; v < kMemBatch; ++v)
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-                    sv[v][h] = ((tm[v] >> h) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + h] : 0.0f;
-#pragma unroll
-            for (int v = 0; v < kMemBatch; ++v)
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint64_t E = ((tm[v] >> h) & 1u) ? fixed_weight(sv[v][h] - smax[h]) : 0ull;
-                    if ((tm[v] >> (8 + h)) & 1u) {
-                        sf[h] += E;
-                    } else {
-                        s1[h] += E;
-                        s2[h] += static_cast<unsigned __int128>(E) * E;
-                    }
-                }
         }
     }
-    // exact reduction (integer sums are order independent)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        uint64_t a = sf[h], b1 = s1[h];
-        uint64_t lo = static_cast<uint64_t>(s2[h]), hi = static_cast<uint64_t>(s2[h] >> 64);
+    for (int hh = 0; hh < G; ++hh) {
+        uint64_t a = sf[hh], b1 = s1[hh], lo = s2lo[hh], hi = s2hi[hh];
         for (int o = 32; o >= 1; o >>= 1) {
             a += shfl_xor_u64(a, o);
             b1 += shfl_xor_u64(b1, o);
@@ -600,22 +631,68 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
             lo = nlo;
         }
         if (lane == 0) {
-            red[wave][h][0] = a;
-            red[wave][h][1] = b1;
-            red[wave][h][2] = hi;
-            red[wave][h][3] = lo;
+            red[wave][hh][0] = a;
+            red[wave][hh][1] = b1;
+            red[wave][hh][2] = hi;
+            red[wave][hh][3] = lo;
         }
     }
     __syncthreads();
     if (tid < G) {
-        const int h = tid;
-        uint64_t SF = 0, S1 = 0;
-        unsigned __int128 S2 = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            SF += red[w][h][0];
-            S1 += red[w][h][1];
-            S2 += (static_cast<unsigned __int128>(red[w][h][2]) << 64) | red[w][h][3];
+        uint64_t SF = 0, S1 = 0, lo = 0, hi = 0;
+        for (int w = 0; w < NW; ++w) {
+            SF += red[w][tid][0];
+            S1 += red[w][tid][1];
+            const uint64_t nlo = lo + red[w][tid][3];
+            hi += red[w][tid][2] + (nlo < lo ? 1u : 0u);
+            lo = nlo;
         }
+        HeadState& hs = P.hs[bh0 + tid];
+        if (SF) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.SF), static_cast<unsigned long long>(SF));
+        if (S1) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S1), static_cast<unsigned long long>(S1));
+        if (lo) {  // 128-bit add: the carry out of the low word is known from its old value
+            const unsigned long long old =
+                atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S2lo), static_cast<unsigned long long>(lo));
+            hi += (old + lo < old) ? 1u : 0u;
+        }
+        if (hi) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S2hi), static_cast<unsigned long long>(hi));
+    }
+}
+
+// ===========================================================================
+// budget: CLT budget from the exact statistics, final-sample threshold
+// ===========================================================================
+__global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
+    __shared__ HeadSamp SS;
+    __shared__ SelShared<1> FS;
+    __shared__ int s_nsel;
+    __shared__ float s_m;
+    const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+    const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
+    const int bg = b * P.Hkv + g;
+    const int L = P.seq_lens[b];
+    const Regions R = regions(P, L);
+    HeadState* hsp = P.hs + bh;
+    if (L == 0) {
+        if (tid == 0) {
+            const HeadState z{};
+            *hsp = z;
+        }
+        return;
+    }
+    for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
+    if (tid < 64) {  // m: max pinned score over I_f and the base sample
+        const int nc = (L + P.cg - 1) / P.cg;
+        float m = -__builtin_inff();
+        for (int c = lane; c < nc; c += 64) m = fmaxf(m, P.cmax[static_cast<size_t>(bh) * P.ncg + c]);
+        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (lane == 0) s_m = m;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const float m = s_m;
+        const uint64_t SF = hsp->SF, S1 = hsp->S1;
+        const unsigned __int128 S2 = (static_cast<unsigned __int128>(hsp->S2hi) << 64) | hsp->S2lo;
         const int NT = R.NT, nb = R.nb;
         int n, flags = 0;
         if (P.force_budget >= 0) {
@@ -648,36 +725,27 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
             }
         }
         if (n == NT) flags |= 1;
-        HeadState& hs = P.hs[bh0 + h];
-        hs.n = n;
-        hs.flags = flags;
-        hs.m = smax[h];
-        hs.wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
-        hs.SF = SF;
-        hs.S1 = S1;
-        hs.S2hi = static_cast<uint64_t>(S2 >> 64);
-        hs.S2lo = static_cast<uint64_t>(S2);
+        hsp->n = n;
+        hsp->flags = flags;
+        hsp->m = m;
+        hsp->wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
         // a new threshold unless the sample is empty, the whole tail or the base sample
-        nsel[h] = (n > 0 && n < NT && n != nb) ? n : 0;
-        nfin[h] = n;
+        s_nsel = (n > 0 && n < NT && n != nb) ? n : 0;
     }
     __syncthreads();
-
-    uint32_t rank[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) rank[h] = static_cast<uint32_t>(nsel[h]);
-    const uint32_t* __restrict__ bits = P.bits;
-    const int words = P.words;
-    block_sample_threshold<G>(SS, FS, R, group_words(P, bg), rank, [&](int h, int i) __attribute__((always_inline)) {
-        return bit_of(bits + (bh0 + h) * words, i);
+    const uint32_t rank = static_cast<uint32_t>(s_nsel);
+    const uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
+    const BinLists BL{P.soff + static_cast<size_t>(bg) * P.ncp * (kSampBins + 1),
+                      P.slist + static_cast<size_t>(bg) * P.ncp * P.cp, P.ncp, P.cp, R.lo, R.hi};
+    head_sample_threshold(SS, FS, BL, group_words(P, bg), rank, [&](int i) __attribute__((always_inline)) {
+        return bit_of(bits, i);
     });
-    if (tid < G) {
-        const int h = tid, n = nfin[h];
-        HeadState& hs = P.hs[bh0 + h];
+    if (tid == 0) {
+        const int n = hsp->n;
         uint64_t thr = 0;  // n == N_t: the whole tail (n == 0: unused)
-        if (nsel[h] > 0) thr = SS.thr[h];
-        else if (n > 0 && n == R.nb) thr = hs.thr_b;
-        hs.thr_n = thr;
+        if (rank > 0) thr = SS.thr;
+        else if (n > 0 && n == R.nb) thr = hsp->thr_b;
+        hsp->thr_n = thr;
     }
 }
 
@@ -687,10 +755,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_budget(Plan P) {
 // then per head the block max and the weights p = w exp(s - max); (2) a pure
 // stream of V rows accumulating sum_i p_i V_i.  Every weight is computed once.
 // ===========================================================================
-constexpr int kGatherUnrollV = 4;  // V rows per batch and lane group (two batches in flight)
+constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group
+constexpr int kTilesPerBatch = 3;  // 16-token K tiles per batch and wave
 
 template <int D, typename KVT, int G>
-__global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gather(Plan P) {
     constexpr int NW = kChunkThreads / 64;
     __shared__ int tok[kGatherChunk];
     __shared__ uint32_t tmeta[kGatherChunk];
@@ -711,7 +780,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
     if (tid < G) {
         const HeadState& s = P.hs[bh0 + tid];
-        hv[tid] = HeadView{s.thr_b, s.thr_n, s.nb, s.n, s.wsamp};
+        hv[tid] = HeadView{s.thr_b, s.thr_n, s.nb, s.n, s.wsamp, s.m};
     }
     __syncthreads();
 
@@ -723,18 +792,21 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
     const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     if (4 * qd < T1) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (4 * qd + 3 >= R.lo && 4 * qd < R.hi) w = *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd);
+        // the quad's sample words and each head's bitmap word, requested together
+        const bool anyM = 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
+        const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+        uint32_t fw[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) fw[h] = P.bits[(bh0 + h) * P.words + (qd >> 3)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
-            if (i >= T1) continue;
-            const bool inM = i >= R.lo && i < R.hi;
+            const bool inM = i >= R.lo && i < R.hi && i < T1;
             const uint64_t key = sample_key(word_of(w, e), static_cast<uint32_t>(i));
             uint32_t fin = 0, fxm = 0, cached = 0;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const bool fx = bit_of(P.bits + (bh0 + h) * P.words, i);
+                const bool fx = i < T1 && ((fw[h] >> (i & 31)) & 1u);
                 const bool tail = inM && !fx;
                 const bool sn = tail && hv[h].n > 0 && key >= hv[h].thr_n;
                 const bool sb = tail && hv[h].nb > 0 && key >= hv[h].thr_b;
@@ -767,14 +839,26 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     const int j = lane % LPT, slot = lane / LPT;
     const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
     const KVT* kbase = static_cast<const KVT*>(P.k);
-    for (int x = tid; x < n; x += nthr) {
-        const uint32_t m = tmeta[x];
-        if ((m >> 16) & 1u) {
-            float v[G];
+    {
+        constexpr int PER = kGatherChunk / kChunkThreads;  // list entries per thread
+        float v[PER][G];
+        uint32_t mm[PER];
 #pragma unroll
-            for (int h = 0; h < G; ++h) v[h] = scrow[static_cast<size_t>(tok[x]) * G + h];
+        for (int e = 0; e < PER; ++e) {
+            const int x = tid + e * nthr;
+            mm[e] = x < n ? tmeta[x] : 0u;
+            const bool cached = (mm[e] >> 16) & 1u;
+            const size_t at = static_cast<size_t>(cached ? tok[x] : 0) * G;
 #pragma unroll
-            for (int h = 0; h < G; ++h) sp[h][x] = ((m >> h) & 1u) ? v[h] : -__builtin_inff();
+            for (int h = 0; h < G; ++h) v[e][h] = cached ? scrow[at + h] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int x = tid + e * nthr;
+            if ((mm[e] >> 16) & 1u) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) sp[h][x] = ((mm[e] >> h) & 1u) ? v[e][h] : -__builtin_inff();
+            }
         }
     }
     if constexpr (sizeof(KVT) == 2) {
@@ -821,6 +905,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
             for (int kb = 0; kb < KB; ++kb) t.a[kb] = *reinterpret_cast<const uint4*>(rp + 32 * kb);
         };
         auto score = [&](const KTile& t, int x0) __attribute__((always_inline)) {
+            // metadata of the four rows this lane may write, read before the products
+            uint32_t mr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mr[r] = tmeta[min(x0 + 4 * kq + r, n - 1)];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -834,24 +922,22 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
                 for (int r = 0; r < 4; ++r) {
                     const float sv = acc[r] + dpp<0x101>(acc[r]) + dpp<0x102>(acc[r]);  // row_shl:1, :2
                     const int x = x0 + 4 * kq + r;
-                    if (writer && x < n) {
-                        const uint32_t m = tmeta[x];
-                        if (!((m >> 16) & 1u)) sp[hh][x] = ((m >> hh) & 1u) ? sv : -__builtin_inff();
-                    }
+                    const bool wr = writer && x < n && !((mr[r] >> 16) & 1u);
+                    if (wr) sp[hh][x] = ((mr[r] >> hh) & 1u) ? sv : -__builtin_inff();
                 }
             }
         };
-        int tI = wave;
-        KTile A, B;
-        if (tI < ntile) issue(A, 16 * tI);
-        while (tI < ntile) {
-            if (tI + nwaves < ntile) issue(B, 16 * (tI + nwaves));
-            score(A, 16 * tI);
-            tI += nwaves;
-            if (tI >= ntile) break;
-            if (tI + nwaves < ntile) issue(A, 16 * (tI + nwaves));
-            score(B, 16 * tI);
-            tI += nwaves;
+        // each wave scores kTilesPerBatch tiles per iteration, all of whose
+        // rows are requested before any is scored (tiles past the end reread
+        // the last tile; their results are not stored)
+        constexpr int NK = kTilesPerBatch;
+        for (int t0w = wave * NK; t0w < ntile; t0w += nwaves * NK) {
+            KTile kt[NK];
+#pragma unroll
+            for (int u = 0; u < NK; ++u) issue(kt[u], 16 * min(t0w + u, ntile - 1));
+#pragma unroll
+            for (int u = 0; u < NK; ++u)
+                if (t0w + u < ntile) score(kt[u], 16 * (t0w + u));
         }
     } else {
         float qreg[G][8];
@@ -940,7 +1026,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
     }
     __syncthreads();
 
-    // (2) sum_i p_i V_i, V rows streamed kGatherUnrollV deep and double-buffered
+    // (2) sum_i p_i V_i over the V rows
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -976,18 +1062,13 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
                 }
             }
         };
-        const int stride = nwaves * TPW * kGatherUnrollV;
-        int base = wave * TPW * kGatherUnrollV;
-        VBatch A, B;
-        if (base < n) issue(A, base);
-        while (base < n) {
-            if (base + stride < n) issue(B, base + stride);
-            accumulate(A);
-            base += stride;
-            if (base >= n) break;
-            if (base + stride < n) issue(A, base + stride);
-            accumulate(B);
-            base += stride;
+        // one batch of kGatherUnrollV rows per lane group per iteration, all
+        // requested before any is accumulated (rows past the end reread the
+        // last row with weight 0)
+        for (int b0 = wave * TPW * kGatherUnrollV; b0 < n; b0 += nwaves * TPW * kGatherUnrollV) {
+            VBatch bt;
+            issue(bt, b0);
+            accumulate(bt);
         }
     }
     // token slots of the wave hold the same dims: plain sums
@@ -1022,11 +1103,13 @@ __global__ __launch_bounds__(kChunkThreads) void k_gather(Plan P) {
 // ===========================================================================
 // combine: merge chunk partials; counts and statistics
 // ===========================================================================
-constexpr int kCombineThreads = 128;
+constexpr int kCombineThreads = 256;
 
 __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
+    constexpr int NW = kCombineThreads / 64;
     __shared__ float wsh[kMaxChunks];
-    __shared__ float rm[kCombineThreads / 64], rl[kCombineThreads / 64];
+    __shared__ float rm[NW], rl[NW];
+    __shared__ float accs[kCombineThreads];
     const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq;
     const int L = P.seq_lens[b];
@@ -1039,7 +1122,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
     if (lane == 0) rm[wave] = mloc;
     __syncthreads();
     float M = -__builtin_inff();
-    for (int w = 0; w < nthr / 64; ++w) M = fmaxf(M, rm[w]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, rm[w]);
     float lloc = 0.f;
     for (int c = tid; c < nc; c += nthr) {
         const float* q = pp + static_cast<size_t>(c) * (D + 2);
@@ -1051,20 +1134,29 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
     if (lane == 0) rl[wave] = lloc;
     __syncthreads();
     float l = 0.f;
-    for (int w = 0; w < nthr / 64; ++w) l += rl[w];
+    for (int w = 0; w < NW; ++w) l += rl[w];
     const bool ok = M != -__builtin_inff() && l > 0.f;
-    for (int e = tid; e < D; e += nthr) {
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        int c = 0;
-        for (; c + 4 <= nc; c += 4) {
-            a0 += wsh[c] * pp[static_cast<size_t>(c) * (D + 2) + 2 + e];
-            a1 += wsh[c + 1] * pp[static_cast<size_t>(c + 1) * (D + 2) + 2 + e];
-            a2 += wsh[c + 2] * pp[static_cast<size_t>(c + 2) * (D + 2) + 2 + e];
-            a3 += wsh[c + 3] * pp[static_cast<size_t>(c + 3) * (D + 2) + 2 + e];
+    // nthr / D groups of chunks per dimension, 8 chunk loads in flight per thread
+    const int ngrp = nthr / D, e = tid % D, grp = tid / D;
+    constexpr int U = 8;
+    float a = 0.f;
+    for (int c0 = grp; c0 < nc; c0 += U * ngrp) {
+        float v[U], wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * ngrp;
+            v[u] = c < nc ? pp[static_cast<size_t>(c) * (D + 2) + 2 + e] : 0.f;
+            wv[u] = c < nc ? wsh[c] : 0.f;
         }
-        for (; c < nc; ++c) a0 += wsh[c] * pp[static_cast<size_t>(c) * (D + 2) + 2 + e];
-        const float a = (a0 + a1) + (a2 + a3);
-        P.out[static_cast<size_t>(bh) * D + e] = ok ? a / l : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) a = __builtin_fmaf(wv[u], v[u], a);
+    }
+    accs[tid] = a;
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+        for (int gi = 0; gi < ngrp; ++gi) t += accs[gi * D + tid];
+        P.out[static_cast<size_t>(bh) * D + tid] = ok ? t / l : 0.0f;
     }
     if (tid == 0) {
         P.lse[bh] = ok ? M + __logf(l) : -__builtin_inff();
@@ -1185,14 +1277,18 @@ struct Marks {
 
 template <int D, typename KVT, int G>
 static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) {
-    const dim3 grid_c(p.ncg, p.B * p.Hkv);
+    const dim3 grid_c(p.ncg, p.B * p.Hkv);         // (chunk, group)
+    const dim3 grid_h(p.Hkv, p.ncg, p.B);          // (KV head, chunk, sequence)
     int rc = 0;
-    hipLaunchKernelGGL((k_base<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
+    hipLaunchKernelGGL((k_base<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
     if ((rc = mk.mark(3))) return rc;
-    hipLaunchKernelGGL((k_budget<G>), dim3(p.B * p.Hkv), dim3(kGroupThreads), 0, st, p);
+    hipLaunchKernelGGL((k_stats<G>), dim3((p.ncg + kStatsChunks - 1) / kStatsChunks, p.B * p.Hkv),
+                       dim3(kChunkThreads), 0, st, p);
     if ((rc = mk.mark(4))) return rc;
+    hipLaunchKernelGGL(k_budget, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
+    if ((rc = mk.mark(5))) return rc;
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
-    return mk.mark(5);
+    return mk.mark(6);
 }
 
 template <int ROW, typename T, int G>
@@ -1228,7 +1324,7 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
     if (rc) return rc;
     if ((rc = mk.mark(1))) return rc;
     // 2. exact top-k, bitmap, base threshold
-    hipLaunchKernelGGL((k_select<G>), dim3(p.B * p.Hkv), dim3(kGroupThreads), 0, st, p);
+    hipLaunchKernelGGL(k_select, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
     if ((rc = mk.mark(2))) return rc;
     // 3-5. base scores, budget, gather
     if (p.d == 128)
@@ -1252,9 +1348,9 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
     }
     if (rc) return rc;
     hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
-    if ((rc = mk.mark(6))) return rc;
-    if (p.idx) hipLaunchKernelGGL(k_emit, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
     if ((rc = mk.mark(7))) return rc;
+    if (p.idx) hipLaunchKernelGGL(k_emit, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
+    if ((rc = mk.mark(8))) return rc;
     return static_cast<int>(hipGetLastError());
 }
 

@@ -7,7 +7,8 @@ namespace vattn {
 
 constexpr int kPage = 16;
 constexpr int kPredThreads = 1024;   // predictor + chunk top-k
-constexpr int kGroupThreads = 1024;  // per-(b, KV head) selection / budget
+constexpr int kSelectThreads = 1024; // per-head exact top-k and base threshold
+constexpr int kBudgetThreads = 256;  // per-head budget and final threshold
 constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
 constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
@@ -26,7 +27,7 @@ struct HeadState {
     uint64_t thr_n;  // final sample = tail tokens with sample key >= thr_n (n > 0)
     float m;         // max pinned score over I_f and the base sample
     float wsamp;     // N_t / n as fp32
-    uint64_t SF, S1, S2hi, S2lo;
+    uint64_t SF, S1, S2hi, S2lo;  // zeroed by select, accumulated by stats
 };
 
 struct Plan {
@@ -55,7 +56,8 @@ struct Plan {
     float* sc;       // [B*Hkv][max_seq_len][G] pinned exact scores (base-sample union)
     float* cmax;     // [B*Hq][ncg] chunk max of pinned scores
     float* part;     // [B*Hq][ncg][d + 2] online-softmax partials (m, l, acc[d])
-    uint32_t* shist; // [B*Hkv][ncp][kSampBins] sampler-word histogram of each chunk's middle
+    uint32_t* soff;  // [B*Hkv][ncp][kSampBins + 1] bin offsets of each chunk's middle tokens
+    int32_t* slist;  // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
     int32_t* btok;   // [B*Hkv][ncg][cg] base-pass member tokens, ascending
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
