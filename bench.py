@@ -1,7 +1,7 @@
 """Benchmark of the verified sparse-attention decode step on one MI355X.
 
-A step is one vattn_decode call (predict, select, base, budget, gather,
-combine) over one batch of the Llama-3-8B-shaped workload: 8 sequences of
+A step is one vattn_decode call (predict, select, base, stats, budget,
+gather, combine) over one batch of the Llama-3-8B-shaped workload: 8 sequences of
 32768 tokens, 32 query / 8 KV heads, head dim 128, bf16 paged KV cache,
 rank-32 low-rank predictor, sinks 128, window 128, top-k 2.5%,
 eps = delta = 0.05.  Inputs are synthetic and resident in HBM before timing.
@@ -174,6 +174,8 @@ def main():
     pred_row = r * 2 if w.cfg["predictor"] == 1 else row
     pred_bytes = float(w.Hkv * (L * pred_row + np.ceil(L / 16) * 4).sum())
     base_bytes = float((Bc * row + Bc * G * 4).sum())
+    # V rows of the union, K rows not scored by the base pass, cached scores,
+    # chunk partials written
     gather_bytes = float((U * row + (U - Bc) * row + Bc * G * 4).sum()
                          + w.B * w.Hq * ncg * (d + 2) * 4)
     step_bytes = pred_bytes + float((U * 2 * row).sum())

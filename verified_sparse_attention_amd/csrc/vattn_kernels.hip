@@ -14,9 +14,9 @@
 //   stats    (chunk, b*Hkv)  exact fixed-point denominator statistics of the
 //                            chunk's members, added to each head's totals
 //   budget   (b*Hq)          CLT budget, final-sample threshold
-//   gather   (chunk, b*Hkv)  one pass over the union of the group's index sets:
-//                            K row (unless its score is cached) and V row per
-//                            token, weighted online softmax for each member head
+//   gather   (chunk, b*Hkv)  over the union of the group's index sets: K row
+//                            (unless its score is cached) and V row per token,
+//                            weighted softmax partials per chunk
 //   combine  (b*Hq)          merge chunk partials -> out, lse, counts, stats
 //   emit     (b*Hq)          optional: the index set in ascending order
 //
@@ -34,7 +34,7 @@
 namespace vattn {
 
 constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
-constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass
+constexpr int kBaseUnroll = 4;  // K rows in flight per lane group in the base pass
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
 __device__ __forceinline__ bool bit_of(const uint32_t* row, int i) {
@@ -75,6 +75,38 @@ size_t predict_lds_bytes(int G, int d, int row, int cp) {
            sizeof(uint32_t) * static_cast<size_t>(G) * cp;
 }
 
+// q~[h][j] = pdot(q_s[h], P[:, j]) in two steps: every chain of 8 (one per
+// thread, consecutive threads on consecutive j so the projection loads
+// coalesce) into `part`, then one thread per output adds the D / 8 chain sums
+// in the pairwise tree order.  Ends with a barrier.
+template <int D, int ROW, int G>
+__device__ __forceinline__ void low_rank_query(const float* qs, const float* __restrict__ proj, float* qv,
+                                               float* part, int tid, int nthr) {
+    constexpr int NB = D / 8;
+    for (int x = tid; x < G * NB * ROW; x += nthr) {
+        const int j = x % ROW, hb = x / ROW, h = hb / NB, e = hb - h * NB;
+        float a[8], pb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            a[k] = qs[h * D + 8 * e + k];
+            pb[k] = proj[(8 * e + k) * ROW + j];
+        }
+        part[(h * ROW + j) * NB + e] = chain8(a, pb);
+    }
+    __syncthreads();
+    for (int o = tid; o < G * ROW; o += nthr) {
+        float t[NB];
+#pragma unroll
+        for (int e = 0; e < NB; ++e) t[e] = part[o * NB + e];
+#pragma unroll
+        for (int w = NB; w > 1; w >>= 1)
+#pragma unroll
+            for (int e = 0; e < w / 2; ++e) t[e] = t[2 * e] + t[2 * e + 1];
+        qv[o] = t[0];
+    }
+    __syncthreads();
+}
+
 template <int ROW, typename T, int G>
 __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -106,6 +138,11 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
     for (int x = tid; x < kSampBins; x += nthr) shist[x] = 0;
     for (int x = tid; x < ntok / kPage; x += nthr) pages[x] = btrow[tb / kPage + x];
+    // scaled queries of the group's heads: q_s = fl32(q * fl32(1/sqrt(d)))
+    for (int x = tid; x < G * d; x += nthr) {
+        const int h = x / d, cc = x - h * d;
+        qs[x] = P.q[(static_cast<size_t>(b) * P.Hq + g * G + h) * d + cc] * P.scale32;
+    }
     __syncthreads();
     uint32_t* uwg = P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
     for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
@@ -156,22 +193,15 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     }
 
     if (R.k > 0) {
-        // 1) query vectors: q_s = fl32(q * fl32(1/sqrt(d))); low-rank q~ = pdot(q_s, P[:, j])
-        for (int x = tid; x < G * d; x += nthr) {
-            const int h = x / d, cc = x - h * d;
-            qs[x] = P.q[(static_cast<size_t>(b) * P.Hq + g * G + h) * d + cc] * P.scale32;
-        }
-        __syncthreads();
+        // 1) low-rank queries q~ = pdot(q_s, P[:, j])
         if (P.predictor == 1) {
-            for (int x = tid; x < G * ROW; x += nthr) {
-                const int h = x / ROW, j = x - h * ROW;
-                qv[x] = (d == 128) ? pdot_serial<128>(qs + h * d, 1, P.proj + j, ROW)
-                                   : pdot_serial<64>(qs + h * d, 1, P.proj + j, ROW);
-            }
+            float* part = reinterpret_cast<float*>(keys);  // free until the score stream
+            if (d == 128) low_rank_query<128, ROW, G>(qs, P.proj, qv, part, tid, nthr);
+            else low_rank_query<64, ROW, G>(qs, P.proj, qv, part, tid, nthr);
         } else {
             for (int x = tid; x < G * ROW; x += nthr) qv[x] = qs[x];
+            __syncthreads();
         }
-        __syncthreads();
 
         // 2) scores: LPT lanes per token row, 8 elements per lane, kUnroll rows in flight
         constexpr int LPT = ROW / 8, TPW = 64 / LPT;
@@ -421,27 +451,28 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     if (T0 >= L) return;
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    // the heads' state, the quad's page, sample words and each head's bitmap
+    // word (a quad never straddles a 32-token word) are requested together
     if (tid < G) {
         const HeadState& s = P.hs[bh0 + tid];
         hv[tid] = HeadView{s.thr_b, 0, s.nb, 0, 0.f, 0.f};
     }
+    const int T1 = min(T0 + P.cg, L);
+    const int qd = (T0 >> 2) + tid;
+    const bool live4 = 4 * qd < T1;
+    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const uint32_t row0 = live4 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
+    const bool anyM = live4 && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
+    const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+    uint32_t fw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
     __syncthreads();
 
-    // membership (one Philox call per 4 tokens): meta = base mask | fixed mask << 8
-    const int T1 = min(T0 + P.cg, L);
+    // membership (one Philox word per token): meta = base mask | fixed mask << 8
     uint32_t m4[4] = {0, 0, 0, 0};
     uint32_t mine = 0;
-    const int qd = (T0 >> 2) + tid;
-    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
-    const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
-    if (4 * qd < T1) {
-        // the quad's sample words and each head's bitmap word (a quad never
-        // straddles a 32-token word), all requested before use
-        const bool anyM = 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
-        const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
-        uint32_t fw[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) fw[h] = P.bits[(bh0 + h) * P.words + (qd >> 3)];
+    if (live4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
@@ -769,7 +800,8 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ HeadView hv[G];
     __shared__ float wred[NW][G];
     __shared__ float hmax[G], hsum[G];
-    __shared__ float wacc[NW][G][D];
+    static_assert(NW * D <= kGatherChunk, "per-wave sums fit in the weight array");
+    float (*wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&sp[0][0]);  // reuses sp after the V pass
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
@@ -778,26 +810,28 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     if (T0 >= L) return;
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    // the heads' state, the quad's page, sample words and each head's bitmap
+    // word are requested together
     if (tid < G) {
         const HeadState& s = P.hs[bh0 + tid];
         hv[tid] = HeadView{s.thr_b, s.thr_n, s.nb, s.n, s.wsamp, s.m};
     }
+    const int T1 = min(T0 + P.cg, L);
+    const int qd = (T0 >> 2) + tid;
+    const bool live4 = 4 * qd < T1;
+    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const uint32_t row0 = live4 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
+    const bool anyM = live4 && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
+    const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+    uint32_t fw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
     __syncthreads();
 
     // membership: meta = final mask | fixed mask << 8 | score cached << 16
-    const int T1 = min(T0 + P.cg, L);
     uint32_t m4[4] = {0, 0, 0, 0};
     uint32_t mine = 0;
-    const int qd = (T0 >> 2) + tid;
-    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
-    const uint32_t row0 = 4 * qd < T1 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
-    if (4 * qd < T1) {
-        // the quad's sample words and each head's bitmap word, requested together
-        const bool anyM = 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
-        const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
-        uint32_t fw[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) fw[h] = P.bits[(bh0 + h) * P.words + (qd >> 3)];
+    if (live4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * qd + e;
@@ -1078,6 +1112,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+    __syncthreads();  // every wave is done with the weights before their space is reused
     if (slot == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
