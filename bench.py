@@ -223,6 +223,34 @@ def main():
                            "union_density": round(float((U / L).mean()), 4)},
               "stage_us": stages}
 
+    # ---- key-side maintenance: append each sequence's newest token (K, V and
+    # its low-rank key row).  Rewriting the current newest token with its own
+    # values keeps the caches unchanged.
+    if kt0 is not None:
+        pos = (sl - 1).to(torch.int32)
+        rows = []
+        for b in range(w.B):
+            p_ = int(w.seq_lens[b]) - 1
+            rows.append(int(w.block_table[b, p_ // 16]))
+        pages = torch.tensor(rows, device=dev).long()
+        slots = (pos.long() % 16)
+        k_new = k0[pages, :, slots].contiguous()
+        v_new = v0[pages, :, slots].contiguous()
+        n_app = 200
+        vsa.append_kv(k_new, v_new, pos, bt, k0, v0, k_lowrank=kt0, proj=proj)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(n_app):
+            vsa.append_kv(k_new, v_new, pos, bt, k0, v0, k_lowrank=kt0, proj=proj)
+        a1.record()
+        torch.cuda.synchronize()
+        app_us = a0.elapsed_time(a1) / n_app * 1e3
+        app_bytes = w.B * w.Hkv * (4 * d * esize + r * 2)
+        result["key_append"] = {"us": round(app_us, 2), "algorithmic_bytes": app_bytes,
+                                "note": "one new token per sequence: K, V and its low-rank key row"}
+        log("append %.2f us per call" % app_us)
+
     if not args.profile:
         # ---- (eps, delta): denominator relative error vs a dense fp32 reference
         with torch.no_grad():

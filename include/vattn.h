@@ -157,6 +157,32 @@ vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const flo
                                 uint16_t* k_lowrank, int32_t num_blocks, int32_t Hkv,
                                 int32_t d, int32_t r, void* hip_stream);
 
+/* Key-side maintenance for one decode step: writes the newest token of each
+ * sequence into the paged caches and, when k_lowrank is given, its low-rank
+ * key row, so the predictor stream of the next vattn_decode sees it (the
+ * window of the decode step includes this newest token).
+ * For every b < B with pos[b] >= 0, page = block_table[b][pos[b] / 16],
+ * slot = pos[b] % 16, and every KV head g:
+ *   k_cache[page][g][slot][:]   = k_new[b][g][:]
+ *   v_cache[page][g][slot][:]   = v_new[b][g][:]
+ *   k_lowrank[page][g][slot][j] = bf16_rne(pdot(k_new[b][g][:], P[:, j]))
+ * with the same pdot and rounding as vattn_project_keys.  pos[b] < 0 leaves
+ * sequence b untouched.
+ * k_new, v_new: [B, Hkv, d] in kv_dtype (device); pos: [B] int32 (device);
+ * block_table: [B, max_blocks] int32 (device); caches as for vattn_decode;
+ * k_lowrank and proj ([d, r] fp32) are both NULL or both given.  All pointers
+ * are caller-owned and 16-byte aligned; the library allocates nothing.
+ * Returns VATTN_E_NULL, VATTN_E_DTYPE, VATTN_E_SHAPE or VATTN_E_UNSUPPORTED
+ * before any launch for bad arguments, VATTN_E_HIP for a failed launch.
+ * pos[b] >= 16 * max_blocks and block ids outside [0, num_blocks) are
+ * undefined behaviour (not checked on the device).  Two sequences must not
+ * write the same page slot.  Asynchronous on hip_stream. */
+vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
+                             const int32_t* block_table, int32_t B, int32_t max_blocks,
+                             void* k_cache, void* v_cache, uint16_t* k_lowrank, const float* proj,
+                             int32_t kv_dtype, int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r,
+                             void* hip_stream);
+
 /* z = Phi^-1(1 - delta/2) rounded to fp32, as vattn_decode uses it (host). */
 double vattn_z_from_delta(double delta);
 

@@ -117,6 +117,28 @@ def test_null_and_workspace_errors(lib):
     assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 0, 2, 128, 32, None) == 2
 
 
+def test_append_kv_argument_checks(lib):
+    P = C.c_void_p
+    ok = dict(k_new=P(256), v_new=P(256), pos=P(256), bt=P(256), B=4, mb=8, kc=P(256), vc=P(256),
+              kt=P(256), proj=P(256), dt=1, nb=32, Hkv=2, d=128, r=32)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.vattn_append_kv(a["k_new"], a["v_new"], a["pos"], a["bt"], a["B"], a["mb"], a["kc"],
+                                   a["vc"], a["kt"], a["proj"], a["dt"], a["nb"], a["Hkv"], a["d"], a["r"],
+                                   None)
+    assert call(k_new=None) == 1
+    assert call(pos=None) == 1
+    assert call(kt=None) == 1          # projection without an output
+    assert call(dt=5) == 3
+    assert call(B=0) == 2
+    assert call(Hkv=0) == 2
+    assert call(d=96) == 6
+    assert call(r=24) == 6
+    assert call(d=64, r=128) == 6     # rank above the head dim
+    assert call(kc=P(260)) == 2        # misaligned
+
+
 def test_workspace_size_monotone(lib):
     cfg = _cfg()
     prev = 0

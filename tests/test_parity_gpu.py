@@ -179,6 +179,44 @@ def test_project_keys_bit_exact():
         assert np.array_equal(kt, want)
 
 
+def test_append_kv_bit_exact():
+    """The newest token of each sequence lands at its page slot in K and V, and
+    its low-rank row equals the oracle's projection; other rows are untouched."""
+    import torch
+    import verified_sparse_attention_amd as vsa
+    _, log = _gpu()
+    for (d, r, dt, with_lr) in ((128, 32, torch.bfloat16, True), (64, 16, torch.float32, True),
+                                (128, 64, torch.bfloat16, True), (64, 32, torch.bfloat16, False)):
+        log("[parity] append_kv d=%d r=%d %s lowrank=%s" % (d, r, dt, with_lr))
+        gen = torch.Generator().manual_seed(7000 + d + r)
+        B, Hkv, max_blocks = 5, 3, 6
+        nb = B * max_blocks + 4
+        bt = torch.randperm(nb, generator=gen)[:B * max_blocks].reshape(B, max_blocks).to(torch.int32)
+        pos = torch.tensor([0, 17, 95, -1, 40], dtype=torch.int32)  # -1: no new token
+        k_cache = torch.randn(nb, Hkv, 16, d, generator=gen).to(dt)
+        v_cache = torch.randn(nb, Hkv, 16, d, generator=gen).to(dt)
+        k_new = (torch.randn(B, Hkv, d, generator=gen) * 2.0).to(dt)
+        v_new = torch.randn(B, Hkv, d, generator=gen).to(dt)
+        P = synthetic.orthonormal(d, r, gen)
+        kt0 = torch.randint(-30000, 30000, (nb, Hkv, 16, r), generator=gen, dtype=torch.int16)
+        kc, vc, kt = k_cache.cuda(), v_cache.cuda(), kt0.cuda()
+        vsa.append_kv(k_new.cuda(), v_new.cuda(), pos.cuda(), bt.cuda(), kc, vc,
+                      k_lowrank=kt if with_lr else None, proj=P.cuda() if with_lr else None)
+        torch.cuda.synchronize()
+        want_k, want_v, want_t = k_cache.clone(), v_cache.clone(), kt0.numpy().view(np.uint16).copy()
+        for b in range(B):
+            p = int(pos[b])
+            if p < 0:
+                continue
+            page, slot = int(bt[b, p // 16]), p % 16
+            want_k[page, :, slot] = k_new[b]
+            want_v[page, :, slot] = v_new[b]
+            if with_lr:
+                want_t[page, :, slot] = oracle.project_rows(k_new[b].float().numpy(), P.numpy())
+        assert torch.equal(kc.cpu(), want_k) and torch.equal(vc.cpu(), want_v)
+        assert np.array_equal(kt.cpu().numpy().view(np.uint16), want_t)
+
+
 def test_deterministic_repeat():
     w = SMALL_CASES["gqa4_bf16_ragged"]()
     GpuCase, log = _gpu()

@@ -27,7 +27,7 @@ PRED_EXACT, PRED_LOWRANK = 0, 1
 STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
 EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
-           "vattn_z_from_delta", "vattn_status_string")
+           "vattn_append_kv", "vattn_z_from_delta", "vattn_status_string")
 NUM_STAGES = 8
 STAGES = ("predict", "select", "base", "stats", "budget", "gather", "combine", "emit")
 
@@ -83,6 +83,10 @@ def load():
         lib.vattn_project_keys.restype = C.c_int
         lib.vattn_project_keys.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                            C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+        lib.vattn_append_kv.restype = C.c_int
+        lib.vattn_append_kv.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                        C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
         lib.vattn_z_from_delta.restype = C.c_double
         lib.vattn_z_from_delta.argtypes = [C.c_double]
         lib.vattn_status_string.restype = C.c_char_p
@@ -249,6 +253,19 @@ def project_keys(k_cache, proj, k_lowrank=None, stream=None):
     if rc != 0:
         raise VattnError(rc, "vattn_project_keys")
     return k_lowrank
+
+
+def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, proj=None, stream=None):
+    """Writes each sequence's newest token (k_new, v_new: [B, Hkv, d]) at position pos[b]
+    of the paged caches, and its low-rank key row when k_lowrank/proj are given."""
+    B, Hkv, d = k_new.shape
+    nb = k_cache.shape[0]
+    r = proj.shape[1] if proj is not None else 0
+    rc = load().vattn_append_kv(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), B,
+                                block_table.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_lowrank),
+                                _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, r, _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_append_kv")
 
 
 def z_from_delta(delta: float) -> float:

@@ -264,6 +264,28 @@ vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const flo
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 
+vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
+                             const int32_t* block_table, int32_t B, int32_t max_blocks, void* k_cache,
+                             void* v_cache, uint16_t* k_lowrank, const float* proj, int32_t kv_dtype,
+                             int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r, void* hip_stream) {
+    if (!k_new || !v_new || !pos || !block_table || !k_cache || !v_cache) return VATTN_E_NULL;
+    if ((k_lowrank == nullptr) != (proj == nullptr)) return VATTN_E_NULL;
+    if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (B < 1 || max_blocks < 1 || num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
+    if (static_cast<long long>(B) * Hkv > 0x7FFFFFFFLL) return VATTN_E_SHAPE;
+    if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
+    if (k_lowrank) {
+        if (r != 16 && r != 32 && r != 64) return VATTN_E_UNSUPPORTED;
+        if (r > d) return VATTN_E_SHAPE;
+    }
+    const void* ptrs[] = {k_new, v_new, k_cache, v_cache, k_lowrank, proj};
+    for (const void* q : ptrs)
+        if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return VATTN_E_SHAPE;
+    const int rc = vattn::launch_append(k_new, v_new, pos, block_table, B, max_blocks, k_cache, v_cache, k_lowrank,
+                                        proj, kv_dtype == VATTN_BF16, Hkv, d, k_lowrank ? r : 16, hip_stream);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
 const char* vattn_status_string(vattn_status s) {
     switch (s) {
         case VATTN_OK: return "VATTN_OK";

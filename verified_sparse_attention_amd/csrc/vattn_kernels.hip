@@ -1299,6 +1299,43 @@ __global__ __launch_bounds__(256) void k_project(const KVT* __restrict__ k, cons
 }
 
 // ===========================================================================
+// append: the newest token of each sequence into the paged caches, with its
+// low-rank key row (same pdot and rounding as the projection above)
+// ===========================================================================
+template <typename KVT, int D, int RK>
+__global__ __launch_bounds__(64) void k_append(const KVT* __restrict__ k_new, const KVT* __restrict__ v_new,
+                                               const int32_t* __restrict__ pos, const int32_t* __restrict__ bt,
+                                               int max_blocks, int Hkv, KVT* __restrict__ kc, KVT* __restrict__ vc,
+                                               uint16_t* __restrict__ kt, const float* __restrict__ proj) {
+    __shared__ float kr[D];
+    const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv, lane = threadIdx.x;
+    const int p = pos[b];
+    if (p < 0) return;
+    const long long row = (static_cast<long long>(bt[static_cast<size_t>(b) * max_blocks + p / kPage]) * Hkv + g) *
+                              kPage + p % kPage;
+    const KVT* ks = k_new + static_cast<size_t>(bg) * D;
+    const KVT* vs = v_new + static_cast<size_t>(bg) * D;
+    for (int e = lane; e < D; e += 64) {
+        const KVT kv = ks[e];
+        kc[row * D + e] = kv;
+        vc[row * D + e] = vs[e];
+        if constexpr (sizeof(KVT) == 2) {
+            kr[e] = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t&>(kv)) << 16);
+        } else {
+            kr[e] = kv;
+        }
+    }
+    if (kt == nullptr) return;  // block-uniform
+    __syncthreads();
+    for (int j = lane; j < RK; j += 64) {
+        const float s = pdot_serial<D>(kr, 1, proj + j, RK);
+        uint32_t u = __float_as_uint(s);
+        u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
+        kt[row * RK + j] = static_cast<uint16_t>(u >> 16);
+    }
+}
+
+// ===========================================================================
 // host-side dispatch
 // ===========================================================================
 // Records events[k] (when profiling) after the k-th stage.
@@ -1424,6 +1461,36 @@ int launch_project(const void* k_cache, int kv_bf16, const float* proj, uint16_t
     } else {
         if (kv_bf16) launch_project_t<uint16_t, 64>(k_cache, proj, kt, nrows, r, st);
         else launch_project_t<float, 64>(k_cache, proj, kt, nrows, r, st);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+template <typename KVT, int D>
+static void launch_append_t(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
+                            int max_blocks, void* kc, void* vc, uint16_t* kt, const float* proj, int Hkv, int r,
+                            hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(B * Hkv));
+    const KVT* kn = static_cast<const KVT*>(k_new);
+    const KVT* vn = static_cast<const KVT*>(v_new);
+    KVT* kcc = static_cast<KVT*>(kc);
+    KVT* vcc = static_cast<KVT*>(vc);
+    switch (r) {
+        case 16: hipLaunchKernelGGL((k_append<KVT, D, 16>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
+        case 32: hipLaunchKernelGGL((k_append<KVT, D, 32>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
+        default: hipLaunchKernelGGL((k_append<KVT, D, 64>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
+    }
+}
+
+int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int kv_bf16,
+                  int Hkv, int d, int r, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d == 128) {
+        if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
+        else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
+    } else {
+        if (kv_bf16) launch_append_t<uint16_t, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
+        else launch_append_t<float, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
     }
     return static_cast<int>(hipGetLastError());
 }

@@ -79,5 +79,8 @@ int launch_decode(const Plan& p, void* stream, void* const* events = nullptr);
 int launch_project(const void* k_cache, int kv_bf16, const float* proj, uint16_t* kt,
                    int num_blocks, int Hkv, int d, int r, void* stream);
 size_t predict_lds_bytes(int G, int d, int row, int cp);
+int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int kv_bf16,
+                  int Hkv, int d, int r, void* stream);
 
 }  // namespace vattn
