@@ -786,6 +786,7 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
 // then per head the block max and the weights p = w exp(s - max); (2) a pure
 // stream of V rows accumulating sum_i p_i V_i.  Every weight is computed once.
 // ===========================================================================
+constexpr float kRescale = 16.0f;  // reference-maximum headroom for the weights (e^16)
 constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group
 constexpr int kTilesPerBatch = 3;  // 16-token K tiles per batch and wave
 
@@ -800,6 +801,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ HeadView hv[G];
     __shared__ float wred[NW][G];
     __shared__ float hmax[G], hsum[G];
+    __shared__ int s_over;  // some member score exceeds its head's reference by kRescale
     static_assert(NW * D <= kGatherChunk, "per-wave sums fit in the weight array");
     float (*wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&sp[0][0]);  // reuses sp after the V pass
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -808,6 +810,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     const int L = P.seq_lens[b];
     const int T0 = c * P.cg;
     if (T0 >= L) return;
+    if (tid == 0) s_over = 0;
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
     // the heads' state, the quad's page, sample words and each head's bitmap
@@ -886,14 +889,20 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
             for (int h = 0; h < G; ++h) v[e][h] = cached ? scrow[at + h] : 0.0f;
         }
+        bool over = false;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int x = tid + e * nthr;
             if ((mm[e] >> 16) & 1u) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) sp[h][x] = ((mm[e] >> h) & 1u) ? v[e][h] : -__builtin_inff();
+                for (int h = 0; h < G; ++h) {
+                    const bool mem = (mm[e] >> h) & 1u;
+                    over |= mem && v[e][h] > hv[h].m + kRescale;
+                    sp[h][x] = mem ? v[e][h] : -__builtin_inff();
+                }
             }
         }
+        if (over) s_over = 1;
     }
     if constexpr (sizeof(KVT) == 2) {
         // bf16 keys: 16-token tiles on the matrix cores.  A = K rows (16 x D),
@@ -921,6 +930,9 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                     qb[cb][kb][e] = static_cast<__bf16>(part);
                 }
         }
+        float mref[NCB];  // reference of the head this lane writes
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) mref[cb] = hv[min(cb * 4 + col / 3, G - 1)].m;
         const int ntile = (n + 15) / 16;
         auto tile_row = [&](int x0) __attribute__((always_inline)) {
             // row of this lane's token; cached or absent tokens read a row that
@@ -952,13 +964,19 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                                                                  acc, 0, 0, 0);
                 const int hh = cb * 4 + col / 3;
                 const bool writer = col < 12 && col % 3 == 0 && hh < G;
+                bool over = false;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float sv = acc[r] + dpp<0x101>(acc[r]) + dpp<0x102>(acc[r]);  // row_shl:1, :2
                     const int x = x0 + 4 * kq + r;
                     const bool wr = writer && x < n && !((mr[r] >> 16) & 1u);
-                    if (wr) sp[hh][x] = ((mr[r] >> hh) & 1u) ? sv : -__builtin_inff();
+                    const bool mem = (mr[r] >> hh) & 1u;
+                    if (wr) {
+                        over |= mem && sv > mref[cb] + kRescale;
+                        sp[hh][x] = mem ? sv : -__builtin_inff();
+                    }
                 }
+                if (over) s_over = 1;
             }
         };
         // each wave scores kTilesPerBatch tiles per iteration, all of whose
@@ -1000,32 +1018,44 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 for (int h = 0; h < G; ++h) sv[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
                 if (j == LPT - 1 && xs[u] >= 0 && !cached) {
                     const int x = xs[u];
+                    bool over = false;
 #pragma unroll
-                    for (int h = 0; h < G; ++h) sp[h][x] = ((mk[u] >> h) & 1u) ? sv[h] : -__builtin_inff();
+                    for (int h = 0; h < G; ++h) {
+                        const bool mem = (mk[u] >> h) & 1u;
+                        over |= mem && sv[h] > hv[h].m + kRescale;
+                        sp[h][x] = mem ? sv[h] : -__builtin_inff();
+                    }
+                    if (over) s_over = 1;
                 }
             }
         }
     }
     __syncthreads();
-    // per-head block max, then weights and their sum
+    // weights against each head's base-pass maximum (the pinned maximum over
+    // its fixed set and base sample); only when some score here exceeds that
+    // by more than kRescale is the block's own maximum taken instead
     {
-        float mx[G];
+        if (s_over) {  // block-uniform: read after the barrier closing the score pass
+            float mx[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) mx[h] = -__builtin_inff();
-        for (int x = tid; x < n; x += nthr)
+            for (int h = 0; h < G; ++h) mx[h] = -__builtin_inff();
+            for (int x = tid; x < n; x += nthr)
 #pragma unroll
-            for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], sp[h][x]);
+                for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], sp[h][x]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float v = mx[h];
-            for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-            if (lane == 0) wred[wave][h] = v;
-        }
-        __syncthreads();
-        if (tid < G) {
-            float v = -__builtin_inff();
-            for (int w = 0; w < NW; ++w) v = fmaxf(v, wred[w][tid]);
-            hmax[tid] = v;
+            for (int h = 0; h < G; ++h) {
+                float v = mx[h];
+                for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+                if (lane == 0) wred[wave][h] = v;
+            }
+            __syncthreads();
+            if (tid < G) {
+                float v = -__builtin_inff();
+                for (int w = 0; w < NW; ++w) v = fmaxf(v, wred[w][tid]);
+                hmax[tid] = v;
+            }
+        } else if (tid < G) {
+            hmax[tid] = hv[tid].m;
         }
         __syncthreads();
         float hm[G], ls[G];
