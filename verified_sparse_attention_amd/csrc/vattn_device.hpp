@@ -88,6 +88,68 @@ __device__ __forceinline__ float tree_across_lanes(float v) {
     return v;
 }
 
+// The same tree for G heads at once, with the sums spread over the row's
+// lanes.  On each quad level (partners lane ^ 1, then lane ^ 2) that still
+// has more than one head per lane, a lane keeps half of its heads and adds its
+// partner's partials of them: G/2 + G/4 adds and G + G/2 selects in place of
+// 2G adds, and each sum then needs finishing (order key, store) in one lane
+// only.  Levels past that, and the row_ror levels of rows over 4 lanes, add as
+// tree_across_lanes does.  Every sum is the tree's (IEEE addition commutes).
+template <int G, int LPT>
+struct Spread {
+    static constexpr int lg(int x) { return x <= 1 ? 0 : 1 + lg(x / 2); }
+    // quad levels that split the heads
+    static constexpr int NS = lg(G) < lg(LPT) ? (lg(G) < 2 ? lg(G) : 2) : (lg(LPT) < 2 ? lg(LPT) : 2);
+    static constexpr int NH = G >> NS;  // heads held per lane
+    // head of slot e in row lane j
+    __device__ static __forceinline__ int head(int j, int e) {
+        int h = e;
+        if constexpr (NS >= 1) h += (j & 1) * (G / 2);
+        if constexpr (NS >= 2) h += ((j >> 1) & 1) * (G / 4);
+        return h;
+    }
+    // the lanes whose sums are complete and not duplicated in another lane
+    __device__ static __forceinline__ bool finisher(int j) { return (j | ((1 << NS) - 1)) == LPT - 1; }
+};
+
+template <int G, int LPT>
+__device__ __forceinline__ void spread_across_lanes(const float (&v)[G], float (&out)[Spread<G, LPT>::NH], int j) {
+    static_assert(LPT == 1 || LPT == 2 || LPT == 4 || LPT == 8 || LPT == 16, "row of 8..128 elements");
+    constexpr int NS = Spread<G, LPT>::NS;
+    float a[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) a[h] = v[h];
+    if constexpr (NS >= 1) {  // lane ^ 1: keep the lower or upper half of the heads
+        const bool up = j & 1;
+#pragma unroll
+        for (int k = 0; k < G / 2; ++k) {
+            const float keep = up ? a[k + G / 2] : a[k];
+            const float send = up ? a[k] : a[k + G / 2];
+            a[k] = keep + dpp<0xB1>(send);
+        }
+    } else if constexpr (LPT >= 2) {
+        a[0] = a[0] + dpp<0xB1>(a[0]);
+    }
+    if constexpr (NS >= 2) {  // lane ^ 2
+        const bool up = (j >> 1) & 1;
+#pragma unroll
+        for (int k = 0; k < G / 4; ++k) {
+            const float keep = up ? a[k + G / 4] : a[k];
+            const float send = up ? a[k] : a[k + G / 4];
+            a[k] = keep + dpp<0x4E>(send);
+        }
+    } else if constexpr (LPT >= 4) {
+#pragma unroll
+        for (int k = 0; k < (G >> NS); ++k) a[k] = a[k] + dpp<0x4E>(a[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < (G >> NS); ++k) {
+        if constexpr (LPT >= 8) a[k] = dpp<0x124>(a[k]) + a[k];   // row_ror:4
+        if constexpr (LPT >= 16) a[k] = dpp<0x128>(a[k]) + a[k];  // row_ror:8
+        out[k] = a[k];
+    }
+}
+
 // Sequential form of the same blocked dot (one thread), N a multiple of 8 with
 // N / 8 a power of two.
 template <int N>
@@ -517,10 +579,20 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
     for (int h = 0; h < NH; ++h) any |= want[h] > 0 && want[h] < total[h];
     for (int x = tid; x < NH * kTopBuckets; x += nthr) (&T.S.hist[0][0])[x] = 0;
     __syncthreads();
+    // the heads' bucket maps in registers (the visitors' head numbers are
+    // compile-time constants once inlined)
+    uint32_t md[NH];
+    float vmn[NH], scl[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        md[h] = T.mode[h];
+        vmn[h] = T.vmin[h];
+        scl[h] = T.scale[h];
+    }
     if (any) {
         // (B) bucket histogram
         items([&](int h, uint32_t ok, uint32_t) __attribute__((always_inline)) {
-            if (T.mode[h] == 1u) atomicAdd(&T.S.hist[h][topk_bucket(ok, T.vmin[h], T.scale[h])], 1u);
+            if (md[h] == 1u) atomicAdd(&T.S.hist[h][topk_bucket(ok, vmn[h], scl[h])], 1u);
         });
         __syncthreads();
         for (int h = wave; h < NH; h += nwaves) {
@@ -536,13 +608,15 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
         __syncthreads();
     }
     // (C) emit the keys above the boundary bucket, list the boundary bucket
+    int bst[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) bst[h] = T.bstar[h];
     items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
-        const uint32_t md = T.mode[h];
-        if (md == 2u) {
+        if (md[h] == 2u) {
             emit(h, topk_key(ok, idx));
-        } else if (md == 1u) {
-            const int bk = topk_bucket(ok, T.vmin[h], T.scale[h]);
-            const int bs = T.bstar[h];
+        } else if (md[h] == 1u) {
+            const int bk = topk_bucket(ok, vmn[h], scl[h]);
+            const int bs = bst[h];
             if (bk > bs) {
                 emit(h, topk_key(ok, idx));
             } else if (bk == bs) {

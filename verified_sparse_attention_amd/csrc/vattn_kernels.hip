@@ -35,6 +35,7 @@ namespace vattn {
 
 constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
 constexpr int kBaseUnroll = 4;  // K rows in flight per lane group in the base pass
+constexpr int kKeyPad = 16;     // words between the predictor's per-head key rows
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
 __device__ __forceinline__ bool bit_of(const uint32_t* row, int i) {
@@ -72,7 +73,7 @@ size_t predict_lds_bytes(int G, int d, int row, int cp) {
     }
     return align16(ts) + sizeof(uint32_t) * (kSampBins + kPredThreads / 64) + sizeof(int32_t) * (cp / kPage + 2) +
            sizeof(float) * (static_cast<size_t>(G) * d + static_cast<size_t>(G) * row) +
-           sizeof(uint32_t) * static_cast<size_t>(G) * cp;
+           sizeof(uint32_t) * static_cast<size_t>(G) * (cp + kKeyPad);
 }
 
 // q~[h][j] = pdot(q_s[h], P[:, j]) in two steps: every chain of 8 (one per
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     off += sizeof(int32_t) * (P.cp / kPage + 2);
     float* qs = reinterpret_cast<float*>(smem + off);  // [G][d]
     float* qv = qs + G * P.d;                           // [G][ROW]
-    uint32_t* keys = reinterpret_cast<uint32_t*>(qv + G * ROW);  // [G][cp]
+    uint32_t* keys = reinterpret_cast<uint32_t*>(qv + G * ROW);  // [G][ks]
+    const int ks = P.cp + kKeyPad;  // head stride of the keys: the G rows of a token in distinct banks
 
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -145,13 +147,21 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     }
     __syncthreads();
     uint32_t* uwg = P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
-    for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
-        const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
-        *reinterpret_cast<uint4*>(uwg + 4 * qd) = w;  // chunks are disjoint at quad granularity
+    // a chunk spans at most kPredKeys tokens: kPhx quads per thread, kept in
+    // registers for the scatter below
+    constexpr int kPhx = kPredKeys / 4 / kPredThreads;
+    uint4 wq[kPhx];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * qd + e;
-            if (i >= t0 && i < t1) atomicAdd(&shist[word_of(w, e) >> (32 - kSampBits)], 1u);
+    for (int e = 0; e < kPhx; ++e) {
+        const int qd = (t0 >> 2) + tid + e * nthr;
+        if (4 * qd < t1) {
+            wq[e] = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
+            *reinterpret_cast<uint4*>(uwg + 4 * qd) = wq[e];  // chunks are disjoint at quad granularity
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int i = 4 * qd + f;
+                if (i >= t0 && i < t1) atomicAdd(&shist[word_of(wq[e], f) >> (32 - kSampBits)], 1u);
+            }
         }
     }
     __syncthreads();
@@ -178,12 +188,15 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         // scatter into LDS (the score area is free until the stream), then one
         // coalesced copy of the chunk's sorted list
         int32_t* stage = reinterpret_cast<int32_t*>(keys);
-        for (int qd = (t0 >> 2) + tid; 4 * qd < t1; qd += nthr) {
-            const uint4 w = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * qd + e;
-                if (i >= t0 && i < t1) stage[atomicAdd(&shist[word_of(w, e) >> (32 - kSampBits)], 1u)] = i;
+        for (int e = 0; e < kPhx; ++e) {
+            const int qd = (t0 >> 2) + tid + e * nthr;
+            if (4 * qd < t1) {
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const int i = 4 * qd + f;
+                    if (i >= t0 && i < t1) stage[atomicAdd(&shist[word_of(wq[e], f) >> (32 - kSampBits)], 1u)] = i;
+                }
             }
         }
         __syncthreads();
@@ -203,8 +216,11 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             __syncthreads();
         }
 
-        // 2) scores: LPT lanes per token row, 8 elements per lane, kUnroll rows in flight
+        // 2) scores: LPT lanes per token row, 8 elements per lane; the G sums
+        //    of a row are spread over its lanes, each finished by one lane
         constexpr int LPT = ROW / 8, TPW = 64 / LPT;
+        using SP = Spread<G, LPT>;
+        constexpr int NH = SP::NH;
         const int j = lane % LPT, slot = lane / LPT;
         float qreg[G][8];
 #pragma unroll
@@ -213,58 +229,68 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             for (int e = 0; e < 8; ++e) qreg[h][e] = qv[h * ROW + 8 * j + e];
         const T* src = static_cast<const T*>(P.predictor == 1 ? static_cast<const void*>(P.kt) : P.k);
         const int cbase = c * P.cp;
-        uint32_t klo[G], khi[G];  // order-key range of the stored scores
+        const bool fin = SP::finisher(j);
+        int kst[NH];  // this lane's heads' score rows, offset by the chunk start
+        uint32_t klo[NH], khi[NH];  // order-key range of the stored scores
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            klo[h] = 0xFFFFFFFFu;
-            khi[h] = 0;
+        for (int e = 0; e < NH; ++e) {
+            kst[e] = SP::head(j, e) * ks - cbase;
+            klo[e] = 0xFFFFFFFFu;
+            khi[e] = 0;
         }
         if (tid < G) {
             TS.lo[tid] = 0xFFFFFFFFu;
             TS.hi[tid] = 0;
             TS.aux[tid] = 0;
         }
-        // rows past the chunk's last page reread its last row and are not stored.
-        // Each iteration requests its whole batch before scoring any of it
-        // (no loads carried across iterations, so the waits stay exact).
-        const int Hkv = P.Hkv, cp = P.cp;
-        uint32_t* __restrict__ kst = keys;
+        // Rows past the chunk's last page reread a row of that page and are
+        // not stored.  Each iteration requests its whole batch before scoring
+        // any of it (no loads carried across iterations, so the waits stay
+        // exact).  Token offsets are non-negative: unsigned page arithmetic.
+        const uint32_t pstride = static_cast<uint32_t>(P.Hkv) * kPage * ROW;  // elements per page
+        const T* gsrc = src + static_cast<size_t>(g) * kPage * ROW + 8 * j;
+        const uint32_t tlast = static_cast<uint32_t>(ntok - 1);
         // rows per lane group and batch: fewer when the G query registers are many
         constexpr int PU = G * sizeof(T) >= 32 ? 2 : G * sizeof(T) >= 16 ? 4 : 2 * kUnroll;
         for (int sb = wave * TPW * PU; sb < ntok; sb += nwaves * TPW * PU) {
             Raw8 kr[PU];
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
-                const int tl = min(sb + u * TPW + slot, ntok - 1);
-                load_raw(src + row_index(pages[tl / kPage], Hkv, g, (tb + tl) % kPage, ROW) + 8 * j, kr[u]);
+                const uint32_t tl = min(static_cast<uint32_t>(sb + u * TPW + slot), tlast);
+                const uint32_t pg = static_cast<uint32_t>(pages[tl / kPage]);
+                load_raw(gsrc + static_cast<uint64_t>(pg) * pstride + (tl % kPage) * ROW, kr[u]);
             }
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
-                const int tt = tb + min(sb + u * TPW + slot, ntok - 1);
+                const int tt = tb + sb + u * TPW + slot;
                 float kf[8];
                 widen<T>(kr[u], kf);
+                float part[G], sv[NH];
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float sc = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-                    if (j == LPT - 1 && tt >= t0 && tt < t1) {
-                        const uint32_t ok = okey(sc);
-                        kst[h * cp + (tt - cbase)] = ok;
-                        klo[h] = min(klo[h], ok);
-                        khi[h] = max(khi[h], ok);
+                for (int h = 0; h < G; ++h) part[h] = chain8(qreg[h], kf);
+                spread_across_lanes<G, LPT>(part, sv, j);
+                if (fin && tt >= t0 && tt < t1) {
+#pragma unroll
+                    for (int e = 0; e < NH; ++e) {
+                        const uint32_t ok = okey(sv[e]);
+                        keys[kst[e] + tt] = ok;
+                        klo[e] = min(klo[e], ok);
+                        khi[e] = max(khi[e], ok);
                     }
                 }
             }
         }
+        // lanes with the same j hold the same heads: reduce over the others
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            uint32_t a = klo[h], bb = khi[h];
-            for (int o = 1; o < 64; o <<= 1) {
+        for (int e = 0; e < NH; ++e) {
+            uint32_t a = klo[e], bb = khi[e];
+            for (int o = LPT; o < 64; o <<= 1) {
                 a = min(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
                 bb = max(bb, static_cast<uint32_t>(__shfl_xor(bb, o, 64)));
             }
-            if (lane == 0) {
-                atomicMin(&TS.lo[h], a);
-                atomicMax(&TS.hi[h], bb);
+            if (lane < LPT && fin) {
+                atomicMin(&TS.lo[SP::head(j, e)], a);
+                atomicMax(&TS.hi[SP::head(j, e)], bb);
             }
         }
         __syncthreads();
@@ -285,7 +311,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
             for (int t = t0 + tid; t < t1; t += nthr)
 #pragma unroll
-                for (int h = 0; h < G; ++h) f(h, keys[h * cp + (t - cbase)], static_cast<uint32_t>(t));
+                for (int h = 0; h < G; ++h) f(h, keys[h * ks + (t - cbase)], static_cast<uint32_t>(t));
         }, [&](int h, uint64_t key) __attribute__((always_inline)) {
             const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
             if (pos < static_cast<uint32_t>(kp)) cand[((bh0 + h) * ncp + c) * kcap + pos] = key;
