@@ -878,22 +878,26 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 cached |= (fx || sb) ? 1u : 0u;
             }
             m4[e] = fin ? (fin | (fxm << 8) | (cached << 16)) : 0u;
-            mine += fin ? 1u : 0u;
+            mine += fin ? (cached ? 0x10000u : 1u) : 0u;  // uncached count | cached count << 16
         }
     }
+    // list: the members whose scores still need their K rows first, [0, nu),
+    // then those with cached scores, [nu, n); both counts fit 16 bits
     uint32_t cnt;
-    uint32_t pos = block_excl_scan(mine, wsum, cnt);
+    const uint32_t pre = block_excl_scan(mine, wsum, cnt);
+    const int nu = static_cast<int>(cnt & 0xFFFFu);
+    uint32_t pu = pre & 0xFFFFu, pc = static_cast<uint32_t>(nu) + (pre >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (m4[e]) {
+            const uint32_t pos = ((m4[e] >> 16) & 1u) ? pc++ : pu++;
             tok[pos] = 4 * qd + e;
             tmeta[pos] = m4[e];
             trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
-            ++pos;
         }
-    if (tid == 0 && P.gcounts && cnt) atomicAdd(&P.gcounts[2 * bg], static_cast<int>(cnt));
+    const int n = nu + static_cast<int>(cnt >> 16);
+    if (tid == 0 && P.gcounts && n) atomicAdd(&P.gcounts[2 * bg], n);
     __syncthreads();
-    const int n = static_cast<int>(cnt);
 
     // (1) scores into LDS (-inf for heads the token does not belong to).
     // Tokens of the base pass take their cached pinned scores (independent
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         uint32_t mm[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int x = tid + e * nthr;
+            const int x = nu + tid + e * nthr;
             mm[e] = x < n ? tmeta[x] : 0u;
             const bool cached = (mm[e] >> 16) & 1u;
             const size_t at = static_cast<size_t>(cached ? tok[x] : 0) * G;
@@ -918,7 +922,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         bool over = false;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int x = tid + e * nthr;
+            const int x = nu + tid + e * nthr;
             if ((mm[e] >> 16) & 1u) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
@@ -959,14 +963,12 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         float mref[NCB];  // reference of the head this lane writes
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) mref[cb] = hv[min(cb * 4 + col / 3, G - 1)].m;
-        const int ntile = (n + 15) / 16;
+        const int ntile = (nu + 15) / 16;
         auto tile_row = [&](int x0) __attribute__((always_inline)) {
-            // row of this lane's token; cached or absent tokens read a row that
-            // is already needed (their result is not used)
+            // row of this lane's token; lanes past the uncached part read a
+            // row that is already needed (their result is not used)
             const int x = x0 + col;
-            const int xr = x < n ? x : x0;
-            const uint32_t m = tmeta[xr];
-            return ((m >> 16) & 1u) ? trow[x0] : trow[xr];
+            return trow[x < nu ? x : x0];
         };
         struct KTile {
             uint4 a[KB];
@@ -980,7 +982,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
             // metadata of the four rows this lane may write, read before the products
             uint32_t mr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mr[r] = tmeta[min(x0 + 4 * kq + r, n - 1)];
+            for (int r = 0; r < 4; ++r) mr[r] = tmeta[min(x0 + 4 * kq + r, nu - 1)];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 for (int r = 0; r < 4; ++r) {
                     const float sv = acc[r] + dpp<0x101>(acc[r]) + dpp<0x102>(acc[r]);  // row_shl:1, :2
                     const int x = x0 + 4 * kq + r;
-                    const bool wr = writer && x < n && !((mr[r] >> 16) & 1u);
+                    const bool wr = writer && x < nu;
                     const bool mem = (mr[r] >> hh) & 1u;
                     if (wr) {
                         over |= mem && sv > mref[cb] + kRescale;
@@ -1023,26 +1025,25 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
-        for (int base = wave * TPW * kUnroll; base < n; base += nwaves * TPW * kUnroll) {
+        for (int base = wave * TPW * kUnroll; base < nu; base += nwaves * TPW * kUnroll) {
             Raw8 kr[kUnroll];
             uint32_t mk[kUnroll];
             int xs[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int x = base + u * TPW + slot;
-                xs[u] = x < n ? x : -1;
-                mk[u] = x < n ? tmeta[x] : 0u;
-                load_raw(kbase + static_cast<size_t>(trow[x < n ? x : 0]) * D + 8 * j, kr[u]);
+                xs[u] = x < nu ? x : -1;
+                mk[u] = x < nu ? tmeta[x] : 0u;
+                load_raw(kbase + static_cast<size_t>(trow[x < nu ? x : 0]) * D + 8 * j, kr[u]);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const bool cached = (mk[u] >> 16) & 1u;
                 float kf[8];
                 widen<KVT>(kr[u], kf);
                 float sv[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) sv[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-                if (j == LPT - 1 && xs[u] >= 0 && !cached) {
+                if (j == LPT - 1 && xs[u] >= 0) {
                     const int x = xs[u];
                     bool over = false;
 #pragma unroll
