@@ -1,7 +1,7 @@
 """Benchmark of the verified sparse-attention decode step on one MI355X.
 
-A step is one vattn_decode call (predict, select, base, stats, budget,
-gather, combine) over one batch of the Llama-3-8B-shaped workload: 8 sequences of
+A step is one vattn_decode call (predict, select, base, budget, gather,
+combine) over one batch of the Llama-3-8B-shaped workload: 8 sequences of
 32768 tokens, 32 query / 8 KV heads, head dim 128, bf16 paged KV cache,
 rank-32 low-rank predictor, sinks 128, window 128, top-k 2.5%,
 eps = delta = 0.05.  Inputs are synthetic and resident in HBM before timing.

@@ -136,11 +136,11 @@ vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_ou
                           void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Kernels of one decode step, in launch order (for vattn_decode_profiled). */
-#define VATTN_NUM_STAGES 8 /* predict, select, base, stats, budget, gather, combine, emit */
+#define VATTN_NUM_STAGES 7 /* predict, select, base, budget, gather, combine, emit */
 
 /* vattn_decode, additionally recording caller-created hipEvent_t handles on
  * hip_stream: events[0] before the first kernel and events[s + 1] after stage s
- * (stage 7, emit, is empty when out->idx is NULL).  n_events must be
+ * (stage 6, emit, is empty when out->idx is NULL).  n_events must be
  * VATTN_NUM_STAGES + 1.  For measurement; timing adds event records only. */
 vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
                                    vattn_outputs* out, void* workspace, size_t ws_bytes,

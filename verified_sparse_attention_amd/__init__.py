@@ -28,8 +28,8 @@ STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYP
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
 EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
            "vattn_append_kv", "vattn_z_from_delta", "vattn_status_string")
-NUM_STAGES = 8
-STAGES = ("predict", "select", "base", "stats", "budget", "gather", "combine", "emit")
+NUM_STAGES = 7
+STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
 
 
 class VattnError(RuntimeError):

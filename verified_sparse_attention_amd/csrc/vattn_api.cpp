@@ -97,7 +97,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, btok, bmeta, bcnt, uw, crange, total;
+    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -123,8 +123,8 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * s.ncp * static_cast<size_t>(s.cp) * sizeof(int32_t));
     L.hh = off;
     off += align_up(BHq * vattn::kSampBins * sizeof(uint32_t));
-    L.btok = off;
-    off += align_up(BHkv * s.ncg * s.cg * sizeof(int32_t));
+    L.bsc = off;
+    off += align_up(BHkv * s.ncg * s.cg * s.G * sizeof(float));
     L.bmeta = off;
     off += align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t));
     L.bcnt = off;
@@ -216,7 +216,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.soff = reinterpret_cast<uint32_t*>(ws + L.soff);
     p.slist = reinterpret_cast<int32_t*>(ws + L.slist);
     p.hh = reinterpret_cast<uint32_t*>(ws + L.hh);
-    p.btok = reinterpret_cast<int32_t*>(ws + L.btok);
+    p.bsc = reinterpret_cast<float*>(ws + L.bsc);
     p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.uw = reinterpret_cast<uint32_t*>(ws + L.uw);

@@ -450,6 +450,20 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     }
 }
 
+// The G scores of one token as one vector store (the score rows are G floats,
+// G a power of two, so a row never straddles a 16-byte boundary).
+template <int G>
+__device__ __forceinline__ void store_scores(float* p, const float (&s)[G]) {
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int k = 0; k < G; k += 4) *reinterpret_cast<float4*>(p + k) = make_float4(s[k], s[k + 1], s[k + 2], s[k + 3]);
+    } else if constexpr (G == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(s[0], s[1]);
+    } else {
+        p[0] = s[0];
+    }
+}
+
 // ===========================================================================
 // base: pinned exact scores of the union of fixed sets and base samples
 // ===========================================================================
@@ -519,7 +533,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     }
     uint32_t cnt;
     uint32_t pos = block_excl_scan(mine, wsum, cnt);
-    int32_t* ltok = P.btok + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
     uint32_t* lmeta = P.bmeta + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -527,7 +540,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
             tok[pos] = 4 * qd + e;
             tmeta[pos] = m4[e];
             trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
-            ltok[pos] = 4 * qd + e;
             lmeta[pos] = m4[e];
             ++pos;
         }
@@ -550,17 +562,19 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     for (int h = 0; h < G; ++h) lmax[h] = -__builtin_inff();
     const KVT* kbase = static_cast<const KVT*>(P.k);
     float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
+    float* lsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
     const int n = static_cast<int>(cnt);
     constexpr int kBU = kBaseUnroll;
     for (int base = wave * TPW * kBU; base < n; base += nwaves * TPW * kBU) {
         Raw8 kr[kBU];
-        int tk[kBU];
+        int tk[kBU], xl[kBU];
         uint32_t mk[kBU];
 #pragma unroll
         for (int u = 0; u < kBU; ++u) {
             const int x = base + u * TPW + slot;
             const bool act = x < n;
             const int xs = act ? x : 0;
+            xl[u] = xs;
             tk[u] = tok[xs];
             mk[u] = act ? tmeta[xs] : 0u;
             load_raw(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kr[u]);
@@ -577,8 +591,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
                 for (int h = 0; h < G; ++h)
                     if ((mk[u] >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
                 if (mk[u]) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) scrow[static_cast<size_t>(tk[u]) * G + h] = s[h];
+                    store_scores<G>(scrow + static_cast<size_t>(tk[u]) * G, s);  // by token, for the gather
+                    store_scores<G>(lsc + static_cast<size_t>(xl[u]) * G, s);    // in list order, for the budget
                 }
             }
         }
@@ -598,134 +612,25 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 }
 
 // ===========================================================================
-// stats: exact fixed-point sums over one base chunk's member list, added to
-// the head's totals with integer atomics (exact, so order independent)
+// budget: exact statistics of the head's base sample, CLT budget, final-sample
+// threshold.  One block per query head.  The statistics are fixed-point
+// integer sums (order independent) over the base members of every chunk of
+// the head's group; each block reduces its own head, so no cross-block
+// accumulation is needed.
 // ===========================================================================
-constexpr int kStatsChunks = 4;  // base chunks per stats block
+constexpr int kStatsBatch = 4;  // entries of each of a wave's two chunks requested per lane at once
 
-template <int G>
-__global__ __launch_bounds__(kChunkThreads) void k_stats(Plan P) {
-    constexpr int NW = kChunkThreads / 64, kBatch = 4;
-    __shared__ float smax[G];
-    __shared__ uint64_t red[NW][G][4];
-    __shared__ int coff[kStatsChunks + 1];
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv, c0 = blockIdx.x * kStatsChunks;
-    const int L = P.seq_lens[b];
-    if (c0 * P.cg >= L) return;
-    const int nc = (L + P.cg - 1) / P.cg;
-    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-    if (wave == 0) {  // members of the block's chunks: counts -> offsets
-        const int cc = c0 + lane;
-        const uint32_t v = (lane < kStatsChunks && cc < nc) ? static_cast<uint32_t>(P.bcnt[static_cast<size_t>(bg) * P.ncg + cc]) : 0u;
-        const uint32_t inc = wave_incl_scan(v);
-        if (lane < kStatsChunks) coff[lane] = static_cast<int>(inc - v);
-        if (lane == kStatsChunks - 1) coff[kStatsChunks] = static_cast<int>(inc);
-    }
-    for (int hh = wave; hh < G; hh += NW) {  // m: max pinned score over I_f and the base sample
-        float m = -__builtin_inff();
-        for (int cc = lane; cc < nc; cc += 64) m = fmaxf(m, P.cmax[(bh0 + hh) * P.ncg + cc]);
-        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (lane == 0) smax[hh] = m;
-    }
-    __syncthreads();
-    const int total = coff[kStatsChunks];
-    if (total == 0) return;
-    const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
-    uint64_t sf[G], s1[G], s2lo[G], s2hi[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) sf[hh] = s1[hh] = s2lo[hh] = s2hi[hh] = 0;
-    for (int y0 = 0; y0 < total; y0 += kBatch * nthr) {
-        int ti[kBatch];
-        uint32_t tm[kBatch];
-#pragma unroll
-        for (int v = 0; v < kBatch; ++v) {
-            const int y = y0 + tid + v * nthr;
-            ti[v] = 0;
-            tm[v] = 0u;
-            if (y < total) {
-                int cc = 0;
-#pragma unroll
-                for (int t = 1; t < kStatsChunks; ++t) cc += y >= coff[t] ? 1 : 0;
-                const size_t at = (static_cast<size_t>(bg) * P.ncg + c0 + cc) * P.cg + (y - coff[cc]);
-                ti[v] = P.btok[at];
-                tm[v] = P.bmeta[at];
-            }
-        }
-        float sv[kBatch][G];
-#pragma unroll
-        for (int v = 0; v < kBatch; ++v)
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh)
-                sv[v][hh] = ((tm[v] >> hh) & 1u) ? scrow[static_cast<size_t>(ti[v]) * G + hh] : 0.0f;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float m = smax[hh];
-#pragma unroll
-            for (int v = 0; v < kBatch; ++v) {
-                const bool mem = (tm[v] >> hh) & 1u, fx = (tm[v] >> (8 + hh)) & 1u;
-                const uint64_t E = mem ? fixed_weight(sv[v][hh] - m) : 0ull;
-                const uint64_t Ef = fx ? E : 0ull, Es = fx ? 0ull : E;
-                sf[hh] += Ef;
-                s1[hh] += Es;
-                const unsigned __int128 e2 = static_cast<unsigned __int128>(Es) * Es;
-                const uint64_t lo = static_cast<uint64_t>(e2);
-                s2hi[hh] += static_cast<uint64_t>(e2 >> 64) + ((s2lo[hh] + lo < s2lo[hh]) ? 1u : 0u);
-                s2lo[hh] += lo;
-            }
-        }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        uint64_t a = sf[hh], b1 = s1[hh], lo = s2lo[hh], hi = s2hi[hh];
-        for (int o = 32; o >= 1; o >>= 1) {
-            a += shfl_xor_u64(a, o);
-            b1 += shfl_xor_u64(b1, o);
-            const uint64_t olo = shfl_xor_u64(lo, o), ohi = shfl_xor_u64(hi, o);
-            const uint64_t nlo = lo + olo;
-            hi = hi + ohi + (nlo < lo ? 1u : 0u);
-            lo = nlo;
-        }
-        if (lane == 0) {
-            red[wave][hh][0] = a;
-            red[wave][hh][1] = b1;
-            red[wave][hh][2] = hi;
-            red[wave][hh][3] = lo;
-        }
-    }
-    __syncthreads();
-    if (tid < G) {
-        uint64_t SF = 0, S1 = 0, lo = 0, hi = 0;
-        for (int w = 0; w < NW; ++w) {
-            SF += red[w][tid][0];
-            S1 += red[w][tid][1];
-            const uint64_t nlo = lo + red[w][tid][3];
-            hi += red[w][tid][2] + (nlo < lo ? 1u : 0u);
-            lo = nlo;
-        }
-        HeadState& hs = P.hs[bh0 + tid];
-        if (SF) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.SF), static_cast<unsigned long long>(SF));
-        if (S1) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S1), static_cast<unsigned long long>(S1));
-        if (lo) {  // 128-bit add: the carry out of the low word is known from its old value
-            const unsigned long long old =
-                atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S2lo), static_cast<unsigned long long>(lo));
-            hi += (old + lo < old) ? 1u : 0u;
-        }
-        if (hi) atomicAdd(reinterpret_cast<unsigned long long*>(&hs.S2hi), static_cast<unsigned long long>(hi));
-    }
-}
-
-// ===========================================================================
-// budget: CLT budget from the exact statistics, final-sample threshold
-// ===========================================================================
 __global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
+    constexpr int NW = kBudgetThreads / 64;
+    static_assert(NW >= 2, "one wave for m, one for the chunk offsets");
     __shared__ HeadSamp SS;
     __shared__ SelShared<1> FS;
+    __shared__ int coff[kMaxChunks + 1];  // member offsets of the group's base chunks
+    __shared__ uint64_t red[NW][4];
     __shared__ int s_nsel;
     __shared__ float s_m;
-    const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
-    const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
+    const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G, hg = h % P.G;
     const int bg = b * P.Hkv + g;
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
@@ -737,19 +642,102 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
         }
         return;
     }
+    const int nc = (L + P.cg - 1) / P.cg;
     for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
-    if (tid < 64) {  // m: max pinned score over I_f and the base sample
-        const int nc = (L + P.cg - 1) / P.cg;
+    if (wave == 0) {  // m: max pinned score over I_f and the base sample
         float m = -__builtin_inff();
         for (int c = lane; c < nc; c += 64) m = fmaxf(m, P.cmax[static_cast<size_t>(bh) * P.ncg + c]);
         for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
         if (lane == 0) s_m = m;
+    } else if (wave == 1) {  // member counts of the chunks -> offsets
+        const int32_t* cnt = P.bcnt + static_cast<size_t>(bg) * P.ncg;
+        uint32_t carry = 0;
+        for (int c0 = 0; c0 < nc; c0 += 64) {
+            const int c = c0 + lane;
+            const uint32_t v = c < nc ? static_cast<uint32_t>(cnt[c]) : 0u;
+            const uint32_t inc = wave_incl_scan(v);
+            if (c < nc) coff[c] = static_cast<int>(carry + inc - v);
+            carry += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
+        }
+        if (lane == 0) coff[nc] = static_cast<int>(carry);
+    }
+    __syncthreads();
+
+    // E_i = fixed_weight(s_i - m) over this head's members: SF over the fixed
+    // set, S1 and S2 (128-bit) over the base sample.  Each wave takes whole
+    // chunks, two at a time, every entry's mask and score requested before any
+    // is used.
+    {
+        const float m = s_m;
+        const int G = P.G;
+        const uint32_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
+        const float* bsc = P.bsc + static_cast<size_t>(bg) * P.ncg * P.cg * G + hg;
+        uint64_t sf = 0, s1 = 0, s2lo = 0, s2hi = 0;
+        for (int cw = wave; cw < nc; cw += 2 * NW) {
+            const int ca = cw, cb = cw + NW;
+            const int na = coff[ca + 1] - coff[ca], nb2 = cb < nc ? coff[cb + 1] - coff[cb] : 0;
+            const int nmax = max(na, nb2);
+            for (int y0 = 0; y0 < nmax; y0 += 64 * kStatsBatch) {
+                uint32_t tm[2][kStatsBatch];
+                float sv[2][kStatsBatch];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int cc = q ? cb : ca, ncc = q ? nb2 : na;
+#pragma unroll
+                    for (int v = 0; v < kStatsBatch; ++v) {
+                        const int y = y0 + lane + 64 * v;
+                        const size_t at = static_cast<size_t>(cc) * P.cg + y;
+                        tm[q][v] = y < ncc ? bmeta[at] : 0u;
+                        sv[q][v] = y < ncc ? bsc[at * G] : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int v = 0; v < kStatsBatch; ++v) {
+                        const bool mem = (tm[q][v] >> hg) & 1u, fx = (tm[q][v] >> (8 + hg)) & 1u;
+                        const uint64_t E = mem ? fixed_weight(sv[q][v] - m) : 0ull;
+                        const uint64_t Es = fx ? 0ull : E;
+                        sf += fx ? E : 0ull;
+                        s1 += Es;
+                        const unsigned __int128 e2 = static_cast<unsigned __int128>(Es) * Es;
+                        const uint64_t lo = static_cast<uint64_t>(e2);
+                        s2hi += static_cast<uint64_t>(e2 >> 64) + ((s2lo + lo < s2lo) ? 1u : 0u);
+                        s2lo += lo;
+                    }
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            sf += shfl_xor_u64(sf, o);
+            s1 += shfl_xor_u64(s1, o);
+            const uint64_t olo = shfl_xor_u64(s2lo, o), ohi = shfl_xor_u64(s2hi, o);
+            const uint64_t nlo = s2lo + olo;
+            s2hi = s2hi + ohi + (nlo < s2lo ? 1u : 0u);
+            s2lo = nlo;
+        }
+        if (lane == 0) {
+            red[wave][0] = sf;
+            red[wave][1] = s1;
+            red[wave][2] = s2hi;
+            red[wave][3] = s2lo;
+        }
     }
     __syncthreads();
     if (tid == 0) {
         const float m = s_m;
-        const uint64_t SF = hsp->SF, S1 = hsp->S1;
-        const unsigned __int128 S2 = (static_cast<unsigned __int128>(hsp->S2hi) << 64) | hsp->S2lo;
+        uint64_t SF = 0, S1 = 0, S2lo = 0, S2hi = 0;
+        for (int w = 0; w < NW; ++w) {
+            SF += red[w][0];
+            S1 += red[w][1];
+            const uint64_t nlo = S2lo + red[w][3];
+            S2hi += red[w][2] + (nlo < S2lo ? 1u : 0u);
+            S2lo = nlo;
+        }
+        hsp->SF = SF;
+        hsp->S1 = S1;
+        hsp->S2hi = S2hi;
+        hsp->S2lo = S2lo;
+        const unsigned __int128 S2 = (static_cast<unsigned __int128>(S2hi) << 64) | S2lo;
         const int NT = R.NT, nb = R.nb;
         int n, flags = 0;
         if (P.force_budget >= 0) {
@@ -1411,13 +1399,10 @@ static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) 
     int rc = 0;
     hipLaunchKernelGGL((k_base<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
     if ((rc = mk.mark(3))) return rc;
-    hipLaunchKernelGGL((k_stats<G>), dim3((p.ncg + kStatsChunks - 1) / kStatsChunks, p.B * p.Hkv),
-                       dim3(kChunkThreads), 0, st, p);
-    if ((rc = mk.mark(4))) return rc;
     hipLaunchKernelGGL(k_budget, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
-    if ((rc = mk.mark(5))) return rc;
+    if ((rc = mk.mark(4))) return rc;
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
-    return mk.mark(6);
+    return mk.mark(5);
 }
 
 template <int ROW, typename T, int G>
@@ -1477,9 +1462,9 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
     }
     if (rc) return rc;
     hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
-    if ((rc = mk.mark(7))) return rc;
+    if ((rc = mk.mark(6))) return rc;
     if (p.idx) hipLaunchKernelGGL(k_emit, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
-    if ((rc = mk.mark(8))) return rc;
+    if ((rc = mk.mark(7))) return rc;
     return static_cast<int>(hipGetLastError());
 }
 

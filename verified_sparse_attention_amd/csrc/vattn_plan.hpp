@@ -8,7 +8,7 @@ namespace vattn {
 constexpr int kPage = 16;
 constexpr int kPredThreads = 1024;   // predictor + chunk top-k
 constexpr int kSelectThreads = 1024; // per-head exact top-k and base threshold
-constexpr int kBudgetThreads = 256;  // per-head budget and final threshold
+constexpr int kBudgetThreads = 1024;  // per-head statistics, budget and final threshold
 constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
 constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
@@ -59,7 +59,7 @@ struct Plan {
     uint32_t* soff;  // [B*Hkv][ncp][kSampBins + 1] bin offsets of each chunk's middle tokens
     int32_t* slist;  // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
-    int32_t* btok;   // [B*Hkv][ncg][cg] base-pass member tokens, ascending
+    float* bsc;      // [B*Hkv][ncg][cg][G] pinned scores of the base-pass members, in list order
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
