@@ -228,25 +228,6 @@ __device__ __forceinline__ double u128_to_f64(unsigned __int128 x) {
 // ---------------------------------------------------------------------------
 // Loads of 8 consecutive elements (one lane's block) as fp32.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load8(const uint16_t* p, float (&f)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        f[2 * k] = __uint_as_float(ws[k] << 16);
-        f[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
-    }
-}
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
-// fp32 rounded to the nearest bf16 (ties to even), returned as fp32.
-__device__ __forceinline__ float bf16_round(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return __uint_as_float(u & 0xFFFF0000u);
-}
-
 struct Raw8 {  // one lane's 8 elements as loaded (bf16: one uint4; fp32: two float4)
     uint4 a, b;
 };
@@ -272,12 +253,6 @@ __device__ __forceinline__ void widen(const Raw8& r, float (&f)[8]) {
         f[4] = __uint_as_float(r.b.x); f[5] = __uint_as_float(r.b.y);
         f[6] = __uint_as_float(r.b.z); f[7] = __uint_as_float(r.b.w);
     }
-}
-__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
 // ---------------------------------------------------------------------------

@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
 // ===========================================================================
 constexpr float kRescale = 16.0f;  // reference-maximum headroom for the weights (e^16)
 constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group
-constexpr int kTilesPerBatch = 3;  // 16-token K tiles per batch and wave
+constexpr int kGatherUnrollK = 8;  // K rows per batch and lane group (VALU scoring)
 
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gather(Plan P) {
@@ -922,128 +922,52 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         }
         if (over) s_over = 1;
     }
-    if constexpr (sizeof(KVT) == 2) {
-        // bf16 keys: 16-token tiles on the matrix cores.  A = K rows (16 x D),
-        // B = the scaled query split into three bf16 terms q_hi + q_lo + q_lo2
-        // (residual ~2^-25 |q|), three columns per head, four heads per column
-        // block; bf16 x bf16 products are exact and accumulate in fp32.
-        constexpr int KB = D / 32, NCB = (G + 3) / 4;
-        const int col = lane & 15, kq = lane >> 4;
-        bf16x8 qb[NCB][KB];
+    {
+        // LPT lanes per K row (8 elements each), the G pinned-order sums
+        // spread over the row's lanes; each batch of rows is requested before
+        // any is scored
+        using SP = Spread<G, LPT>;
+        constexpr int NH = SP::NH, KU = kGatherUnrollK;
+        const bool fin = SP::finisher(j);
+        int hsel[NH];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            const int hh = cb * 4 + col / 3, term = col % 3;
-            const bool live = col < 12 && hh < G;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float part = 0.0f;
-                    if (live) {
-                        const float qsv = P.q[(bh0 + hh) * D + 32 * kb + 8 * kq + e] * P.scale32;
-                        const float hi = bf16_round(qsv);
-                        const float lo = bf16_round(qsv - hi);
-                        part = term == 0 ? hi : term == 1 ? lo : bf16_round((qsv - hi) - lo);
-                    }
-                    qb[cb][kb][e] = static_cast<__bf16>(part);
-                }
-        }
-        float mref[NCB];  // reference of the head this lane writes
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) mref[cb] = hv[min(cb * 4 + col / 3, G - 1)].m;
-        const int ntile = (nu + 15) / 16;
-        auto tile_row = [&](int x0) __attribute__((always_inline)) {
-            // row of this lane's token; lanes past the uncached part read a
-            // row that is already needed (their result is not used)
-            const int x = x0 + col;
-            return trow[x < nu ? x : x0];
-        };
-        struct KTile {
-            uint4 a[KB];
-        };
-        auto issue = [&](KTile& t, int x0) __attribute__((always_inline)) {
-            const KVT* rp = kbase + static_cast<size_t>(tile_row(x0)) * D + 8 * kq;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) t.a[kb] = *reinterpret_cast<const uint4*>(rp + 32 * kb);
-        };
-        auto score = [&](const KTile& t, int x0) __attribute__((always_inline)) {
-            // metadata of the four rows this lane may write, read before the products
-            uint32_t mr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mr[r] = tmeta[min(x0 + 4 * kq + r, nu - 1)];
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.a[kb]), qb[cb][kb],
-                                                                 acc, 0, 0, 0);
-                const int hh = cb * 4 + col / 3;
-                const bool writer = col < 12 && col % 3 == 0 && hh < G;
-                bool over = false;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float sv = acc[r] + dpp<0x101>(acc[r]) + dpp<0x102>(acc[r]);  // row_shl:1, :2
-                    const int x = x0 + 4 * kq + r;
-                    const bool wr = writer && x < nu;
-                    const bool mem = (mr[r] >> hh) & 1u;
-                    if (wr) {
-                        over |= mem && sv > mref[cb] + kRescale;
-                        sp[hh][x] = mem ? sv : -__builtin_inff();
-                    }
-                }
-                if (over) s_over = 1;
-            }
-        };
-        // each wave scores kTilesPerBatch tiles per iteration, all of whose
-        // rows are requested before any is scored (tiles past the end reread
-        // the last tile; their results are not stored)
-        constexpr int NK = kTilesPerBatch;
-        for (int t0w = wave * NK; t0w < ntile; t0w += nwaves * NK) {
-            KTile kt[NK];
-#pragma unroll
-            for (int u = 0; u < NK; ++u) issue(kt[u], 16 * min(t0w + u, ntile - 1));
-#pragma unroll
-            for (int u = 0; u < NK; ++u)
-                if (t0w + u < ntile) score(kt[u], 16 * (t0w + u));
-        }
-    } else {
+        for (int e = 0; e < NH; ++e) hsel[e] = SP::head(j, e);
         float qreg[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
-        for (int base = wave * TPW * kUnroll; base < nu; base += nwaves * TPW * kUnroll) {
-            Raw8 kr[kUnroll];
-            uint32_t mk[kUnroll];
-            int xs[kUnroll];
+        bool over = false;
+        for (int base = wave * TPW * KU; base < nu; base += nwaves * TPW * KU) {
+            Raw8 kr[KU];
+            uint32_t mk[KU];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < KU; ++u) {
                 const int x = base + u * TPW + slot;
-                xs[u] = x < nu ? x : -1;
                 mk[u] = x < nu ? tmeta[x] : 0u;
                 load_raw(kbase + static_cast<size_t>(trow[x < nu ? x : 0]) * D + 8 * j, kr[u]);
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < KU; ++u) {
                 float kf[8];
                 widen<KVT>(kr[u], kf);
-                float sv[G];
+                float part[G], sv[NH];
 #pragma unroll
-                for (int h = 0; h < G; ++h) sv[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-                if (j == LPT - 1 && xs[u] >= 0) {
-                    const int x = xs[u];
-                    bool over = false;
+                for (int h = 0; h < G; ++h) part[h] = chain8(qreg[h], kf);
+                spread_across_lanes<G, LPT>(part, sv, j);
+                const int x = base + u * TPW + slot;
+                if (fin && x < nu) {
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
+                    for (int e = 0; e < NH; ++e) {
+                        const int h = hsel[e];
                         const bool mem = (mk[u] >> h) & 1u;
-                        over |= mem && sv[h] > hv[h].m + kRescale;
-                        sp[h][x] = mem ? sv[h] : -__builtin_inff();
+                        over |= mem && sv[e] > hv[h].m + kRescale;
+                        sp[h][x] = mem ? sv[e] : -__builtin_inff();
                     }
-                    if (over) s_over = 1;
                 }
             }
         }
+        if (over) s_over = 1;
     }
     __syncthreads();
     // weights against each head's base-pass maximum (the pinned maximum over
