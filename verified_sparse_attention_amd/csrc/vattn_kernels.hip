@@ -450,20 +450,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     }
 }
 
-// The G scores of one token as one vector store (the score rows are G floats,
-// G a power of two, so a row never straddles a 16-byte boundary).
-template <int G>
-__device__ __forceinline__ void store_scores(float* p, const float (&s)[G]) {
-    if constexpr (G >= 4) {
-#pragma unroll
-        for (int k = 0; k < G; k += 4) *reinterpret_cast<float4*>(p + k) = make_float4(s[k], s[k + 1], s[k + 2], s[k + 3]);
-    } else if constexpr (G == 2) {
-        *reinterpret_cast<float2*>(p) = make_float2(s[0], s[1]);
-    } else {
-        p[0] = s[0];
-    }
-}
-
 // ===========================================================================
 // base: pinned exact scores of the union of fixed sets and base samples
 // ===========================================================================
@@ -549,17 +535,25 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     }
     __syncthreads();
 
-    // pinned scores for all G heads of each listed token
+    // pinned scores for all G heads of each listed token: the G sums of a row
+    // are spread over its lanes, each finished (max, two stores) by one lane
     constexpr int LPT = D / 8, TPW = 64 / LPT;
+    using SP = Spread<G, LPT>;
+    constexpr int NH = SP::NH;
     const int j = lane % LPT, slot = lane / LPT;
+    const bool fin = SP::finisher(j);
+    int hsel[NH];
+    float lmax[NH];
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+        hsel[e] = SP::head(j, e);
+        lmax[e] = -__builtin_inff();
+    }
     float qreg[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
-    float lmax[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) lmax[h] = -__builtin_inff();
     const KVT* kbase = static_cast<const KVT*>(P.k);
     float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
     float* lsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
@@ -583,25 +577,27 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
         for (int u = 0; u < kBU; ++u) {
             float kf[8];
             widen<KVT>(kr[u], kf);
-            float s[G];
+            float part[G], sv[NH];
 #pragma unroll
-            for (int h = 0; h < G; ++h) s[h] = tree_across_lanes<LPT>(chain8(qreg[h], kf));
-            if (j == LPT - 1) {  // the lane holding the pinned sums
+            for (int h = 0; h < G; ++h) part[h] = chain8(qreg[h], kf);
+            spread_across_lanes<G, LPT>(part, sv, j);
+            if (fin && mk[u]) {
 #pragma unroll
-                for (int h = 0; h < G; ++h)
-                    if ((mk[u] >> h) & 1u) lmax[h] = fmaxf(lmax[h], s[h]);
-                if (mk[u]) {
-                    store_scores<G>(scrow + static_cast<size_t>(tk[u]) * G, s);  // by token, for the gather
-                    store_scores<G>(lsc + static_cast<size_t>(xl[u]) * G, s);    // in list order, for the budget
+                for (int e = 0; e < NH; ++e) {
+                    if ((mk[u] >> hsel[e]) & 1u) lmax[e] = fmaxf(lmax[e], sv[e]);
+                    scrow[static_cast<size_t>(tk[u]) * G + hsel[e]] = sv[e];  // by token, for the gather
+                    lsc[static_cast<size_t>(xl[u]) * G + hsel[e]] = sv[e];    // in list order, for the budget
                 }
             }
         }
     }
+    // per head maximum: lanes with the same j hold the same heads
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float v = lmax[h];
-        for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-        if (lane == 0) wmax[wave][h] = v;
+    for (int e = 0; e < NH; ++e)
+        for (int o = LPT; o < 64; o <<= 1) lmax[e] = fmaxf(lmax[e], __shfl_xor(lmax[e], o, 64));
+    if (lane < LPT && fin) {
+#pragma unroll
+        for (int e = 0; e < NH; ++e) wmax[wave][hsel[e]] = lmax[e];
     }
     __syncthreads();
     if (tid < G) {
