@@ -71,7 +71,7 @@ size_t predict_lds_bytes(int G, int d, int row, int cp) {
         case 4: ts = sizeof(TopkShared<4>); break;
         default: ts = sizeof(TopkShared<8>); break;
     }
-    return align16(ts) + sizeof(uint32_t) * (kSampBins + kPredThreads / 64) + sizeof(int32_t) * (cp / kPage + 2) +
+    return align16(ts) + sizeof(uint32_t) * (kSampBins + kPredThreads / 64) + align16(sizeof(int32_t) * (cp / kPage + 2)) +
            sizeof(float) * (static_cast<size_t>(G) * d + static_cast<size_t>(G) * row) +
            sizeof(uint32_t) * static_cast<size_t>(G) * (cp + kKeyPad);
 }
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     uint32_t* wsum = shist + kSampBins;  // scan scratch, one word per wave
     off += sizeof(uint32_t) * (kSampBins + kPredThreads / 64);
     int32_t* pages = reinterpret_cast<int32_t*>(smem + off);  // the chunk's page ids
-    off += sizeof(int32_t) * (P.cp / kPage + 2);
+    off += align16(sizeof(int32_t) * (P.cp / kPage + 2));      // keys below start 16-byte aligned
     float* qs = reinterpret_cast<float*>(smem + off);  // [G][d]
     float* qv = qs + G * P.d;                           // [G][ROW]
     uint32_t* keys = reinterpret_cast<uint32_t*>(qv + G * ROW);  // [G][ks]
@@ -308,10 +308,23 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
         const int ncp = P.ncp, kcap = P.kcap;
         uint64_t* __restrict__ cand = P.cand;
+        // each visit reads 4 consecutive keys of every head with one 16-byte
+        // LDS load per head (offsets from the 16-byte aligned chunk start)
+        const int o0 = (t0 - cbase) & ~3, o1 = t1 - cbase;
         block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
-            for (int t = t0 + tid; t < t1; t += nthr)
+            for (int o = o0 + 4 * tid; o < o1; o += 4 * nthr) {
+                uint4 kk[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) f(h, keys[h * ks + (t - cbase)], static_cast<uint32_t>(t));
+                for (int h = 0; h < G; ++h) kk[h] = *reinterpret_cast<const uint4*>(keys + h * ks + o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = cbase + o + e;
+                    if (t >= t0 && t < t1) {
+#pragma unroll
+                        for (int h = 0; h < G; ++h) f(h, word_of(kk[h], e), static_cast<uint32_t>(t));
+                    }
+                }
+            }
         }, [&](int h, uint64_t key) __attribute__((always_inline)) {
             const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
             if (pos < static_cast<uint32_t>(kp)) cand[((bh0 + h) * ncp + c) * kcap + pos] = key;
