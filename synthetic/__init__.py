@@ -118,7 +118,7 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
          topk_ppm=25000, base_ppm=50000, force_budget=-1, eps=0.05, delta=0.05, seed=0,
          data_seed=1000, shuffle=False, q_std=1.0, k_std=1.0, planted=8, plant_scale=4.0,
          outlier_channels=4, outlier_scale=8.0, lowrank_dim=24, lowrank_noise=0.1,
-         peaked_frac=0.5, max_seq_len=None) -> Workload:
+         peaked_frac=0.5, hidden_logit=40.0, max_seq_len=None) -> Workload:
     """Draw one workload.
 
     recipe:
@@ -131,6 +131,15 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
       lowrank   K = Z U^T + N(0, lowrank_noise^2), U a d x lowrank_dim orthonormal
                 basis per KV head, Z ~ N(0, I)
       mixed     per (b, KV head) a seeded coin: `planted` or `flat` (k_std=q_std=0.3)
+      hidden    as normal, plus keys the low-rank predictor cannot see: for every
+                query head h one key c * u / |u| with u = q_h - P P^T q_h (the
+                part of q_h outside the predictor's span), so its predicted score
+                is ~0 while its scaled score q_h . K / sqrt(d) is `hidden_logit`;
+                and, when G >= 2, one key that adds to head 0's hidden direction
+                a component along P P^T q_1, which puts it among head 1's
+                predicted top scores (a base-pass member of the group) while it
+                stays outside head 0's fixed set.  Positions are uniform in the
+                middle half of each sequence.  LOWRANK predictor only.
     """
     gen = torch.Generator().manual_seed(int(data_seed))
     seq_lens = [int(x) for x in seq_lens]
@@ -147,12 +156,16 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
     if recipe == "outlier":
         outlier_idx = torch.stack([torch.randperm(d, generator=gen)[:outlier_channels]
                                    for _ in range(Hkv)])
+    hidden_proj = None
+    if recipe == "hidden":
+        assert predictor == 1
+        hidden_proj = orthonormal(d, rank, gen)
     U = None
     if recipe == "lowrank":
         U = torch.stack([orthonormal(d, lowrank_dim, gen) for _ in range(Hkv)])
     for b, L in enumerate(seq_lens):
         v = torch.randn(Hkv, L, d, generator=gen)
-        if recipe in ("normal", "planted"):
+        if recipe in ("normal", "planted", "hidden"):
             k = torch.randn(Hkv, L, d, generator=gen) * k_std
         elif recipe == "flat":
             k = torch.randn(Hkv, L, d, generator=gen) * k_std
@@ -190,13 +203,30 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
                 qh = q[b, h] / q[b, h].norm()
                 k[g, pos[j]] = plant_scale * qh + torch.randn(d, generator=gen)
                 plants.append((b, h, int(pos[j])))
+        if recipe == "hidden" and L >= 8:
+            Pm = hidden_proj.double()
+            for g in range(Hkv):
+                pos = (L // 4 + torch.randperm(max(L // 2, 1), generator=gen)[:G + 1]).tolist()
+                for hh in range(G):
+                    qh = q[b, g * G + hh].double()
+                    u = qh - Pm @ (Pm.T @ qh)
+                    c = hidden_logit * math.sqrt(d) / float(u.norm())
+                    k[g, pos[hh]] = (c * u / u.norm()).float()
+                    plants.append((b, g * G + hh, int(pos[hh])))
+                if G >= 2:
+                    q0, q1 = q[b, g * G].double(), q[b, g * G + 1].double()
+                    u = q0 - Pm @ (Pm.T @ q0)
+                    w = Pm @ (Pm.T @ q1)
+                    kk = hidden_logit * math.sqrt(d) / float(u.norm()) * u / u.norm() + 40.0 * w / w.norm()
+                    k[g, pos[G]] = kk.float()
+                    plants.append((b, g * G, int(pos[G])))
         rows_k.append(k)
         rows_v.append(v)
 
     dt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
     k_cache = _to_paged(rows_k, bt, seq_lens, num_blocks, dt)
     v_cache = _to_paged(rows_v, bt, seq_lens, num_blocks, dt)
-    proj = orthonormal(d, rank, gen) if predictor == 1 else None
+    proj = hidden_proj if hidden_proj is not None else (orthonormal(d, rank, gen) if predictor == 1 else None)
     cfg = dict(sinks=sinks, window=window, topk_abs=topk_abs, topk_ppm=topk_ppm,
                base_ppm=base_ppm, force_budget=force_budget, predictor=predictor,
                rank=rank if predictor == 1 else 0, eps=eps, delta=delta, seed=seed)

@@ -142,6 +142,14 @@ EDGE_CASES = {
     "base_ppm_max": lambda: synthetic.make(
         B=1, Hq=2, Hkv=2, d=64, seq_lens=(900,), kv_dtype="f32", predictor=0, sinks=4, window=4,
         topk_abs=10, base_ppm=1000000),
+    # keys outside the predictor's span with scaled scores of 40 against ~4 for
+    # the fixed set and a 2-token base sample: every chunk holding one takes
+    # its weights against its own maximum (the rescale fallback), through the
+    # K rows and, for the key in head 1's top-k, through the cached scores
+    "hidden_rescale": lambda: synthetic.make(
+        name="hidden_rescale", B=2, Hq=4, Hkv=2, d=128, seq_lens=(3000, 2100), kv_dtype="bf16",
+        recipe="hidden", predictor=1, rank=32, sinks=4, window=4, topk_abs=4, base_ppm=1,
+        force_budget=10 ** 9, data_seed=31),
     "page_unaligned_regions": lambda: synthetic.make(
         B=2, Hq=8, Hkv=1, d=128, seq_lens=(1037, 4099), kv_dtype="bf16", recipe="planted",
         predictor=1, rank=32, sinks=5, window=27, topk_abs=33, shuffle=True),
