@@ -85,7 +85,12 @@ typedef struct {
     uint64_t seed;        /* Philox4x32-10 key; callers vary it per step and layer     */
 } vattn_cfg;
 
-/* Inputs.  All pointers are device pointers except where noted. */
+/* Inputs.  All pointers are device pointers except where noted.  k_cache and
+ * v_cache may instead point into pinned host memory that is mapped for the
+ * device (hipHostMalloc): the kernels then read only the rows they use over the
+ * host link (edgentiq vAttention post, section "Performance and Efficiency":
+ * decode with the KV cache hosted on the CPU), while k_lowrank and the workspace
+ * stay in device memory. */
 typedef struct {
     const float* q;             /* [B, Hq, d] fp32                                   */
     const void* k_cache;        /* [num_blocks, Hkv, 16, d] kv_dtype                  */

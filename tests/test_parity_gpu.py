@@ -161,6 +161,22 @@ def test_parity_edge_cases(name):
     run_both(EDGE_CASES[name](), seeds=(0, 5), tag=name)
 
 
+@pytest.mark.parametrize("name", ["gqa4_bf16_ragged", "gqa2_d64_f32_r16", "exact_bf16_d128_g2"])
+def test_parity_host_kv(name):
+    """K and V in pinned host memory, read by the kernels over the host link
+    (the low-rank keys stay in HBM): the same results as the oracle."""
+    w = SMALL_CASES[name]()
+    GpuCase, log = _gpu()
+    log("[parity] host-resident KV %s" % name)
+    case = GpuCase(w, kv_host=True)
+    assert not case.k.is_cuda and case.k.is_pinned() and case.v.is_pinned()
+    arrays = w.oracle_arrays()
+    for s in (0, 4):
+        g = case.run(s)
+        o = oracle.decode(**arrays, cfg=dict(w.cfg, seed=s), want_idx=True, nthreads=8)
+        compare(w, g, o, tag="%s host kv seed=%d" % (name, s))
+
+
 def test_full_budget_matches_dense():
     w = EDGE_CASES["forced_full"]()
     GpuCase, log = _gpu()
