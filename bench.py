@@ -38,6 +38,8 @@ def parse():
                     help="few steps, no CPU baseline or rate (for rocprofv3 runs)")
     ap.add_argument("--rate-seeds", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-kv", action="store_true",
+                    help="also time the step with K/V in pinned host memory (adds a host_kv object)")
     return ap.parse_args()
 
 
@@ -251,7 +253,7 @@ def main():
                                 "note": "one new token per sequence: K, V and its low-rank key row"}
         log("append %.2f us per call" % app_us)
 
-    if not args.profile:
+    if args.host_kv and not args.profile:
         # ---- host-resident K/V: the caches in pinned, device-mapped host memory,
         # read by the kernels over the host link (the low-rank keys and the
         # workspace stay in HBM).  Compared with moving the whole K/V over the
@@ -301,6 +303,7 @@ def main():
             % (host_ms, link_gbs, dense_ms))
         del hdec, kh, vh, dst
 
+    if not args.profile:
         # ---- (eps, delta): denominator relative error vs a dense fp32 reference
         with torch.no_grad():
             lse_dense = torch.empty(w.B, w.Hq, dtype=torch.float64, device=dev)
