@@ -89,6 +89,11 @@ SMALL_CASES = {
         name="flat_crowded_bucket", B=1, Hq=8, Hkv=2, d=128, seq_lens=(20000,), kv_dtype="bf16",
         recipe="flat", q_std=0.3, k_std=0.3, predictor=1, rank=32, sinks=16, window=16,
         topk_ppm=25000, eps=0.02, data_seed=18),
+    # one sequence, few heads, 20 predictor chunks: the chunk candidates are
+    # pre-merged in 8 uneven parts before the per-head select
+    "premerge_parts": lambda: synthetic.make(
+        name="premerge_parts", B=1, Hq=4, Hkv=1, d=128, seq_lens=(40000,), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=32, sinks=64, window=64, topk_ppm=25000, data_seed=19),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
@@ -150,6 +155,10 @@ EDGE_CASES = {
         name="hidden_rescale", B=2, Hq=4, Hkv=2, d=128, seq_lens=(3000, 2100), kv_dtype="bf16",
         recipe="hidden", predictor=1, rank=32, sinks=4, window=4, topk_abs=4, base_ppm=1,
         force_budget=10 ** 9, data_seed=31),
+    # pre-merged parts with fewer candidates than k (kept whole) and more
+    "premerge_keep_all": lambda: synthetic.make(
+        name="premerge_keep_all", B=1, Hq=2, Hkv=1, d=64, seq_lens=(36000,), kv_dtype="f32",
+        predictor=0, sinks=8, window=8, topk_abs=5000, data_seed=20),
     "page_unaligned_regions": lambda: synthetic.make(
         B=2, Hq=8, Hkv=1, d=128, seq_lens=(1037, 4099), kv_dtype="bf16", recipe="planted",
         predictor=1, rank=32, sinks=5, window=27, topk_abs=33, shuffle=True),

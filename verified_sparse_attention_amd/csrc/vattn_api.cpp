@@ -41,7 +41,7 @@ double normal_isf(double p) {
 }
 
 struct Shape {
-    int G, cp, ncp, kcap, cg, ncg, words;
+    int G, cp, ncp, kcap, cg, ncg, words, nparts, kcap2;
 };
 
 vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
@@ -92,12 +92,24 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
         sh->cg = vattn::kGatherChunk;
         sh->ncg = (in->max_seq_len + sh->cg - 1) / sh->cg;
         sh->words = (in->max_seq_len + 31) / 32;
+        // few heads and many predictor chunks: pre-merge the chunk candidates
+        // in parts so the per-head select is not left with every chunk
+        sh->nparts = (static_cast<long long>(in->B) * in->Hq < vattn::kPremergeMaxHeads &&
+                      sh->ncp >= vattn::kPremergeMinChunks) ? vattn::kPremergeParts : 0;
+        // a part keeps min(k, its chunks' candidates): at most k, and at most
+        // cp tokens from each of its chunks (the largest part has ceil(ncp / parts))
+        if (sh->nparts) {
+            const long long per = static_cast<long long>(sh->cp) * ((sh->ncp + sh->nparts - 1) / sh->nparts);
+            sh->kcap2 = static_cast<int>(kmax < per ? (kmax < 1 ? 1 : kmax) : per);
+        } else {
+            sh->kcap2 = 0;
+        }
     }
     return VATTN_OK;
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, total;
+    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, cand2, crange2, pcount, hist2, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -133,6 +145,14 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * (static_cast<size_t>(s.ncg) * s.cg) * sizeof(uint32_t));
     L.crange = off;
     off += align_up(BHq * s.ncp * 2 * sizeof(uint32_t));
+    L.cand2 = off;
+    off += align_up(BHq * s.nparts * static_cast<size_t>(s.kcap2) * sizeof(uint64_t));
+    L.crange2 = off;
+    off += align_up(BHq * s.nparts * 2 * sizeof(uint32_t));
+    L.pcount = off;
+    off += align_up(BHq * s.nparts * sizeof(int32_t));
+    L.hist2 = off;
+    off += align_up(BHkv * s.nparts * vattn::kSampBins * sizeof(uint32_t));
     L.total = off;
     return L;
 }
@@ -221,6 +241,12 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.uw = reinterpret_cast<uint32_t*>(ws + L.uw);
     p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
+    p.nparts = s.nparts;
+    p.kcap2 = s.kcap2;
+    p.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);
+    p.crange2 = reinterpret_cast<uint32_t*>(ws + L.crange2);
+    p.pcount = reinterpret_cast<int32_t*>(ws + L.pcount);
+    p.hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
     p.out = out->out;
     p.lse = out->lse;
     p.idx = out->idx;

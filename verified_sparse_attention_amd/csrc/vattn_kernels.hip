@@ -338,14 +338,89 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     }
 }
 
-// ===========================================================================
-// select: exact top-k, fixed-set bitmap, tail histograms, base threshold
-// ===========================================================================
+// Candidates a predictor chunk emits for one head: min(k, its middle tokens).
 __device__ __forceinline__ int chunk_candidates(int cp, const Regions R, int c) {
     const int a = max(c * cp, R.lo), e = min((c + 1) * cp, R.hi);
     return a < e ? min(R.k, e - a) : 0;
 }
 
+// ===========================================================================
+// pre-merge (few heads, many predictor chunks): block (head, part) merges the
+// candidates of its share of the chunks into that share's exact top-min(k, n)
+// (the global top-k is within the union of the parts' top-k), and the group's
+// first head sums the share's sample-word histograms; the select then merges
+// kPremergeParts parts instead of every chunk.
+// ===========================================================================
+__global__ __launch_bounds__(kSelectThreads) void k_premerge(Plan P) {
+    __shared__ TopkShared<1> TS;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int bh = blockIdx.x, s = blockIdx.y, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
+    const int bg = b * P.Hkv + g;
+    const int L = P.seq_lens[b];
+    const Regions R = regions(P, L);
+    const int cp = P.cp, ncp = P.ncp, kcap = P.kcap, np = P.nparts;
+    const int c0 = s * ncp / np, c1 = (s + 1) * ncp / np;  // the part's chunks
+    if (h % P.G == 0) {  // the group's tail histogram over the part's chunks
+        const uint32_t* soffg = P.soff + static_cast<size_t>(bg) * ncp * (kSampBins + 1);
+        uint32_t* h2 = P.hist2 + (static_cast<size_t>(bg) * np + s) * kSampBins;
+        for (int x = tid; x < kSampBins; x += nthr) {
+            uint32_t sum = 0;
+            for (int c = c0; c < c1; ++c) {
+                if (max(c * cp, R.lo) >= min((c + 1) * cp, R.hi)) continue;
+                const uint32_t* off = soffg + static_cast<size_t>(c) * (kSampBins + 1) + x;
+                sum += off[1] - off[0];
+            }
+            h2[x] = sum;
+        }
+    }
+    uint32_t tot = 0, lo = 0xFFFFFFFFu, hi = 0;
+    for (int c = c0; c < c1; ++c) {
+        const int nc = chunk_candidates(cp, R, c);
+        if (!nc) continue;
+        const uint32_t* cr = P.crange + (static_cast<size_t>(bh) * ncp + c) * 2;
+        tot += static_cast<uint32_t>(nc);
+        lo = min(lo, cr[0]);
+        hi = max(hi, cr[1]);
+    }
+    const uint32_t keep = min(static_cast<uint32_t>(R.k), tot);
+    if (tid == 0) TS.aux[0] = 0;
+    const uint64_t* __restrict__ cand = P.cand + (static_cast<size_t>(bh) * ncp + c0) * kcap;
+    uint64_t* __restrict__ out = P.cand2 + (static_cast<size_t>(bh) * np + s) * P.kcap2;  // keep <= kcap2
+    const int slots = (c1 - c0) * kcap;
+    const uint32_t want[1] = {keep}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
+    constexpr int kBatch = 8;
+    block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
+        for (int x0 = tid; x0 < slots; x0 += kBatch * nthr) {
+            uint64_t kk[kBatch];
+            bool ok[kBatch];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) {
+                const int x = x0 + t * nthr;
+                const int c = x / kcap, p = x - c * kcap;
+                ok[t] = x < slots && p < chunk_candidates(cp, R, c0 + c);
+                kk[t] = ok[t] ? cand[x] : 0ull;
+            }
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t)
+                if (ok[t]) f(0, static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
+        }
+    }, [&](int, uint64_t key) __attribute__((always_inline)) {
+        const uint32_t pos = atomicAdd(&TS.aux[0], 1u);
+        if (pos < keep) out[pos] = key;
+    });
+    if (tid == 0) {
+        P.pcount[static_cast<size_t>(bh) * np + s] = static_cast<int32_t>(keep);
+        uint32_t* cr = P.crange2 + (static_cast<size_t>(bh) * np + s) * 2;
+        cr[0] = TS.thr[0] ? static_cast<uint32_t>(TS.thr[0] >> 32) : lo;
+        cr[1] = hi;
+    }
+}
+
+// ===========================================================================
+// select: exact top-k, fixed-set bitmap, tail histograms, base threshold
+// ===========================================================================
+
+template <bool PM>  // PM: the candidates come pre-merged in P.nparts parts
 __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     __shared__ TopkShared<1> TS;
     __shared__ HeadSamp SS;
@@ -357,7 +432,19 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     const uint32_t* uwg = group_words(P, bg);
     // lambdas below capture these locals, never the kernel argument itself
     const int cp = P.cp, ncp = P.ncp, kcap = P.kcap;
-    const uint64_t* __restrict__ cand = P.cand + static_cast<size_t>(bh) * ncp * kcap;
+    // candidate parts: the predictor chunks, or (few heads, many chunks) the
+    // pre-merged groups of chunks with explicit counts and histograms
+    const int np = PM ? P.nparts : 0, nparts = PM ? np : ncp;
+    const int pk = PM ? P.kcap2 : kcap;  // key slots per part
+    const uint64_t* __restrict__ cand = PM ? P.cand2 + static_cast<size_t>(bh) * np * pk
+                                           : P.cand + static_cast<size_t>(bh) * ncp * kcap;
+    const uint32_t* __restrict__ crng = PM ? P.crange2 + static_cast<size_t>(bh) * np * 2
+                                           : P.crange + static_cast<size_t>(bh) * ncp * 2;
+    const int32_t* __restrict__ pcnt = PM ? P.pcount + static_cast<size_t>(bh) * np : nullptr;
+    auto part_count = [&](int c) __attribute__((always_inline)) {
+        if constexpr (PM) return static_cast<int>(pcnt[c]);
+        else return chunk_candidates(cp, R, c);
+    };
     uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
     const uint32_t* soffg = P.soff + static_cast<size_t>(bg) * ncp * (kSampBins + 1);
     if (tid == 0 && P.gcounts && h % P.G == 0) {
@@ -378,7 +465,15 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
         bits[w] = word;
     }
     constexpr int kCB = 4;  // chunks whose loads are issued together
-    for (int x = tid; x < kSampBins; x += nthr) {
+    if constexpr (PM) {
+        const uint32_t* h2 = P.hist2 + static_cast<size_t>(bg) * np * kSampBins;
+        for (int x = tid; x < kSampBins; x += nthr) {
+            uint32_t sum = 0;
+            for (int c = 0; c < np; ++c) sum += h2[static_cast<size_t>(c) * kSampBins + x];
+            SS.hist[x] = sum;
+        }
+    }
+    for (int x = tid; !PM && x < kSampBins; x += nthr) {
         uint32_t sum = 0;
         for (int c0 = 0; c0 < ncp; c0 += kCB) {
             uint32_t a[kCB], e[kCB];
@@ -400,14 +495,14 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     //    out of the tail histogram (block_topk starts with a barrier)
     if (R.k > 0) {
         uint32_t tot = 0, lo = 0xFFFFFFFFu, hi = 0;
-        for (int c0 = 0; c0 < ncp; c0 += kCB) {
+        for (int c0 = 0; c0 < nparts; c0 += kCB) {
             uint32_t clo[kCB], chi[kCB];
 #pragma unroll
             for (int t = 0; t < kCB; ++t) {
                 const int c = c0 + t;
-                const int nc = c < ncp ? chunk_candidates(cp, R, c) : 0;
+                const int nc = c < nparts ? part_count(c) : 0;
                 tot += static_cast<uint32_t>(nc);
-                const uint32_t* cr = P.crange + (static_cast<size_t>(bh) * ncp + (nc ? c : 0)) * 2;
+                const uint32_t* cr = crng + static_cast<size_t>(nc ? c : 0) * 2;
                 clo[t] = nc ? cr[0] : 0xFFFFFFFFu;
                 chi[t] = nc ? cr[1] : 0u;
             }
@@ -418,7 +513,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
             }
         }
         const uint32_t want[1] = {static_cast<uint32_t>(R.k)}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
-        const int slots = ncp * kcap;
+        const int slots = nparts * pk;
         constexpr int kBatch = 8;  // candidate keys loaded before any is visited
         block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
             for (int x0 = tid; x0 < slots; x0 += kBatch * nthr) {
@@ -427,8 +522,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
 #pragma unroll
                 for (int t = 0; t < kBatch; ++t) {
                     const int x = x0 + t * nthr;
-                    const int c = x / kcap, p = x - c * kcap;
-                    ok[t] = x < slots && p < chunk_candidates(cp, R, c);
+                    const int c = x / pk, p = x - c * pk;
+                    ok[t] = x < slots && p < part_count(c);
                     kk[t] = ok[t] ? cand[x] : 0ull;
                 }
 #pragma unroll
@@ -1371,7 +1466,12 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
     if (rc) return rc;
     if ((rc = mk.mark(1))) return rc;
     // 2. exact top-k, bitmap, base threshold
-    hipLaunchKernelGGL(k_select, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+    if (p.nparts > 0) {
+        hipLaunchKernelGGL(k_premerge, dim3(p.B * p.Hq, p.nparts), dim3(kSelectThreads), 0, st, p);
+        hipLaunchKernelGGL(k_select<true>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(k_select<false>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+    }
     if ((rc = mk.mark(2))) return rc;
     // 3-5. base scores, budget, gather
     if (p.d == 128)

@@ -16,6 +16,9 @@ constexpr int kSampBits = 11;        // sampler histogram: top bits of the Philo
 constexpr int kSampBins = 1 << kSampBits;
 constexpr int kTopBuckets = 256;     // value-range buckets of the top-k select
 constexpr int kListCap = 128;        // boundary-bucket list capacity per head
+constexpr int kPremergeParts = 4;    // candidate parts after the pre-merge
+constexpr int kPremergeMaxHeads = 128;  // pre-merge when B*Hq is below this ...
+constexpr int kPremergeMinChunks = 16;  // ... and there are at least this many predictor chunks
 constexpr int kGatherChunk = 4 * kChunkThreads;  // tokens per base/gather block
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 #define VATTN_MAX_SEQ_TOKENS (1 << 20)
@@ -64,6 +67,12 @@ struct Plan {
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
     uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
+    // pre-merged candidate parts (nparts > 0 only: few heads, many chunks)
+    int nparts, kcap2; // parts; key slots per part = min(k bound, cp * chunks in the largest part)
+    uint64_t* cand2;   // [B*Hq][nparts][kcap2] each part's exact top-min(k, n) keys
+    uint32_t* crange2; // [B*Hq][nparts][2] their order-key brackets
+    int32_t* pcount;   // [B*Hq][nparts] keys per part
+    uint32_t* hist2;   // [B*Hkv][nparts][kSampBins] tail sample-word histogram per part
     // outputs
     float* out;
     float* lse;
