@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             for (int u = 0; u < PU; ++u) {
                 const uint32_t tl = min(static_cast<uint32_t>(sb + u * TPW + slot), tlast);
                 const uint32_t pg = static_cast<uint32_t>(pages[tl / kPage]);
-                load_raw(gsrc + static_cast<uint64_t>(pg) * pstride + (tl % kPage) * ROW, kr[u]);
+                load_raw_nt(gsrc + static_cast<uint64_t>(pg) * pstride + (tl % kPage) * ROW, kr[u]);
             }
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
             xl[u] = xs;
             tk[u] = tok[xs];
             mk[u] = act ? tmeta[xs] : 0u;
-            load_raw(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kr[u]);
+            load_raw_nt(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kr[u]);
         }
 #pragma unroll
         for (int u = 0; u < kBU; ++u) {
@@ -1049,7 +1049,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
             for (int u = 0; u < KU; ++u) {
                 const int x = base + u * TPW + slot;
                 mk[u] = x < nu ? tmeta[x] : 0u;
-                load_raw(kbase + static_cast<size_t>(trow[x < nu ? x : 0]) * D + 8 * j, kr[u]);
+                load_raw_nt(kbase + static_cast<size_t>(trow[x < nu ? x : 0]) * D + 8 * j, kr[u]);
             }
 #pragma unroll
             for (int u = 0; u < KU; ++u) {
@@ -1151,7 +1151,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
             for (int u = 0; u < kGatherUnrollV; ++u) {
                 const int x = min(b0 + u * TPW + slot, n - 1);
-                load_raw(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
+                load_raw_nt(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
             }
         };
         auto accumulate = [&](const VBatch& bt) __attribute__((always_inline)) {
