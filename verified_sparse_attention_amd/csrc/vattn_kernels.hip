@@ -908,6 +908,45 @@ constexpr float kRescale = 16.0f;  // reference-maximum headroom for the weights
 constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group
 constexpr int kGatherUnrollK = 8;  // K rows per batch and lane group (VALU scoring)
 
+// Group of a gather block.  Block row y takes the group of rank y when the
+// groups are ordered by expected member density (n_fixed + n) / L of their
+// densest head, descending, ties to the lower group: the groups with the most
+// rows per chunk are dispatched first, so the blocks still running at the end
+// of the kernel are the light ones and the tail, where too few blocks are left
+// to keep HBM busy, stays short.  Every block derives the same order from the
+// budgets (written by the previous kernel).  With more heads than threads the
+// rows keep their own groups.
+template <int G>
+__device__ __forceinline__ int gather_group(const Plan& P, int tid) {
+    __shared__ float gw[kChunkThreads];
+    __shared__ int s_bg;
+    const int nh = P.B * P.Hq, ngr = P.B * P.Hkv, y = blockIdx.y;
+    if (nh > kChunkThreads) return y;  // uniform over the grid
+    if (tid == 0) s_bg = y;
+    float w = 0.0f;
+    if (tid < nh) {
+        const HeadState& s = P.hs[tid];
+        const int L = s.L;
+        w = L > 0 ? static_cast<float>(s.n_fixed + s.n) / static_cast<float>(L) : 0.0f;
+    }
+    // a group's heads are G consecutive threads of one wave
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) w = fmaxf(w, __shfl_xor(w, o, 64));
+    if (tid < nh && tid % G == 0) gw[tid / G] = w;
+    __syncthreads();
+    if (tid < ngr) {  // thread tid ranks group tid
+        const float mine = gw[tid];
+        int rank = 0;
+        for (int u = 0; u < ngr; ++u) {
+            const float o = gw[u];
+            rank += (o > mine || (o == mine && u < tid)) ? 1 : 0;
+        }
+        if (rank == y) s_bg = tid;
+    }
+    __syncthreads();
+    return s_bg;
+}
+
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gather(Plan P) {
     constexpr int NW = kChunkThreads / 64;
@@ -924,7 +963,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     float (*wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&sp[0][0]);  // reuses sp after the V pass
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    const int bg = blockIdx.y, b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
+    const int bg = gather_group<G>(P, tid), b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
     const int L = P.seq_lens[b];
     const int T0 = c * P.cg;
     if (T0 >= L) return;
