@@ -53,7 +53,7 @@ class GpuCase:
             self.v = w.v_cache.to(dev)
         self.dec = vsa.Decoder(self.q, self.k, self.v, self.bt, self.sl, vsa.Config.from_dict(w.cfg),
                                max_seq_len=w.max_seq_len, k_lowrank=self.kt, proj=self.proj,
-                               want_idx=want_idx)
+                               want_idx=want_idx, want_group_counts=True)
 
     def run(self, seed=None):
         if seed is not None:
@@ -65,4 +65,5 @@ class GpuCase:
                  stats=self.dec.stats.cpu().numpy().view(np.uint64), z32=self.dec.z_used)
         if self.dec.idx is not None:
             r["idx"] = self.dec.idx.cpu().numpy()
+        r["gcounts"] = self.dec.group_counts.cpu().numpy()
         return r

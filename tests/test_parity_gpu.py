@@ -44,6 +44,12 @@ def compare(w, g, o, groups=None, tag=""):
             err_o = np.max(np.abs(g["out"][b, h].astype(np.float64) - o["out"][b, h]))
             err_l = abs(float(g["lse"][b, h]) - o["lse"][b, h])
             assert err_o <= tol and err_l <= tol, (ctx, err_o, err_l)
+        # the group's union of index sets, counted by the gather blocks of every
+        # chunk (atomics from blocks spread over all the device's dies)
+        if "gcounts" in g and "idx" in o:
+            sets = [o["idx"][b, h][o["idx"][b, h] >= 0] for h in range(kv * G, (kv + 1) * G)]
+            nu = np.unique(np.concatenate(sets)).size
+            assert int(g["gcounts"][b, kv, 0]) == nu, (tag, b, kv, int(g["gcounts"][b, kv, 0]), nu)
 
 
 def run_both(w, seeds=(None,), groups=None, want_idx=True, tag=""):

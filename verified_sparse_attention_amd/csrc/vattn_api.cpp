@@ -109,7 +109,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, cand2, crange2, pcount, hist2, total;
+    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -145,6 +145,8 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * (static_cast<size_t>(s.ncg) * s.cg) * sizeof(uint32_t));
     L.crange = off;
     off += align_up(BHq * s.ncp * 2 * sizeof(uint32_t));
+    L.gw = off;
+    off += align_up(BHkv * sizeof(uint32_t));
     L.cand2 = off;
     off += align_up(BHq * s.nparts * static_cast<size_t>(s.kcap2) * sizeof(uint64_t));
     L.crange2 = off;
@@ -241,6 +243,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.uw = reinterpret_cast<uint32_t*>(ws + L.uw);
     p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
+    p.gw = reinterpret_cast<uint32_t*>(ws + L.gw);
     p.nparts = s.nparts;
     p.kcap2 = s.kcap2;
     p.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);

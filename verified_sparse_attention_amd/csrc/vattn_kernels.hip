@@ -451,6 +451,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
         P.gcounts[2 * bg] = 0;
         P.gcounts[2 * bg + 1] = 0;
     }
+    if (tid == 0 && h % P.G == 0) P.gw[bg] = 0u;  // the budgets raise it
 
     // 1) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
     const int wl = (L + 31) >> 5;
@@ -875,6 +876,9 @@ __global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
         }
         if (n == NT) flags |= 1;
         hsp->n = n;
+        // the group's gather dispatch weight: expected member density (non-negative
+        // fp32 values order as their bit patterns)
+        atomicMax(&P.gw[bg], __float_as_uint(static_cast<float>(R.sp + R.wp + R.k + n) / static_cast<float>(L)));
         hsp->flags = flags;
         hsp->m = m;
         hsp->wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
@@ -914,28 +918,18 @@ constexpr int kGatherUnrollK = 8;  // K rows per batch and lane group (VALU scor
 // rows per chunk are dispatched first, so the blocks still running at the end
 // of the kernel are the light ones and the tail, where too few blocks are left
 // to keep HBM busy, stays short.  Every block derives the same order from the
-// budgets (written by the previous kernel).  With more heads than threads the
-// rows keep their own groups.
-template <int G>
+// group weights the budgets wrote.  With more groups than threads the rows
+// keep their own groups.
 __device__ __forceinline__ int gather_group(const Plan& P, int tid) {
     __shared__ float gw[kChunkThreads];
     __shared__ int s_bg;
-    const int nh = P.B * P.Hq, ngr = P.B * P.Hkv, y = blockIdx.y;
-    if (nh > kChunkThreads) return y;  // uniform over the grid
+    const int ngr = P.B * P.Hkv, y = blockIdx.y;
+    if (ngr > kChunkThreads) return y;  // uniform over the grid
     if (tid == 0) s_bg = y;
-    float w = 0.0f;
-    if (tid < nh) {
-        const HeadState& s = P.hs[tid];
-        const int L = s.L;
-        w = L > 0 ? static_cast<float>(s.n_fixed + s.n) / static_cast<float>(L) : 0.0f;
-    }
-    // a group's heads are G consecutive threads of one wave
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) w = fmaxf(w, __shfl_xor(w, o, 64));
-    if (tid < nh && tid % G == 0) gw[tid / G] = w;
+    const float mine = tid < ngr ? __uint_as_float(P.gw[tid]) : 0.0f;
+    if (tid < ngr) gw[tid] = mine;
     __syncthreads();
     if (tid < ngr) {  // thread tid ranks group tid
-        const float mine = gw[tid];
         int rank = 0;
         for (int u = 0; u < ngr; ++u) {
             const float o = gw[u];
@@ -963,7 +957,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     float (*wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&sp[0][0]);  // reuses sp after the V pass
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
-    const int bg = gather_group<G>(P, tid), b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
+    const int bg = gather_group(P, tid), b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
     const int L = P.seq_lens[b];
     const int T0 = c * P.cg;
     if (T0 >= L) return;

@@ -67,6 +67,7 @@ struct Plan {
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
     uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
+    uint32_t* gw;      // [B*Hkv] gather dispatch weight: max over the group's heads of (n_fixed + n) / L, fp32 bits
     // pre-merged candidate parts (nparts > 0 only: few heads, many chunks)
     int nparts, kcap2; // parts; key slots per part = min(k bound, cp * chunks in the largest part)
     uint64_t* cand2;   // [B*Hq][nparts][kcap2] each part's exact top-min(k, n) keys
