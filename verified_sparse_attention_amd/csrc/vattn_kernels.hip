@@ -1329,45 +1329,80 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
 // emit: the index set of one head, ascending, -1 padded
 // ===========================================================================
 __global__ __launch_bounds__(kEmitThreads) void k_emit(Plan P) {
-    __shared__ uint32_t wsum[kEmitThreads / 64];
+    // A span of 4 * kEmitQuads * kEmitThreads tokens is one pass: wave w owns
+    // quads [w * 64 * kEmitQuads, (w + 1) * 64 * kEmitQuads) of it and lane l
+    // the quads l + 64 k (coalesced loads), so the wave's tokens ascend in
+    // (k, lane) order; one wave prefix sum per k and one block scan of the
+    // wave totals place every member.
+    constexpr int NW = kEmitThreads / 64, KQ = kEmitQuads, SPAN = 4 * KQ * kEmitThreads;
+    __shared__ uint32_t wtot[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq;
     const int G = P.G, g = h / G;
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
     const HeadState hs = P.hs[bh];
     const uint32_t* bits = P.bits + static_cast<size_t>(bh) * P.words;
+    const uint32_t* uwg = group_words(P, b * P.Hkv + g);
     int32_t* out = P.idx + static_cast<size_t>(bh) * P.idx_cap;
+    const int cap = P.idx_cap;
     int written = 0;
-    for (int T0 = 0; T0 < L; T0 += 4 * blockDim.x) {
-        const int qd = (T0 >> 2) + threadIdx.x;
-        bool mem[4] = {false, false, false, false};
-        uint32_t mine = 0;
-        if (4 * qd < L) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (4 * qd + 3 >= R.lo && 4 * qd < R.hi)
-                w = *reinterpret_cast<const uint4*>(group_words(P, b * P.Hkv + g) + 4 * qd);
+    for (int S0 = 0; S0 < L; S0 += SPAN) {
+        const int q0 = (S0 >> 2) + wave * 64 * KQ + lane;
+        uint4 w[KQ];
+        uint32_t fw[KQ];
+#pragma unroll
+        for (int k = 0; k < KQ; ++k) {  // every load of the span first
+            const int qd = q0 + 64 * k;
+            const bool live = 4 * qd < L;
+            const bool anyM = live && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
+            w[k] = anyM ? *reinterpret_cast<const uint4*>(uwg + 4 * qd) : make_uint4(0, 0, 0, 0);
+            fw[k] = live ? bits[qd >> 3] : 0u;
+        }
+        uint32_t m[KQ], ex[KQ], run = 0;
+#pragma unroll
+        for (int k = 0; k < KQ; ++k) {
+            const int qd = q0 + 64 * k;
+            uint32_t mk = 0;
+#pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * qd + e;
-                if (i >= L) continue;
-                const bool fx = bit_of(bits, i);
+                const bool fx = i < L && ((fw[k] >> (i & 31)) & 1u);
                 const bool inM = i >= R.lo && i < R.hi;
                 const bool sn = inM && !fx && hs.n > 0 &&
-                                sample_key(word_of(w, e), static_cast<uint32_t>(i)) >= hs.thr_n;
-                mem[e] = fx || sn;
-                mine += mem[e] ? 1u : 0u;
+                                sample_key(word_of(w[k], e), static_cast<uint32_t>(i)) >= hs.thr_n;
+                mk |= (fx || sn) ? (1u << e) : 0u;
             }
+            m[k] = mk;
+            const uint32_t c = static_cast<uint32_t>(__builtin_popcount(mk));
+            const uint32_t inc = wave_incl_scan(c);
+            ex[k] = run + inc - c;
+            run += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
         }
-        uint32_t tot;
-        uint32_t pos = block_excl_scan(mine, wsum, tot) + written;
-        for (int e = 0; e < 4; ++e)
-            if (mem[e]) {
-                if (pos < static_cast<uint32_t>(P.idx_cap)) out[pos] = 4 * qd + e;
-                ++pos;
-            }
-        written += static_cast<int>(tot);
+        if (lane == 0) wtot[wave] = run;
+        __syncthreads();
+        uint32_t woff = 0, stot = 0;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) {
+            const uint32_t t = wtot[x];
+            woff += x < wave ? t : 0u;
+            stot += t;
+        }
+        __syncthreads();  // the totals are rewritten by the next span
+#pragma unroll
+        for (int k = 0; k < KQ; ++k) {
+            uint32_t pos = static_cast<uint32_t>(written) + woff + ex[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((m[k] >> e) & 1u) {
+                    if (pos < static_cast<uint32_t>(cap)) out[pos] = 4 * (q0 + 64 * k) + e;
+                    ++pos;
+                }
+        }
+        written += static_cast<int>(stot);
     }
-    written = min(written, P.idx_cap);
-    for (int x = written + threadIdx.x; x < P.idx_cap; x += blockDim.x) out[x] = -1;
+    written = min(written, cap);
+    for (int x = written + tid; x < cap; x += kEmitThreads) out[x] = -1;
 }
 
 // ===========================================================================

@@ -11,6 +11,7 @@ constexpr int kSelectThreads = 1024; // per-head exact top-k and base threshold
 constexpr int kBudgetThreads = 1024;  // per-head statistics, budget and final threshold
 constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
+constexpr int kEmitQuads = 8;       // token quads per lane and pass of the index-set emission
 constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
 constexpr int kSampBits = 11;        // sampler histogram: top bits of the Philox word
 constexpr int kSampBins = 1 << kSampBits;
