@@ -275,6 +275,12 @@ FULL = {
     "flat_128k": (lambda: synthetic.flat_128k(), [(0, 0), (0, 6)]),
     "ragged_b64": (lambda: synthetic.ragged_b64(), [(0, 1), (17, 4), (40, 0), (63, 7)]),
     "wide_gqa_64k": (lambda: synthetic.wide_gqa_64k(), [(1, 2), (3, 7)]),
+    # the longest sequence the library takes (2^20 tokens): 256 predictor
+    # chunks pre-merged in parts, 1024 gather chunks, 32 emission passes
+    "max_seq_1m": (lambda: synthetic.make(
+        name="max_seq_1m", B=1, Hq=4, Hkv=1, d=64, seq_lens=(1 << 20,), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=32, sinks=64, window=64, topk_ppm=2500, eps=0.05,
+        data_seed=31), [(0, 0)]),
 }
 
 
