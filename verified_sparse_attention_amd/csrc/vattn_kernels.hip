@@ -725,8 +725,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 // ===========================================================================
 constexpr int kStatsBatch = 4;  // entries of each of a wave's two chunks requested per lane at once
 
-__global__ __launch_bounds__(kBudgetThreads) void k_budget(Plan P) {
-    constexpr int NW = kBudgetThreads / 64;
+template <int kThreads>  // per block
+__global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
+    constexpr int NW = kThreads / 64;
     static_assert(NW >= 2, "one wave for m, one for the chunk offsets");
     __shared__ HeadSamp SS;
     __shared__ SelShared<1> FS;
@@ -1495,7 +1496,11 @@ static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) 
     int rc = 0;
     hipLaunchKernelGGL((k_base<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
     if ((rc = mk.mark(3))) return rc;
-    hipLaunchKernelGGL(k_budget, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
+    // with many heads the per-head kernels run smaller blocks, several per CU
+    if (p.B * p.Hq >= kManyHeads)
+        hipLaunchKernelGGL(k_budget<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+    else
+        hipLaunchKernelGGL(k_budget<kBudgetThreads>, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
     if ((rc = mk.mark(4))) return rc;
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
     return mk.mark(5);
@@ -1538,7 +1543,8 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
         hipLaunchKernelGGL(k_premerge, dim3(p.B * p.Hq, p.nparts), dim3(kSelectThreads), 0, st, p);
         hipLaunchKernelGGL(k_select<true>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
     } else {
-        hipLaunchKernelGGL(k_select<false>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+        hipLaunchKernelGGL(k_select<false>, dim3(p.B * p.Hq),
+                           dim3(p.B * p.Hq >= kManyHeads ? kHeadThreadsMany : kSelectThreads), 0, st, p);
     }
     if ((rc = mk.mark(2))) return rc;
     // 3-5. base scores, budget, gather
