@@ -1329,13 +1329,14 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
 // ===========================================================================
 // emit: the index set of one head, ascending, -1 padded
 // ===========================================================================
-__global__ __launch_bounds__(kEmitThreads) void k_emit(Plan P) {
-    // A span of 4 * kEmitQuads * kEmitThreads tokens is one pass: wave w owns
+template <int kThreads>  // per block
+__global__ __launch_bounds__(kThreads) void k_emit(Plan P) {
+    // A span of 4 * kEmitQuads * kThreads tokens is one pass: wave w owns
     // quads [w * 64 * kEmitQuads, (w + 1) * 64 * kEmitQuads) of it and lane l
     // the quads l + 64 k (coalesced loads), so the wave's tokens ascend in
     // (k, lane) order; one wave prefix sum per k and one block scan of the
     // wave totals place every member.
-    constexpr int NW = kEmitThreads / 64, KQ = kEmitQuads, SPAN = 4 * KQ * kEmitThreads;
+    constexpr int NW = kThreads / 64, KQ = kEmitQuads, SPAN = 4 * KQ * kThreads;
     __shared__ uint32_t wtot[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq;
@@ -1403,7 +1404,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(Plan P) {
         written += static_cast<int>(stot);
     }
     written = min(written, cap);
-    for (int x = written + tid; x < cap; x += kEmitThreads) out[x] = -1;
+    for (int x = written + tid; x < cap; x += kThreads) out[x] = -1;
 }
 
 // ===========================================================================
@@ -1570,7 +1571,12 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
     if (rc) return rc;
     hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
     if ((rc = mk.mark(6))) return rc;
-    if (p.idx) hipLaunchKernelGGL(k_emit, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
+    if (p.idx) {
+        if (p.B * p.Hq >= kManyHeads)
+            hipLaunchKernelGGL(k_emit<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+        else
+            hipLaunchKernelGGL(k_emit<kEmitThreads>, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
+    }
     if ((rc = mk.mark(7))) return rc;
     return static_cast<int>(hipGetLastError());
 }
