@@ -5,18 +5,21 @@
 //                            score the G query heads of the KV group, keep the
 //                            chunk's top-k candidates per head; the chunk's
 //                            sample words, grouped by their top bits
+//   premerge (b*Hq, part)    only with few heads and many chunks: each part's
+//                            chunk candidates reduced to its exact top-k
 //   select   (b*Hq)          exact top-k from the candidates, fixed-set bitmap
 //                            (sinks, window, top-k), tail histogram,
 //                            base-sample threshold in the sample order
-//   base     (chunk, b*Hkv)  pinned exact scores of the union of the group's
+//   base     (b*Hkv, chunk)  pinned exact scores of the union of the group's
 //                            fixed sets and base samples -> score cache, chunk
 //                            maxima, member lists
-//   stats    (chunk, b*Hkv)  exact fixed-point denominator statistics of the
-//                            chunk's members, added to each head's totals
-//   budget   (b*Hq)          CLT budget, final-sample threshold
-//   gather   (chunk, b*Hkv)  over the union of the group's index sets: K row
-//                            (unless its score is cached) and V row per token,
-//                            weighted softmax partials per chunk
+//   budget   (b*Hq)          exact fixed-point denominator statistics of the
+//                            head's fixed set and base sample, CLT budget,
+//                            final-sample threshold, the group's dispatch weight
+//   gather   (chunk, b*Hkv)  over the union of the group's index sets, groups
+//                            densest first: K row (unless its score is cached)
+//                            and V row per token, weighted softmax partials
+//                            per chunk
 //   combine  (b*Hq)          merge chunk partials -> out, lse, counts, stats
 //   emit     (b*Hq)          optional: the index set in ascending order
 //
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
         return bit_of_coherent(bits, i);
     });
     if (tid == 0) {
-        HeadState hs{};  // the statistics start at zero for the stats pass
+        HeadState hs{};  // statistics, budget and thresholds are filled in by the budget pass
         hs.L = L;
         hs.k = R.k;
         hs.n_fixed = R.sp + R.wp + R.k;

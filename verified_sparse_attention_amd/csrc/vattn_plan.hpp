@@ -33,7 +33,7 @@ struct HeadState {
     uint64_t thr_n;  // final sample = tail tokens with sample key >= thr_n (n > 0)
     float m;         // max pinned score over I_f and the base sample
     float wsamp;     // N_t / n as fp32
-    uint64_t SF, S1, S2hi, S2lo;  // zeroed by select, accumulated by stats
+    uint64_t SF, S1, S2hi, S2lo;  // exact sums, written by the budget pass
 };
 
 struct Plan {
