@@ -59,8 +59,8 @@ def _load():
             lib = C.CDLL(_LIB)
             P = C.c_void_p
             lib.orc_decode.restype = C.c_int
-            lib.orc_decode.argtypes = [C.POINTER(OrcCfg)] + [C.c_int] * 7 + [P] * 7 + \
-                [C.c_int, C.c_int] + [P] * 5 + [C.c_int] + [P] * 3
+            lib.orc_decode.argtypes = [C.POINTER(OrcCfg)] + [C.c_int] * 7 + [P] * 4 + [C.c_int] + \
+                [P] * 3 + [C.c_int, C.c_int] + [P] * 5 + [C.c_int] + [P] * 3
             lib.orc_pdot.restype = C.c_float
             lib.orc_pdot.argtypes = [P, C.c_int, P, C.c_int, C.c_int]
             lib.orc_pexp.restype = C.c_float
@@ -147,7 +147,8 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
 
     q: [B,Hq,d] float32.  k_cache/v_cache: [num_blocks,Hkv,16,d] float32, or
     uint16 holding bf16 bit patterns.  block_table [B,max_blocks] int32,
-    seq_lens [B] int32, proj [d,r] float32 (low-rank predictor) or None.
+    seq_lens [B] int32, proj [d,r] float32 (low-rank predictor; or [Hkv,d,r], one basis per
+    KV head) or None.
     cfg keys: sinks, window, topk_abs, topk_ppm, base_ppm, force_budget,
     predictor (0 exact, 1 low-rank), rank, eps, delta, seed.
     groups: iterable of (b, g) to evaluate (default all).  Returns a dict of
@@ -166,8 +167,12 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max()) if seq_lens.size else 0
     max_seq_len = max(int(max_seq_len), 1)
+    proj_heads = 1
     if proj is not None:
         proj = np.ascontiguousarray(proj, dtype=np.float32)
+        if proj.ndim == 3:  # one basis per KV head
+            assert proj.shape[0] == Hkv
+            proj_heads = Hkv
     c = OrcCfg(int(cfg["sinks"]), int(cfg["window"]), int(cfg.get("topk_abs", -1)),
                int(cfg.get("topk_ppm", 0)), int(cfg.get("base_ppm", 50000)),
                int(cfg.get("force_budget", -1)), int(cfg["predictor"]), int(cfg.get("rank", 0)),
@@ -187,7 +192,7 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
         garr = np.array([b * Hkv + g for (b, g) in groups], dtype=np.int32)
         ng = garr.shape[0]
     rc = _load().orc_decode(C.byref(c), B, Hq, Hkv, d, max_blocks, int(kv_bf16), max_seq_len,
-                            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proj), _ptr(block_table),
+                            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proj), proj_heads, _ptr(block_table),
                             _ptr(seq_lens), _ptr(garr), ng, int(nthreads), _ptr(out), _ptr(lse),
                             _ptr(lse_dense), _ptr(out_dense), _ptr(idx), max_seq_len,
                             _ptr(counts), _ptr(stats), _ptr(pred))

@@ -224,7 +224,8 @@ typedef struct {
     const float* q;
     const void* k_cache;
     const void* v_cache;
-    const float* proj;
+    const float* proj;   /* [proj_heads][d][r]: one basis, or one per KV head */
+    int proj_heads;
     const int32_t* block_table;
     const int32_t* seq_lens;
     /* outputs */
@@ -342,7 +343,8 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
     float* qt = NULL;
     if (cfg->predictor == 1) {
         qt = (float*)malloc(sizeof(float) * r);
-        for (int j = 0; j < r; ++j) qt[j] = orc_pdot(qs, 1, cx->proj + j, r, d);
+        const float* P = cx->proj + (size_t)(cx->proj_heads > 1 ? g : 0) * d * r;  /* the group's basis */
+        for (int j = 0; j < r; ++j) qt[j] = orc_pdot(qs, 1, P + j, r, d);
     }
     orc_item* items = (orc_item*)malloc(sizeof(orc_item) * (nM > 0 ? nM : 1));
     for (int t = 0; t < nM; ++t) {
@@ -470,7 +472,7 @@ static void decode_group(const orc_ctx* cx, int b, int g) {
     if (cx->cfg->predictor == 1 && L > 0) {
         int r = cx->cfg->rank;
         uint16_t* kt16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * r);
-        orc_project_rows(K, L, d, cx->proj, r, kt16);
+        orc_project_rows(K, L, d, cx->proj + (size_t)(cx->proj_heads > 1 ? g : 0) * d * r, r, kt16);
         Kt = (float*)malloc(sizeof(float) * (size_t)L * r);
         for (int64_t t = 0; t < (int64_t)L * r; ++t) Kt[t] = bf16_to_f32(kt16[t]);
         free(kt16);
@@ -486,17 +488,18 @@ static void decode_group(const orc_ctx* cx, int b, int g) {
  */
 int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks, int kv_bf16,
                int max_seq_len, const float* q, const void* k_cache, const void* v_cache,
-               const float* proj, const int32_t* block_table, const int32_t* seq_lens,
+               const float* proj, int proj_heads, const int32_t* block_table, const int32_t* seq_lens,
                const int32_t* groups, int n_groups, int nthreads, double* out, double* lse,
                double* lse_dense, double* out_dense, int32_t* idx, int idx_cap,
                int32_t* counts, uint64_t* stats, float* pred_scores) {
     if (!cfg || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse) return 1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d % 8 != 0 || d > 512) return 2;
     if (cfg->predictor == 1 && (!proj || cfg->rank % 8 != 0 || cfg->rank > d)) return 3;
+    if (proj_heads != 1 && proj_heads != Hkv) return 3;
     if (idx && idx_cap < max_seq_len) return 4;
     orc_init_constants();
     orc_ctx cx = {cfg, B, Hq, Hkv, d, max_blocks, kv_bf16, max_seq_len, q, k_cache, v_cache,
-                  proj, block_table, seq_lens, out, lse, lse_dense, out_dense, idx, idx_cap,
+                  proj, proj_heads, block_table, seq_lens, out, lse, lse_dense, out_dense, idx, idx_cap,
                   counts, stats, pred_scores};
     int total = groups ? n_groups : B * Hkv;
     if (nthreads < 1) nthreads = 1;

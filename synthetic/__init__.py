@@ -17,7 +17,7 @@ Layouts (all contiguous, host tensors):
   v_cache      [num_blocks, Hkv, 16, d]      same dtype as k_cache
   block_table  [B, max_blocks]               int32 (page ids, -1 unused)
   seq_lens     [B]                           int32
-  proj         [d, r]                        float32, orthonormal columns
+  proj         [d, r] or [Hkv, d, r]         float32, orthonormal columns (one basis, or one per KV head)
 """
 from __future__ import annotations
 
@@ -118,7 +118,7 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
          topk_ppm=25000, base_ppm=50000, force_budget=-1, eps=0.05, delta=0.05, seed=0,
          data_seed=1000, shuffle=False, q_std=1.0, k_std=1.0, planted=8, plant_scale=4.0,
          outlier_channels=4, outlier_scale=8.0, lowrank_dim=24, lowrank_noise=0.1,
-         peaked_frac=0.5, hidden_logit=40.0, max_seq_len=None) -> Workload:
+         peaked_frac=0.5, hidden_logit=40.0, max_seq_len=None, proj_per_head=False) -> Workload:
     """Draw one workload.
 
     recipe:
@@ -226,7 +226,12 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
     dt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
     k_cache = _to_paged(rows_k, bt, seq_lens, num_blocks, dt)
     v_cache = _to_paged(rows_v, bt, seq_lens, num_blocks, dt)
-    proj = hidden_proj if hidden_proj is not None else (orthonormal(d, rank, gen) if predictor == 1 else None)
+    if hidden_proj is not None:
+        proj = hidden_proj
+    elif predictor == 1 and proj_per_head:  # a seeded orthonormal basis for every KV head
+        proj = torch.stack([orthonormal(d, rank, gen) for _ in range(Hkv)])
+    else:
+        proj = orthonormal(d, rank, gen) if predictor == 1 else None
     cfg = dict(sinks=sinks, window=window, topk_abs=topk_abs, topk_ppm=topk_ppm,
                base_ppm=base_ppm, force_budget=force_budget, predictor=predictor,
                rank=rank if predictor == 1 else 0, eps=eps, delta=delta, seed=seed)

@@ -380,3 +380,41 @@ def test_degenerate_inputs():
     r = run(w, want_pred=True)
     assert np.all(r["counts"][0, :, 0] == 0) and np.all(r["counts"][0, :, 1] == 500)
     _structure_check(w, r)
+
+
+# ---------------------------------------------------------------------------
+# One predictor basis per KV head: each group's low-rank query and keys use
+# its own basis, and nothing else changes.
+# ---------------------------------------------------------------------------
+def _per_head_case():
+    return synthetic.make(name="per_head_bases", B=2, Hq=8, Hkv=4, d=64, seq_lens=(900, 517),
+                          kv_dtype="bf16", recipe="outlier", predictor=1, rank=16, sinks=8,
+                          window=16, topk_ppm=30000, proj_per_head=True, data_seed=41)
+
+
+def test_per_head_bases_equal_to_one_shared_basis_give_its_results():
+    w = _per_head_case()
+    a = w.oracle_arrays()
+    P = a["proj"][1]
+    shared = oracle.decode(**dict(a, proj=P), cfg=w.cfg)
+    stacked = oracle.decode(**dict(a, proj=np.stack([P] * w.Hkv)), cfg=w.cfg)
+    for key in ("idx", "counts", "stats", "out", "lse"):
+        assert np.array_equal(shared[key], stacked[key]), key
+
+
+def test_each_group_uses_its_own_basis():
+    w = _per_head_case()
+    a = w.oracle_arrays()
+    assert a["proj"].shape == (w.Hkv, w.d, 16)
+    full = oracle.decode(**a, cfg=w.cfg)
+    G = w.Hq // w.Hkv
+    differs = 0
+    for g in range(w.Hkv):
+        own = oracle.decode(**dict(a, proj=a["proj"][g]), cfg=w.cfg, groups=[(b, g) for b in range(w.B)])
+        other = oracle.decode(**dict(a, proj=a["proj"][(g + 1) % w.Hkv]), cfg=w.cfg,
+                              groups=[(b, g) for b in range(w.B)])
+        hs = slice(g * G, (g + 1) * G)
+        for key in ("idx", "counts", "stats", "out", "lse"):
+            assert np.array_equal(full[key][:, hs], own[key][:, hs]), (g, key)
+        differs += int(not np.array_equal(full["idx"][:, hs], other["idx"][:, hs]))
+    assert differs > 0  # the bases matter: another head's basis selects other tokens
