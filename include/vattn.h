@@ -97,7 +97,8 @@ typedef struct {
     const void* v_cache;        /* [num_blocks, Hkv, 16, d] kv_dtype                  */
     const uint16_t* k_lowrank;  /* [num_blocks, Hkv, 16, r] bf16 bits (LOWRANK only;  */
                                 /* produced by vattn_project_keys), else NULL         */
-    const float* proj;          /* [d, r] fp32 (LOWRANK only), else NULL              */
+    const float* proj;          /* [d, r] fp32, or [Hkv, d, r] (proj_heads = Hkv)     */
+                                /* (LOWRANK only), else NULL                          */
     const int32_t* block_table; /* [B, max_blocks] page ids                           */
     const int32_t* seq_lens;    /* [B] tokens in each sequence, 0 <= L <= max_seq_len  */
     int32_t B;                  /* host: batch, >= 1                                  */
@@ -108,6 +109,10 @@ typedef struct {
     int32_t max_seq_len;        /* host: bound on seq_lens, 1 .. VATTN_MAX_SEQ,       */
                                 /*       <= 16 * max_blocks                            */
     int32_t kv_dtype;           /* host: vattn_dtype of k_cache / v_cache             */
+    int32_t proj_heads;         /* host: 0 or 1: one basis for all heads; Hkv: one    */
+                                /*   basis per KV head (its query heads' low-rank     */
+                                /*   queries and its low-rank keys use it); else      */
+                                /*   VATTN_E_SHAPE                                    */
 } vattn_inputs;
 
 /* Outputs.  out and lse are required; the others are optional (NULL = skip). */
@@ -153,14 +158,16 @@ vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
 
 /* Low-rank key cache for the LOWRANK predictor (Loki page, abstract: keys
  * scored in a low-dimensional space): k_lowrank[p][g][t][j] =
- * bf16_rne(pdot(K[p][g][t][:], P[:, j])) for every page p < num_blocks.
- * k_cache: [num_blocks, Hkv, 16, d] kv_dtype; proj: [d, r] fp32;
+ * bf16_rne(pdot(K[p][g][t][:], P_g[:, j])) for every page p < num_blocks,
+ * P_g = proj (proj_heads 0 or 1: [d, r] fp32) or proj[g] (proj_heads = Hkv:
+ * [Hkv, d, r] fp32); another proj_heads gives VATTN_E_SHAPE.
+ * k_cache: [num_blocks, Hkv, 16, d] kv_dtype;
  * k_lowrank: [num_blocks, Hkv, 16, r] bf16 bits (output).  pdot is the
  * blocked fp32 dot product the predictor uses (fma chains over blocks of 8,
  * then a pairwise tree over the block partials).  Asynchronous on hip_stream. */
 vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const float* proj,
                                 uint16_t* k_lowrank, int32_t num_blocks, int32_t Hkv,
-                                int32_t d, int32_t r, void* hip_stream);
+                                int32_t d, int32_t r, int32_t proj_heads, void* hip_stream);
 
 /* Key-side maintenance for one decode step: writes the newest token of each
  * sequence into the paged caches and, when k_lowrank is given, its low-rank
@@ -170,12 +177,13 @@ vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const flo
  * slot = pos[b] % 16, and every KV head g:
  *   k_cache[page][g][slot][:]   = k_new[b][g][:]
  *   v_cache[page][g][slot][:]   = v_new[b][g][:]
- *   k_lowrank[page][g][slot][j] = bf16_rne(pdot(k_new[b][g][:], P[:, j]))
+ *   k_lowrank[page][g][slot][j] = bf16_rne(pdot(k_new[b][g][:], P_g[:, j]))
  * with the same pdot and rounding as vattn_project_keys.  pos[b] < 0 leaves
  * sequence b untouched.
  * k_new, v_new: [B, Hkv, d] in kv_dtype (device); pos: [B] int32 (device);
  * block_table: [B, max_blocks] int32 (device); caches as for vattn_decode;
- * k_lowrank and proj ([d, r] fp32) are both NULL or both given.  All pointers
+ * k_lowrank and proj are both NULL or both given; proj and proj_heads as for
+ * vattn_project_keys (P_g the KV head's basis).  All pointers
  * are caller-owned and 16-byte aligned; the library allocates nothing.
  * Returns VATTN_E_NULL, VATTN_E_DTYPE, VATTN_E_SHAPE or VATTN_E_UNSUPPORTED
  * before any launch for bad arguments, VATTN_E_HIP for a failed launch.
@@ -186,7 +194,7 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
                              const int32_t* block_table, int32_t B, int32_t max_blocks,
                              void* k_cache, void* v_cache, uint16_t* k_lowrank, const float* proj,
                              int32_t kv_dtype, int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r,
-                             void* hip_stream);
+                             int32_t proj_heads, void* hip_stream);
 
 /* z = Phi^-1(1 - delta/2) rounded to fp32, as vattn_decode uses it (host). */
 double vattn_z_from_delta(double delta);

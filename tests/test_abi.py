@@ -78,6 +78,7 @@ BAD = [
     ("eps0", {}, dict(eps=0.0), 4),
     ("delta1", {}, dict(delta=1.0), 4),
     ("predictor", {}, dict(predictor=5), 4),
+    ("proj_heads", dict(proj_heads=3), {}, 2),  # neither one basis nor one per KV head
     ("rank", {}, dict(rank=24), 6),
     ("rank_gt_d", dict(d=64), dict(rank=128), 6),
 ]
@@ -111,22 +112,23 @@ def test_null_and_workspace_errors(lib):
     assert _decode(lib, inp, cfg, ws=256 + 64, ws_bytes=need) == 5
     # project_keys argument checks
     P = C.c_void_p
-    assert lib.vattn_project_keys(None, 1, P(256), P(256), 4, 2, 128, 32, None) == 1
-    assert lib.vattn_project_keys(P(256), 3, P(256), P(256), 4, 2, 128, 32, None) == 3
-    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 4, 2, 128, 24, None) == 6
-    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 0, 2, 128, 32, None) == 2
+    assert lib.vattn_project_keys(None, 1, P(256), P(256), 4, 2, 128, 32, 1, None) == 1
+    assert lib.vattn_project_keys(P(256), 3, P(256), P(256), 4, 2, 128, 32, 1, None) == 3
+    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 4, 2, 128, 24, 1, None) == 6
+    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 0, 2, 128, 32, 1, None) == 2
+    assert lib.vattn_project_keys(P(256), 1, P(256), P(256), 4, 2, 128, 32, 3, None) == 2  # proj_heads
 
 
 def test_append_kv_argument_checks(lib):
     P = C.c_void_p
     ok = dict(k_new=P(256), v_new=P(256), pos=P(256), bt=P(256), B=4, mb=8, kc=P(256), vc=P(256),
-              kt=P(256), proj=P(256), dt=1, nb=32, Hkv=2, d=128, r=32)
+              kt=P(256), proj=P(256), dt=1, nb=32, Hkv=2, d=128, r=32, ph=1)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.vattn_append_kv(a["k_new"], a["v_new"], a["pos"], a["bt"], a["B"], a["mb"], a["kc"],
                                    a["vc"], a["kt"], a["proj"], a["dt"], a["nb"], a["Hkv"], a["d"], a["r"],
-                                   None)
+                                   a["ph"], None)
     assert call(k_new=None) == 1
     assert call(pos=None) == 1
     assert call(kt=None) == 1          # projection without an output
@@ -137,6 +139,7 @@ def test_append_kv_argument_checks(lib):
     assert call(r=24) == 6
     assert call(d=64, r=128) == 6     # rank above the head dim
     assert call(kc=P(260)) == 2        # misaligned
+    assert call(ph=3) == 2             # neither one basis nor one per KV head
 
 
 def test_workspace_size_monotone(lib):

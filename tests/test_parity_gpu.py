@@ -100,6 +100,11 @@ SMALL_CASES = {
     "premerge_parts": lambda: synthetic.make(
         name="premerge_parts", B=1, Hq=4, Hkv=1, d=128, seq_lens=(40000,), kv_dtype="bf16",
         recipe="outlier", predictor=1, rank=32, sinks=64, window=64, topk_ppm=25000, data_seed=19),
+    # one predictor basis per KV head (4 groups, each with its own P_g)
+    "per_head_bases": lambda: synthetic.make(
+        name="per_head_bases", B=2, Hq=16, Hkv=4, d=128, seq_lens=(5000, 2100), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=32, sinks=32, window=64, topk_ppm=25000,
+        proj_per_head=True, data_seed=20),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
@@ -216,6 +221,17 @@ def test_project_keys_bit_exact():
         rows = k.float().reshape(-1, d).numpy()
         want = oracle.project_rows(rows, P.numpy()).reshape(kt.shape)
         assert np.array_equal(kt, want)
+    # one basis per KV head: head g's rows use P_g
+    for (d, r, dt) in ((128, 32, torch.bfloat16), (64, 16, torch.float32), (128, 64, torch.bfloat16)):
+        log("[parity] project_keys per head d=%d r=%d %s" % (d, r, dt))
+        gen = torch.Generator().manual_seed(d * 3000 + r)
+        k = (torch.randn(29, 4, 16, d, generator=gen) * 2.0).to(dt)
+        Ph = torch.stack([synthetic.orthonormal(d, r, gen) for _ in range(4)])
+        kt = vsa.project_keys(k.cuda(), Ph.cuda()).cpu().numpy().view(np.uint16)
+        for g in range(4):
+            rows = k[:, g].float().reshape(-1, d).numpy()
+            want = oracle.project_rows(rows, Ph[g].numpy()).reshape(kt[:, g].shape)
+            assert np.array_equal(kt[:, g], want), g
 
 
 def test_append_kv_bit_exact():
@@ -224,9 +240,10 @@ def test_append_kv_bit_exact():
     import torch
     import verified_sparse_attention_amd as vsa
     _, log = _gpu()
-    for (d, r, dt, with_lr) in ((128, 32, torch.bfloat16, True), (64, 16, torch.float32, True),
-                                (128, 64, torch.bfloat16, True), (64, 32, torch.bfloat16, False)):
-        log("[parity] append_kv d=%d r=%d %s lowrank=%s" % (d, r, dt, with_lr))
+    for (d, r, dt, with_lr, per_head) in ((128, 32, torch.bfloat16, True, False), (64, 16, torch.float32, True, False),
+                                          (128, 64, torch.bfloat16, True, False), (64, 32, torch.bfloat16, False, False),
+                                          (128, 32, torch.bfloat16, True, True), (64, 16, torch.float32, True, True)):
+        log("[parity] append_kv d=%d r=%d %s lowrank=%s per_head=%s" % (d, r, dt, with_lr, per_head))
         gen = torch.Generator().manual_seed(7000 + d + r)
         B, Hkv, max_blocks = 5, 3, 6
         nb = B * max_blocks + 4
@@ -236,7 +253,8 @@ def test_append_kv_bit_exact():
         v_cache = torch.randn(nb, Hkv, 16, d, generator=gen).to(dt)
         k_new = (torch.randn(B, Hkv, d, generator=gen) * 2.0).to(dt)
         v_new = torch.randn(B, Hkv, d, generator=gen).to(dt)
-        P = synthetic.orthonormal(d, r, gen)
+        P = (torch.stack([synthetic.orthonormal(d, r, gen) for _ in range(Hkv)]) if per_head
+             else synthetic.orthonormal(d, r, gen))
         kt0 = torch.randint(-30000, 30000, (nb, Hkv, 16, r), generator=gen, dtype=torch.int16)
         kc, vc, kt = k_cache.cuda(), v_cache.cuda(), kt0.cuda()
         vsa.append_kv(k_new.cuda(), v_new.cuda(), pos.cuda(), bt.cuda(), kc, vc,
@@ -250,7 +268,10 @@ def test_append_kv_bit_exact():
             page, slot = int(bt[b, p // 16]), p % 16
             want_k[page, :, slot] = k_new[b]
             want_v[page, :, slot] = v_new[b]
-            if with_lr:
+            if with_lr and per_head:
+                for g in range(Hkv):
+                    want_t[page, g, slot] = oracle.project_rows(k_new[b, g:g + 1].float().numpy(), P[g].numpy())[0]
+            elif with_lr:
                 want_t[page, :, slot] = oracle.project_rows(k_new[b].float().numpy(), P.numpy())
         assert torch.equal(kc.cpu(), want_k) and torch.equal(vc.cpu(), want_v)
         assert np.array_equal(kt.cpu().numpy().view(np.uint16), want_t)

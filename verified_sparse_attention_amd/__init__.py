@@ -50,7 +50,7 @@ class vattn_inputs(C.Structure):
                 ("k_lowrank", C.c_void_p), ("proj", C.c_void_p), ("block_table", C.c_void_p),
                 ("seq_lens", C.c_void_p), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
                 ("d", C.c_int32), ("max_blocks", C.c_int32), ("num_blocks", C.c_int32),
-                ("max_seq_len", C.c_int32), ("kv_dtype", C.c_int32)]
+                ("max_seq_len", C.c_int32), ("kv_dtype", C.c_int32), ("proj_heads", C.c_int32)]
 
 
 class vattn_outputs(C.Structure):
@@ -82,11 +82,11 @@ def load():
                                               C.c_void_p, C.POINTER(C.c_void_p), C.c_int32]
         lib.vattn_project_keys.restype = C.c_int
         lib.vattn_project_keys.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
-                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+                                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
         lib.vattn_append_kv.restype = C.c_int
         lib.vattn_append_kv.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
-                                        C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+                                        C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
         lib.vattn_z_from_delta.restype = C.c_double
         lib.vattn_z_from_delta.argtypes = [C.c_double]
         lib.vattn_status_string.restype = C.c_char_p
@@ -151,7 +151,12 @@ def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowra
                         None if k_lowrank is None else k_lowrank.data_ptr(),
                         None if proj is None else proj.data_ptr(), block_table.data_ptr(),
                         seq_lens.data_ptr(), B, Hq, k_cache.shape[1], d, block_table.shape[1],
-                        k_cache.shape[0], int(max_seq_len), _kv_dtype(k_cache))
+                        k_cache.shape[0], int(max_seq_len), _kv_dtype(k_cache), _proj_heads(proj))
+
+
+def _proj_heads(proj):
+    """proj [d, r]: one basis (1); [Hkv, d, r]: one per KV head (Hkv)."""
+    return 1 if proj is None or proj.dim() == 2 else int(proj.shape[0])
 
 
 def workspace_size(inputs: vattn_inputs, cfg: Config) -> int:
@@ -242,14 +247,15 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_l
 
 
 def project_keys(k_cache, proj, k_lowrank=None, stream=None):
-    """Low-rank key cache bf16(K P) for the low-rank predictor (as int16 bit patterns)."""
+    """Low-rank key cache bf16(K P) for the low-rank predictor (as int16 bit patterns);
+    proj [d, r], or [Hkv, d, r] for one basis per KV head."""
     import torch
     nb, Hkv, page, d = k_cache.shape
-    r = proj.shape[1]
+    r = proj.shape[-1]
     if k_lowrank is None:
         k_lowrank = torch.empty(nb, Hkv, page, r, dtype=torch.int16, device=k_cache.device)
     rc = load().vattn_project_keys(_ptr(k_cache), _kv_dtype(k_cache), _ptr(proj), _ptr(k_lowrank),
-                                   nb, Hkv, d, r, _stream_handle(stream))
+                                   nb, Hkv, d, r, _proj_heads(proj), _stream_handle(stream))
     if rc != 0:
         raise VattnError(rc, "vattn_project_keys")
     return k_lowrank
@@ -260,10 +266,11 @@ def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, 
     of the paged caches, and its low-rank key row when k_lowrank/proj are given."""
     B, Hkv, d = k_new.shape
     nb = k_cache.shape[0]
-    r = proj.shape[1] if proj is not None else 0
+    r = proj.shape[-1] if proj is not None else 0
     rc = load().vattn_append_kv(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), B,
                                 block_table.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_lowrank),
-                                _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, r, _stream_handle(stream))
+                                _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, r, _proj_heads(proj),
+                                _stream_handle(stream))
     if rc != 0:
         raise VattnError(rc, "vattn_append_kv")
 

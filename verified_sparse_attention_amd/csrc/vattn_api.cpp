@@ -56,6 +56,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
     if (in->num_blocks < 1) return VATTN_E_SHAPE;
     if (static_cast<long long>(in->B) * in->Hkv > 65535) return VATTN_E_SHAPE;
     if (in->kv_dtype != VATTN_F32 && in->kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (in->proj_heads != 0 && in->proj_heads != 1 && in->proj_heads != in->Hkv) return VATTN_E_SHAPE;
     if (cfg->sinks < 0 || cfg->window < 0 || cfg->topk_abs < -1) return VATTN_E_CFG;
     if (cfg->topk_ppm < 0 || cfg->topk_ppm > 1000000) return VATTN_E_CFG;
     if (cfg->base_ppm < 1 || cfg->base_ppm > 1000000) return VATTN_E_CFG;
@@ -226,6 +227,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.v = in->v_cache;
     p.kt = in->k_lowrank;
     p.proj = in->proj;
+    p.proj_stride = (in->proj_heads > 1 && cfg->predictor == VATTN_PRED_LOWRANK) ? in->d * cfg->rank : 0;
     p.bt = in->block_table;
     p.seq_lens = in->seq_lens;
     char* ws = static_cast<char*>(workspace);
@@ -279,8 +281,9 @@ vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
 
 vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const float* proj,
                                 uint16_t* k_lowrank, int32_t num_blocks, int32_t Hkv, int32_t d,
-                                int32_t r, void* hip_stream) {
+                                int32_t r, int32_t proj_heads, void* hip_stream) {
     if (!k_cache || !proj || !k_lowrank) return VATTN_E_NULL;
+    if (proj_heads != 0 && proj_heads != 1 && proj_heads != Hkv) return VATTN_E_SHAPE;
     if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
     if (num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
     if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
@@ -288,16 +291,18 @@ vattn_status vattn_project_keys(const void* k_cache, int32_t kv_dtype, const flo
     if (r > d) return VATTN_E_SHAPE;
     const long long rows = static_cast<long long>(num_blocks) * Hkv * VATTN_PAGE;
     if ((rows + 3) / 4 > 0x7FFFFFFFLL) return VATTN_E_SHAPE;
-    const int rc = vattn::launch_project(k_cache, kv_dtype == VATTN_BF16, proj, k_lowrank, num_blocks, Hkv,
-                                         d, r, hip_stream);
+    const int rc = vattn::launch_project(k_cache, kv_dtype == VATTN_BF16, proj, proj_heads > 1 ? d * r : 0,
+                                         k_lowrank, num_blocks, Hkv, d, r, hip_stream);
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 
 vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t* pos,
                              const int32_t* block_table, int32_t B, int32_t max_blocks, void* k_cache,
                              void* v_cache, uint16_t* k_lowrank, const float* proj, int32_t kv_dtype,
-                             int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r, void* hip_stream) {
+                             int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r, int32_t proj_heads,
+                             void* hip_stream) {
     if (!k_new || !v_new || !pos || !block_table || !k_cache || !v_cache) return VATTN_E_NULL;
+    if (proj_heads != 0 && proj_heads != 1 && proj_heads != Hkv) return VATTN_E_SHAPE;
     if ((k_lowrank == nullptr) != (proj == nullptr)) return VATTN_E_NULL;
     if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
     if (B < 1 || max_blocks < 1 || num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
@@ -311,7 +316,8 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
     for (const void* q : ptrs)
         if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return VATTN_E_SHAPE;
     const int rc = vattn::launch_append(k_new, v_new, pos, block_table, B, max_blocks, k_cache, v_cache, k_lowrank,
-                                        proj, kv_dtype == VATTN_BF16, Hkv, d, k_lowrank ? r : 16, hip_stream);
+                                        proj, (k_lowrank && proj_heads > 1) ? d * r : 0, kv_dtype == VATTN_BF16,
+                                        Hkv, d, k_lowrank ? r : 16, hip_stream);
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 

@@ -212,8 +212,9 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         // 1) low-rank queries q~ = pdot(q_s, P[:, j])
         if (P.predictor == 1) {
             float* part = reinterpret_cast<float*>(keys);  // free until the score stream
-            if (d == 128) low_rank_query<128, ROW, G>(qs, P.proj, qv, part, tid, nthr);
-            else low_rank_query<64, ROW, G>(qs, P.proj, qv, part, tid, nthr);
+            const float* pg = P.proj + static_cast<size_t>(g) * P.proj_stride;  // the group's basis
+            if (d == 128) low_rank_query<128, ROW, G>(qs, pg, qv, part, tid, nthr);
+            else low_rank_query<64, ROW, G>(qs, pg, qv, part, tid, nthr);
         } else {
             for (int x = tid; x < G * ROW; x += nthr) qv[x] = qs[x];
             __syncthreads();
@@ -1415,12 +1416,15 @@ __global__ __launch_bounds__(kThreads) void k_emit(Plan P) {
 // ===========================================================================
 template <typename KVT, int D, int RK>
 __global__ __launch_bounds__(256) void k_project(const KVT* __restrict__ k, const float* __restrict__ proj,
-                                                 uint16_t* __restrict__ kt, long long nrows) {
-    constexpr int RPB = 256 / RK;  // rows per block
+                                                 uint16_t* __restrict__ kt, long long nrows, int Hkv,
+                                                 int proj_stride) {
+    constexpr int RPB = 256 / RK;  // rows per block, all of one (page, KV head): RPB divides 16
+    static_assert(kPage % RPB == 0, "a block's rows share their KV head");
     __shared__ float ps[D * RK];
     __shared__ float kr[RPB][D];
-    for (int x = threadIdx.x; x < D * RK; x += 256) ps[x] = proj[x];
     const long long r0 = static_cast<long long>(blockIdx.x) * RPB;
+    const float* pg = proj + static_cast<size_t>((r0 / kPage) % Hkv) * proj_stride;  // the head's basis
+    for (int x = threadIdx.x; x < D * RK; x += 256) ps[x] = pg[x];
     for (int x = threadIdx.x; x < RPB * D; x += 256) {
         const int rr = x / D, e = x - rr * D;
         const long long row = r0 + rr;
@@ -1452,7 +1456,8 @@ template <typename KVT, int D, int RK>
 __global__ __launch_bounds__(64) void k_append(const KVT* __restrict__ k_new, const KVT* __restrict__ v_new,
                                                const int32_t* __restrict__ pos, const int32_t* __restrict__ bt,
                                                int max_blocks, int Hkv, KVT* __restrict__ kc, KVT* __restrict__ vc,
-                                               uint16_t* __restrict__ kt, const float* __restrict__ proj) {
+                                               uint16_t* __restrict__ kt, const float* __restrict__ proj,
+                                               int proj_stride) {
     __shared__ float kr[D];
     const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv, lane = threadIdx.x;
     const int p = pos[b];
@@ -1474,7 +1479,7 @@ __global__ __launch_bounds__(64) void k_append(const KVT* __restrict__ k_new, co
     if (kt == nullptr) return;  // block-uniform
     __syncthreads();
     for (int j = lane; j < RK; j += 64) {
-        const float s = pdot_serial<D>(kr, 1, proj + j, RK);
+        const float s = pdot_serial<D>(kr, 1, proj + static_cast<size_t>(g) * proj_stride + j, RK);
         uint32_t u = __float_as_uint(s);
         u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
         kt[row * RK + j] = static_cast<uint16_t>(u >> 16);
@@ -1586,69 +1591,69 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
 
 template <typename KVT, int D>
 static void launch_project_t(const void* k, const float* proj, uint16_t* kt, long long nrows, int r,
-                             hipStream_t st) {
+                             int Hkv, int proj_stride, hipStream_t st) {
     switch (r) {
         case 16: {
             const long long nb = (nrows + 15) / 16;
             hipLaunchKernelGGL((k_project<KVT, D, 16>), dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
-                               static_cast<const KVT*>(k), proj, kt, nrows);
+                               static_cast<const KVT*>(k), proj, kt, nrows, Hkv, proj_stride);
             break;
         }
         case 32: {
             const long long nb = (nrows + 7) / 8;
             hipLaunchKernelGGL((k_project<KVT, D, 32>), dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
-                               static_cast<const KVT*>(k), proj, kt, nrows);
+                               static_cast<const KVT*>(k), proj, kt, nrows, Hkv, proj_stride);
             break;
         }
         default: {
             const long long nb = (nrows + 3) / 4;
             hipLaunchKernelGGL((k_project<KVT, D, 64>), dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
-                               static_cast<const KVT*>(k), proj, kt, nrows);
+                               static_cast<const KVT*>(k), proj, kt, nrows, Hkv, proj_stride);
             break;
         }
     }
 }
 
-int launch_project(const void* k_cache, int kv_bf16, const float* proj, uint16_t* kt, int num_blocks,
-                   int Hkv, int d, int r, void* stream) {
+int launch_project(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint16_t* kt,
+                   int num_blocks, int Hkv, int d, int r, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const long long nrows = static_cast<long long>(num_blocks) * Hkv * kPage;
     if (d == 128) {
-        if (kv_bf16) launch_project_t<uint16_t, 128>(k_cache, proj, kt, nrows, r, st);
-        else launch_project_t<float, 128>(k_cache, proj, kt, nrows, r, st);
+        if (kv_bf16) launch_project_t<uint16_t, 128>(k_cache, proj, kt, nrows, r, Hkv, proj_stride, st);
+        else launch_project_t<float, 128>(k_cache, proj, kt, nrows, r, Hkv, proj_stride, st);
     } else {
-        if (kv_bf16) launch_project_t<uint16_t, 64>(k_cache, proj, kt, nrows, r, st);
-        else launch_project_t<float, 64>(k_cache, proj, kt, nrows, r, st);
+        if (kv_bf16) launch_project_t<uint16_t, 64>(k_cache, proj, kt, nrows, r, Hkv, proj_stride, st);
+        else launch_project_t<float, 64>(k_cache, proj, kt, nrows, r, Hkv, proj_stride, st);
     }
     return static_cast<int>(hipGetLastError());
 }
 
 template <typename KVT, int D>
 static void launch_append_t(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                            int max_blocks, void* kc, void* vc, uint16_t* kt, const float* proj, int Hkv, int r,
-                            hipStream_t st) {
+                            int max_blocks, void* kc, void* vc, uint16_t* kt, const float* proj, int proj_stride,
+                            int Hkv, int r, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(B * Hkv));
     const KVT* kn = static_cast<const KVT*>(k_new);
     const KVT* vn = static_cast<const KVT*>(v_new);
     KVT* kcc = static_cast<KVT*>(kc);
     KVT* vcc = static_cast<KVT*>(vc);
     switch (r) {
-        case 16: hipLaunchKernelGGL((k_append<KVT, D, 16>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
-        case 32: hipLaunchKernelGGL((k_append<KVT, D, 32>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
-        default: hipLaunchKernelGGL((k_append<KVT, D, 64>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj); break;
+        case 16: hipLaunchKernelGGL((k_append<KVT, D, 16>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
+        case 32: hipLaunchKernelGGL((k_append<KVT, D, 32>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
+        default: hipLaunchKernelGGL((k_append<KVT, D, 64>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
     }
 }
 
 int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int kv_bf16,
-                  int Hkv, int d, int r, void* stream) {
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int proj_stride,
+                  int kv_bf16, int Hkv, int d, int r, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d == 128) {
-        if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
-        else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
+        if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
+        else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
     } else {
-        if (kv_bf16) launch_append_t<uint16_t, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
-        else launch_append_t<float, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, Hkv, r, st);
+        if (kv_bf16) launch_append_t<uint16_t, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
+        else launch_append_t<float, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
     }
     return static_cast<int>(hipGetLastError());
 }

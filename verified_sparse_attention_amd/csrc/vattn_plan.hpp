@@ -53,6 +53,7 @@ struct Plan {
     const void* v;
     const uint16_t* kt;
     const float* proj;
+    int proj_stride;  // floats between the KV heads' bases (0: one basis for all)
     const int32_t* bt;
     const int32_t* seq_lens;
     // workspace
@@ -89,11 +90,11 @@ struct Plan {
 
 // Launches one decode step.  Returns 0 or a hipError_t value.
 int launch_decode(const Plan& p, void* stream, void* const* events = nullptr);
-int launch_project(const void* k_cache, int kv_bf16, const float* proj, uint16_t* kt,
+int launch_project(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint16_t* kt,
                    int num_blocks, int Hkv, int d, int r, void* stream);
 size_t predict_lds_bytes(int G, int d, int row, int cp);
 int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int kv_bf16,
-                  int Hkv, int d, int r, void* stream);
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int proj_stride,
+                  int kv_bf16, int Hkv, int d, int r, void* stream);
 
 }  // namespace vattn
