@@ -196,6 +196,29 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
                              int32_t kv_dtype, int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r,
                              int32_t proj_heads, void* hip_stream);
 
+/* Key Gram matrices for a per-head predictor basis.  The Loki page (abstract)
+ * finds that key vectors lie in a much lower-dimensional space; a KV head's
+ * basis P_g for vattn_project_keys (proj_heads = Hkv) can be taken as the r
+ * leading eigenvectors of
+ *   gram[g][i][j] = sum over b < B, t < seq_lens[b] of K[b, t, g, i] K[b, t, g, j]
+ * (K[b, t, g] the cached key of token t of sequence b, read through
+ * block_table as in vattn_decode), the keys' uncentered second moments.  The
+ * eigensolve of this d x d matrix is the caller's (host calibration, outside
+ * the decode path).  Products and sums are fp32 (matrix-core bf16 products,
+ * exact in fp32, then fp32 sums in a fixed order: the result is the same on
+ * every call).
+ * k_cache: [num_blocks, Hkv, 16, d] bf16 only (VATTN_E_UNSUPPORTED for fp32);
+ * block_table [B, max_blocks], seq_lens [B] int32 (device); gram: [Hkv, d, d]
+ * fp32 (device, output); workspace: device buffer of at least
+ * vattn_key_gram_workspace_size bytes, 256-byte aligned, contents garbage
+ * afterwards.  Host-checkable errors are returned before any launch; the
+ * library allocates nothing.  Asynchronous on hip_stream. */
+size_t vattn_key_gram_workspace_size(int32_t B, int32_t Hkv, int32_t d, int32_t max_seq_len);
+vattn_status vattn_key_gram(const void* k_cache, int32_t kv_dtype, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t num_blocks,
+                            int32_t Hkv, int32_t d, int32_t max_seq_len, float* gram, void* workspace,
+                            size_t ws_bytes, void* hip_stream);
+
 /* z = Phi^-1(1 - delta/2) rounded to fp32, as vattn_decode uses it (host). */
 double vattn_z_from_delta(double delta);
 

@@ -142,6 +142,32 @@ def test_append_kv_argument_checks(lib):
     assert call(ph=3) == 2             # neither one basis nor one per KV head
 
 
+def test_key_gram_argument_checks(lib):
+    P = C.c_void_p
+    ws = lib.vattn_key_gram_workspace_size(2, 4, 128, 10000)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.vattn_key_gram_workspace_size(2, 4, 96, 10000) == 0
+    assert lib.vattn_key_gram_workspace_size(2, 4, 128, (1 << 20) + 1) == 0
+    assert lib.vattn_key_gram_workspace_size(2, 4, 128, 20000) >= ws
+
+    def call(**kw):
+        a = dict(k=P(256), dt=1, bt=P(256), sl=P(256), B=2, mb=700, nb=1400, Hkv=4, d=128, msl=10000,
+                 gram=P(256), ws=P(256), wsb=ws)
+        a.update(kw)
+        return lib.vattn_key_gram(a["k"], a["dt"], a["bt"], a["sl"], a["B"], a["mb"], a["nb"], a["Hkv"], a["d"],
+                                  a["msl"], a["gram"], a["ws"], a["wsb"], None)
+    assert call(k=None) == 1
+    assert call(gram=None) == 1
+    assert call(dt=7) == 3
+    assert call(dt=0) == 6            # fp32 caches: bf16 only
+    assert call(d=96) == 6
+    assert call(B=0) == 2
+    assert call(mb=10) == 2           # block table shorter than max_seq_len
+    assert call(k=P(264)) == 2        # misaligned
+    assert call(ws=None) == 5
+    assert call(wsb=ws - 1) == 5
+
+
 def test_workspace_size_monotone(lib):
     cfg = _cfg()
     prev = 0

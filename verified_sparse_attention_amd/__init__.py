@@ -27,7 +27,8 @@ PRED_EXACT, PRED_LOWRANK = 0, 1
 STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
 EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
-           "vattn_append_kv", "vattn_z_from_delta", "vattn_status_string")
+           "vattn_append_kv", "vattn_key_gram_workspace_size", "vattn_key_gram", "vattn_z_from_delta",
+           "vattn_status_string")
 NUM_STAGES = 7
 STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
 
@@ -87,6 +88,11 @@ def load():
         lib.vattn_append_kv.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                         C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+        lib.vattn_key_gram_workspace_size.restype = C.c_size_t
+        lib.vattn_key_gram_workspace_size.argtypes = [C.c_int32] * 4
+        lib.vattn_key_gram.restype = C.c_int
+        lib.vattn_key_gram.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p] + [C.c_int32] * 6 + \
+            [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         lib.vattn_z_from_delta.restype = C.c_double
         lib.vattn_z_from_delta.argtypes = [C.c_double]
         lib.vattn_status_string.restype = C.c_char_p
@@ -273,6 +279,27 @@ def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, 
                                 _stream_handle(stream))
     if rc != 0:
         raise VattnError(rc, "vattn_append_kv")
+
+
+def key_gram(k_cache, block_table, seq_lens, max_seq_len, stream=None):
+    """Per KV head, the keys' second-moment matrix sum_t K_t K_t^T over every cached
+    token ([Hkv, d, d] fp32 on the device; bf16 caches).  A head's predictor basis
+    can be taken as its r leading eigenvectors."""
+    import torch
+    nb, Hkv, page, d = k_cache.shape
+    B, max_blocks = block_table.shape
+    lib = load()
+    need = int(lib.vattn_key_gram_workspace_size(B, Hkv, d, int(max_seq_len)))
+    if need == 0:
+        raise VattnError(2, "vattn_key_gram_workspace_size")
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=k_cache.device)
+    wp = (ws.data_ptr() + 255) // 256 * 256
+    gram = torch.empty(Hkv, d, d, dtype=torch.float32, device=k_cache.device)
+    rc = lib.vattn_key_gram(_ptr(k_cache), _kv_dtype(k_cache), _ptr(block_table), _ptr(seq_lens), B, max_blocks,
+                            nb, Hkv, d, int(max_seq_len), _ptr(gram), C.c_void_p(wp), need, _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_key_gram")
+    return gram
 
 
 def z_from_delta(delta: float) -> float:

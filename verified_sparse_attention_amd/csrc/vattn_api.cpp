@@ -321,6 +321,32 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 
+size_t vattn_key_gram_workspace_size(int32_t B, int32_t Hkv, int32_t d, int32_t max_seq_len) {
+    if (B < 1 || Hkv < 1 || (d != 64 && d != 128) || max_seq_len < 1 || max_seq_len > VATTN_MAX_SEQ) return 0;
+    const size_t nchunk = (static_cast<size_t>(max_seq_len) + vattn::kGramChunk - 1) / vattn::kGramChunk;
+    return align_up(static_cast<size_t>(B) * Hkv * nchunk * d * d * sizeof(float));
+}
+
+vattn_status vattn_key_gram(const void* k_cache, int32_t kv_dtype, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t num_blocks,
+                            int32_t Hkv, int32_t d, int32_t max_seq_len, float* gram, void* workspace,
+                            size_t ws_bytes, void* hip_stream) {
+    if (!k_cache || !block_table || !seq_lens || !gram) return VATTN_E_NULL;
+    if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (kv_dtype != VATTN_BF16) return VATTN_E_UNSUPPORTED;
+    if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
+    if (B < 1 || Hkv < 1 || num_blocks < 1 || max_blocks < 1) return VATTN_E_SHAPE;
+    if (static_cast<long long>(B) * Hkv > 65535) return VATTN_E_SHAPE;
+    if (max_seq_len < 1 || max_seq_len > VATTN_MAX_SEQ) return VATTN_E_SHAPE;
+    if (static_cast<long long>(max_blocks) * VATTN_PAGE < max_seq_len) return VATTN_E_SHAPE;
+    if (!aligned(k_cache, 16) || !aligned(gram, 4)) return VATTN_E_SHAPE;
+    const size_t need = vattn_key_gram_workspace_size(B, Hkv, d, max_seq_len);
+    if (!workspace || !aligned(workspace, kAlign) || ws_bytes < need) return VATTN_E_WORKSPACE;
+    const int rc = vattn::launch_gram(static_cast<const uint16_t*>(k_cache), block_table, seq_lens, B, max_blocks,
+                                      Hkv, d, max_seq_len, gram, static_cast<float*>(workspace), hip_stream);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
 const char* vattn_status_string(vattn_status s) {
     switch (s) {
         case VATTN_OK: return "VATTN_OK";

@@ -1589,6 +1589,115 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
     return static_cast<int>(hipGetLastError());
 }
 
+// ===========================================================================
+// key Gram matrices: gram[g] = sum over every cached token of K K^T (fp32),
+// from which a caller takes a KV head's predictor basis (its leading
+// eigenvectors).  A dense contraction over tokens, so on the matrix cores:
+// one block per (sequence, KV head, chunk of kGramChunk tokens) stages
+// kGramTile tokens at a time feature-major in LDS and accumulates the d x d
+// product in 16 x 16 tiles; a second pass sums the chunk partials in a fixed
+// order, so the result does not depend on scheduling.
+// ===========================================================================
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_gram_part(const uint16_t* __restrict__ k, const int32_t* __restrict__ bt,
+                                                   const int32_t* __restrict__ seq_lens, int max_blocks, int Hkv,
+                                                   int nchunk, float* __restrict__ part) {
+    constexpr int NT = D / 16;   // 16 x 16 output tiles per side
+    constexpr int RPW = NT / 4;  // tile rows per wave (4 waves)
+    constexpr int RS = kGramTile + 8;  // LDS row stride (elements), 16-byte aligned rows
+    __shared__ __align__(16) __bf16 kf[D * RS];  // [feature][token]
+    const int c = blockIdx.x, bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
+    const int L = min(seq_lens[b], max_blocks * kPage);  // never past the block-table row
+    const int t0 = c * kGramChunk;
+    if (t0 >= L) return;  // block-uniform; the reduction skips this partial
+    const int t1 = min(t0 + kGramChunk, L);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    f32x4_t acc[RPW][NT];
+#pragma unroll
+    for (int ri = 0; ri < RPW; ++ri)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[ri][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int32_t* btrow = bt + static_cast<size_t>(b) * max_blocks;
+    for (int ts = t0; ts < t1; ts += kGramTile) {
+        // 16-byte pieces (8 features of one token) into the feature-major tile;
+        // tokens past the chunk are zero and add nothing
+        constexpr int PIECES = kGramTile * D / 8;
+        for (int x = tid; x < PIECES; x += 256) {
+            const int tt = x / (D / 8), f8 = (x % (D / 8)) * 8, t = ts + tt;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t < t1) {
+                const size_t row = (static_cast<size_t>(btrow[t / kPage]) * Hkv + g) * kPage + (t % kPage);
+                v = *reinterpret_cast<const uint4*>(k + row * D + f8);
+            }
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                kf[(f8 + 2 * q) * RS + tt] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] & 0xFFFFu));
+                kf[(f8 + 2 * q + 1) * RS + tt] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] >> 16));
+            }
+        }
+        __syncthreads();
+        // 32 tokens per step: lane l gives row l % 16 of a tile, tokens
+        // 8 (l / 16) .. + 8 (one 16-byte LDS read per operand)
+        for (int ks = 0; ks < kGramTile; ks += 32) {
+            const int tk = ks + 8 * (lane / 16), fr = lane % 16;
+            bf16x8_t bop[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) bop[j] = *reinterpret_cast<const bf16x8_t*>(&kf[(16 * j + fr) * RS + tk]);
+#pragma unroll
+            for (int ri = 0; ri < RPW; ++ri) {
+                const int i = wave * RPW + ri;
+                const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(&kf[(16 * i + fr) * RS + tk]);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[ri][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[j], acc[ri][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // the tile is restaged
+    }
+    // tile (i, j): lane l holds rows 16 i + 4 (l / 16) + r, column 16 j + l % 16
+    float* out = part + (static_cast<size_t>(bg) * nchunk + c) * D * D;
+#pragma unroll
+    for (int ri = 0; ri < RPW; ++ri)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                out[(16 * (wave * RPW + ri) + 4 * (lane / 16) + r) * D + 16 * j + lane % 16] = acc[ri][j][r];
+}
+
+// gram[g][e] = sum over sequences b, then chunks c (ascending) of the partials
+__global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ part, const int32_t* __restrict__ seq_lens,
+                                                     int B, int Hkv, int nchunk, int DD, float* __restrict__ gram) {
+    const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y;
+    if (e >= DD) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) {
+        const int nc = min((seq_lens[b] + kGramChunk - 1) / kGramChunk, nchunk);
+        const float* pp = part + (static_cast<size_t>(b) * Hkv + g) * nchunk * DD + e;
+        for (int c = 0; c < nc; ++c) s += pp[static_cast<size_t>(c) * DD];
+    }
+    gram[static_cast<size_t>(g) * DD + e] = s;
+}
+
+int launch_gram(const uint16_t* k_cache, const int32_t* bt, const int32_t* seq_lens, int B, int max_blocks,
+                int Hkv, int d, int max_seq_len, float* gram, float* part, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int nchunk = (max_seq_len + kGramChunk - 1) / kGramChunk;
+    const dim3 grid(static_cast<unsigned>(nchunk), static_cast<unsigned>(B * Hkv));
+    if (d == 128)
+        hipLaunchKernelGGL(k_gram_part<128>, grid, dim3(256), 0, st, k_cache, bt, seq_lens, max_blocks, Hkv, nchunk, part);
+    else
+        hipLaunchKernelGGL(k_gram_part<64>, grid, dim3(256), 0, st, k_cache, bt, seq_lens, max_blocks, Hkv, nchunk, part);
+    const int DD = d * d;
+    hipLaunchKernelGGL(k_gram_reduce, dim3(static_cast<unsigned>((DD + 255) / 256), static_cast<unsigned>(Hkv)),
+                       dim3(256), 0, st, part, seq_lens, B, Hkv, nchunk, DD, gram);
+    return static_cast<int>(hipGetLastError());
+}
+
 template <typename KVT, int D>
 static void launch_project_t(const void* k, const float* proj, uint16_t* kt, long long nrows, int r,
                              int Hkv, int proj_stride, hipStream_t st) {

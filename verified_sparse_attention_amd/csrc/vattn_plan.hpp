@@ -24,6 +24,8 @@ constexpr int kPremergeMaxHeads = 128;  // pre-merge when B*Hq is below this ...
 constexpr int kPremergeMinChunks = 16;  // ... and there are at least this many predictor chunks
 constexpr int kGatherChunk = 4 * kChunkThreads;  // tokens per base/gather block
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kGramChunk = 4096;     // tokens per partial of the key Gram matrices
+constexpr int kGramTile = 128;       // tokens staged in LDS at a time
 #define VATTN_MAX_SEQ_TOKENS (1 << 20)
 
 // Per (sequence, query head) state handed from kernel to kernel.
@@ -93,6 +95,8 @@ int launch_decode(const Plan& p, void* stream, void* const* events = nullptr);
 int launch_project(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint16_t* kt,
                    int num_blocks, int Hkv, int d, int r, void* stream);
 size_t predict_lds_bytes(int G, int d, int row, int cp);
+int launch_gram(const uint16_t* k_cache, const int32_t* bt, const int32_t* seq_lens, int B, int max_blocks,
+                int Hkv, int d, int max_seq_len, float* gram, float* part, void* stream);
 int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
                   int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int proj_stride,
                   int kv_bf16, int Hkv, int d, int r, void* stream);
