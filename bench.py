@@ -253,6 +253,31 @@ def main():
                                 "note": "one new token per sequence: K, V and its low-rank key row"}
         log("append %.2f us per call" % app_us)
 
+    # ---- calibration, not part of the decode step: the keys' Gram matrices per
+    # KV head (the second moments a per-head predictor basis is taken from), a
+    # dense contraction over every cached token on the matrix cores
+    if k0.dtype == torch.bfloat16 and not args.profile:
+        gram = vsa.key_gram(k0, bt, sl, w.max_seq_len)
+        gws = torch.empty(int(vsa.load().vattn_key_gram_workspace_size(w.B, w.Hkv, d, w.max_seq_len)) + 256,
+                          dtype=torch.uint8, device=dev)
+        vsa.key_gram(k0, bt, sl, w.max_seq_len, gram=gram, workspace=gws)
+        torch.cuda.synchronize()
+        n_g = 20
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(n_g):
+            vsa.key_gram(k0, bt, sl, w.max_seq_len, gram=gram, workspace=gws)
+        g1.record()
+        torch.cuda.synchronize()
+        g_us = g0.elapsed_time(g1) / n_g * 1e3
+        tokens = int(w.seq_lens.sum())
+        g_bytes = tokens * w.Hkv * d * esize
+        g_flops = 2 * tokens * w.Hkv * d * d
+        result["key_gram"] = {"us": round(g_us, 1), "bytes": g_bytes, "GBps": round(g_bytes / g_us / 1e3, 1),
+                              "TFLOPs": round(g_flops / g_us / 1e6, 1),
+                              "note": "calibration of per-KV-head predictor bases, not part of the decode step"}
+        log("key gram %.1f us (%.0f GB/s)" % (g_us, g_bytes / g_us / 1e3))
+
     if args.host_kv and not args.profile:
         # ---- host-resident K/V: the caches in pinned, device-mapped host memory,
         # read by the kernels over the host link (the low-rank keys and the

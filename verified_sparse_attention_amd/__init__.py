@@ -281,10 +281,11 @@ def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, 
         raise VattnError(rc, "vattn_append_kv")
 
 
-def key_gram(k_cache, block_table, seq_lens, max_seq_len, stream=None):
+def key_gram(k_cache, block_table, seq_lens, max_seq_len, gram=None, workspace=None, stream=None):
     """Per KV head, the keys' second-moment matrix sum_t K_t K_t^T over every cached
     token ([Hkv, d, d] fp32 on the device; bf16 caches).  A head's predictor basis
-    can be taken as its r leading eigenvectors."""
+    can be taken as its r leading eigenvectors.  gram and workspace (uint8) may be
+    passed in to reuse them."""
     import torch
     nb, Hkv, page, d = k_cache.shape
     B, max_blocks = block_table.shape
@@ -292,9 +293,13 @@ def key_gram(k_cache, block_table, seq_lens, max_seq_len, stream=None):
     need = int(lib.vattn_key_gram_workspace_size(B, Hkv, d, int(max_seq_len)))
     if need == 0:
         raise VattnError(2, "vattn_key_gram_workspace_size")
-    ws = torch.empty(need + 256, dtype=torch.uint8, device=k_cache.device)
-    wp = (ws.data_ptr() + 255) // 256 * 256
-    gram = torch.empty(Hkv, d, d, dtype=torch.float32, device=k_cache.device)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=k_cache.device)
+    wp = (workspace.data_ptr() + 255) // 256 * 256
+    if workspace.numel() - (wp - workspace.data_ptr()) < need:
+        raise ValueError("workspace too small: need %d bytes" % need)
+    if gram is None:
+        gram = torch.empty(Hkv, d, d, dtype=torch.float32, device=k_cache.device)
     rc = lib.vattn_key_gram(_ptr(k_cache), _kv_dtype(k_cache), _ptr(block_table), _ptr(seq_lens), B, max_blocks,
                             nb, Hkv, d, int(max_seq_len), _ptr(gram), C.c_void_p(wp), need, _stream_handle(stream))
     if rc != 0:

@@ -1609,6 +1609,7 @@ __global__ __launch_bounds__(256) void k_gram_part(const uint16_t* __restrict__ 
     constexpr int RPW = NT / 4;  // tile rows per wave (4 waves)
     constexpr int RS = kGramTile + 8;  // LDS row stride (elements), 16-byte aligned rows
     __shared__ __align__(16) __bf16 kf[D * RS];  // [feature][token]
+    __shared__ int32_t pgs[kGramChunk / kPage];  // the chunk's page ids
     const int c = blockIdx.x, bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
     const int L = min(seq_lens[b], max_blocks * kPage);  // never past the block-table row
     const int t0 = c * kGramChunk;
@@ -1621,25 +1622,51 @@ __global__ __launch_bounds__(256) void k_gram_part(const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[ri][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int32_t* btrow = bt + static_cast<size_t>(b) * max_blocks;
-    for (int ts = t0; ts < t1; ts += kGramTile) {
-        // 16-byte pieces (8 features of one token) into the feature-major tile;
-        // tokens past the chunk are zero and add nothing
-        constexpr int PIECES = kGramTile * D / 8;
-        for (int x = tid; x < PIECES; x += 256) {
-            const int tt = x / (D / 8), f8 = (x % (D / 8)) * 8, t = ts + tt;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t < t1) {
-                const size_t row = (static_cast<size_t>(btrow[t / kPage]) * Hkv + g) * kPage + (t % kPage);
-                v = *reinterpret_cast<const uint4*>(k + row * D + f8);
-            }
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int x = tid; x < kGramChunk / kPage; x += 256)
+        if (t0 + x * kPage < t1) pgs[x] = btrow[t0 / kPage + x];
+    __syncthreads();
+    // staging: a thread takes 4 consecutive tokens x 8 features (four 16-byte
+    // row pieces) per pair and writes each feature's 4 tokens as one 8-byte
+    // word; the next tile's pieces are requested before the current tile's
+    // products, so the loads overlap the matrix work
+    constexpr int OCT = D / 8;                          // feature octets per token
+    constexpr int PAIRS = (kGramTile / 4) * OCT / 256;  // (token quad, octet) pairs per thread
+    static_assert(PAIRS >= 1 && (kGramTile / 4) * OCT % 256 == 0, "whole pairs per thread");
+    uint4 pre[PAIRS][4];
+    auto fetch = [&](int ts) __attribute__((always_inline)) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                kf[(f8 + 2 * q) * RS + tt] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] & 0xFFFFu));
-                kf[(f8 + 2 * q + 1) * RS + tt] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] >> 16));
+        for (int pi = 0; pi < PAIRS; ++pi) {
+            const int pr = tid + 256 * pi, tq = pr / OCT, fo = pr % OCT;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = ts + 4 * tq + u;
+                pre[pi][u] = make_uint4(0, 0, 0, 0);
+                if (t < t1) {
+                    const size_t row = (static_cast<size_t>(pgs[(t - t0) / kPage]) * Hkv + g) * kPage + (t % kPage);
+                    pre[pi][u] = *reinterpret_cast<const uint4*>(k + row * D + 8 * fo);
+                }
+            }
+        }
+    };
+    fetch(t0);
+    for (int ts = t0; ts < t1; ts += kGramTile) {
+#pragma unroll
+        for (int pi = 0; pi < PAIRS; ++pi) {
+            const int pr = tid + 256 * pi, tq = pr / OCT, fo = pr % OCT;
+            const uint32_t w[4][4] = {{pre[pi][0].x, pre[pi][0].y, pre[pi][0].z, pre[pi][0].w},
+                                      {pre[pi][1].x, pre[pi][1].y, pre[pi][1].z, pre[pi][1].w},
+                                      {pre[pi][2].x, pre[pi][2].y, pre[pi][2].z, pre[pi][2].w},
+                                      {pre[pi][3].x, pre[pi][3].y, pre[pi][3].z, pre[pi][3].w}};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {  // feature 8 fo + q of tokens 4 tq .. 4 tq + 3
+                const int sh = 16 * (q & 1);
+                const uint32_t lo = ((w[0][q >> 1] >> sh) & 0xFFFFu) | (((w[1][q >> 1] >> sh) & 0xFFFFu) << 16);
+                const uint32_t hi = ((w[2][q >> 1] >> sh) & 0xFFFFu) | (((w[3][q >> 1] >> sh) & 0xFFFFu) << 16);
+                *reinterpret_cast<uint2*>(&kf[(8 * fo + q) * RS + 4 * tq]) = make_uint2(lo, hi);
             }
         }
         __syncthreads();
+        if (ts + kGramTile < t1) fetch(ts + kGramTile);  // block-uniform
         // 32 tokens per step: lane l gives row l % 16 of a tile, tokens
         // 8 (l / 16) .. + 8 (one 16-byte LDS read per operand)
         for (int ks = 0; ks < kGramTile; ks += 32) {
