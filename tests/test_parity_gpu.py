@@ -484,3 +484,48 @@ def test_pca_bases_from_the_gram():
     ov_rand = overlap(w.proj.numpy())
     log("   top-k overlap with exact scores: pca %.3f, random %.3f" % (ov_pca, ov_rand))
     assert ov_pca > 0.7 and ov_pca > ov_rand + 0.3  # measured on the CPU: 0.81 against 0.19
+
+
+def test_graph_replay():
+    """A decode captured in a HIP graph (no allocation, no memset inside) and
+    replayed with new queries written into the same buffer gives, on every
+    replay, exactly the eager result for those queries.  The configuration,
+    seed included, is part of the captured launch."""
+    import torch
+    GpuCase, log = _gpu()
+    log("[parity] graph replay")
+    case = GpuCase(SMALL_CASES["gqa4_bf16_ragged"]())
+    gen = torch.Generator().manual_seed(77)
+    qs = [torch.randn(case.q.shape, generator=gen).cuda() for _ in range(3)]
+    keys = ("idx", "counts", "stats", "out", "lse")
+
+    def outputs():
+        d = case.dec
+        return dict(out=d.out.cpu().numpy(), lse=d.lse.cpu().numpy(), counts=d.counts.cpu().numpy(),
+                    idx=d.idx.cpu().numpy(), stats=d.stats.cpu().numpy().view(np.uint64))
+    eager = []
+    for qn in qs:
+        case.q.copy_(qn)
+        case.run(11)
+        eager.append(outputs())
+    case.q.copy_(qs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        case.dec()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        case.dec()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, qn in enumerate(qs):
+            case.q.copy_(qn)
+            graph.replay()
+            torch.cuda.synchronize()
+            got = outputs()
+            for key in keys:
+                assert np.array_equal(got[key], eager[i][key]), (rep, i, key)
+            case.q.copy_(qs[(i + 1) % len(qs)])  # eager work between the replays
+            case.run(11)
