@@ -107,6 +107,11 @@ SMALL_CASES = {
         name="per_head_bases", B=2, Hq=16, Hkv=4, d=128, seq_lens=(5000, 2100), kv_dtype="bf16",
         recipe="outlier", predictor=1, rank=32, sinks=32, window=64, topk_ppm=25000,
         proj_per_head=True, data_seed=20),
+    # per-head bases with G = 8 and the pre-merge (one 40K sequence, 16 heads)
+    "per_head_g8_premerge": lambda: synthetic.make(
+        name="per_head_g8_premerge", B=1, Hq=16, Hkv=2, d=128, seq_lens=(40000,), kv_dtype="bf16",
+        recipe="lowrank", predictor=1, rank=32, sinks=64, window=64, topk_ppm=20000,
+        proj_per_head=True, data_seed=21),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
