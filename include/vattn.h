@@ -10,7 +10,8 @@
  *      + the k best tokens of the middle by a predictor score.  The predictor
  *      is either exact scaled scores ("oracle top-k", same post, section
  *      "Performance and Efficiency") or scores in a rank-r key space (pith.science
- *      page "Loki: Low-rank Keys for Efficient Sparse Attention", abstract);
+ *      page "Loki: Low-rank Keys for Efficient Sparse Attention", abstract),
+ *      one basis for all heads or one per KV head;
  *   2. a uniform sample without replacement of the remaining tail, of N_t tokens.
  *      A base sample of n_b tokens estimates the spread of exp(s - m) over the
  *      tail.  The final size n is the central-limit budget
@@ -23,9 +24,8 @@
  *      sample; lse = log sum_i w_i e^{s_i}.  Scores s_i = q . K_i / sqrt(d).
  *
  * Conventions for every entry point:
- *  - Device pointers are caller-owned.  The library allocates no device or host
- *    memory in vattn_decode / vattn_project_keys; scratch space is the caller's
- *    workspace.
+ *  - Device pointers are caller-owned.  No entry point allocates device or host
+ *    memory; scratch space is the caller's workspace.
  *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL means
  *    the null stream).  No entry point synchronizes.
  *  - Errors are returned as vattn_status; nothing aborts or throws across the
