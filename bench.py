@@ -355,6 +355,53 @@ def main():
                                    "delta": w.cfg["delta"], "reference": "dense fp32 scores, fp64 logsumexp"}
         log("eps violations %d / %d" % (viol, trials))
 
+        # ---- the same workload with a per-KV-head PCA predictor basis (the r
+        # leading eigenvectors of each head's key Gram matrix over the first half
+        # of every sequence, as a basis fitted at prefill; host eigensolve):
+        # step time, union density and the (eps, delta) rate.  Context only; the
+        # headline value above uses the workload's random basis.
+        if kt0 is not None and k0.dtype == torch.bfloat16:
+            gram = vsa.key_gram(k0, bt, (sl // 2).contiguous(), w.max_seq_len)
+            _, evec = torch.linalg.eigh(gram.double().cpu())
+            p_pca = evec[:, :, -r:].flip(-1).float().contiguous().to(dev)  # [Hkv, d, r], descending
+            pca_decs = []
+            for (k, v, _) in inst:
+                pca_decs.append(vsa.Decoder(q, k, v, bt, sl, vsa.Config.from_dict(w.cfg), max_seq_len=w.max_seq_len,
+                                         k_lowrank=vsa.project_keys(k, p_pca), proj=p_pca,
+                                         want_group_counts=True, workspace=ws))
+            for s in range(warm):
+                pca_decs[s % n_inst].set_seed(20_000 + s)
+                pca_decs[s % n_inst]()
+            torch.cuda.synchronize()
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record()
+            for s in range(steps):
+                pca_decs[s % n_inst].set_seed(30_000 + s)
+                pca_decs[s % n_inst]()
+            p1.record()
+            torch.cuda.synchronize()
+            pca_ms = p0.elapsed_time(p1) / steps
+            pv = pt = 0
+            pd = pca_decs[0]
+            for s in range(args.rate_seeds):
+                pd.set_seed(1_000_000 + s)
+                pd()
+                rel = (torch.exp(pd.lse.double() - lse_dense) - 1.0).abs()
+                pv += int((rel > w.cfg["eps"]).sum())
+                pt += rel.numel()
+            torch.cuda.synchronize()
+            Up = pd.group_counts[:, :, 0].double().cpu().numpy()
+            result["pca_basis"] = {
+                "ms_per_step": round(pca_ms, 5), "value": round(heads_tokens / (pca_ms * 1e-3), 1),
+                "unit": "heads·tokens/s", "union_density": round(float((Up / L).mean()), 4),
+                "eps_violation": {"rate": round(pv / pt, 5), "violations": pv, "trials": pt,
+                                  "seeds": args.rate_seeds, "delta": w.cfg["delta"]},
+                "note": "same workload with a per-KV-head basis: the %d leading eigenvectors of vattn_key_gram "
+                        "over the first half of each sequence (a Loki-style basis fitted at prefill)" % r}
+            log("pca basis: %.4f ms/step, union density %.3f, eps violations %d / %d"
+                % (pca_ms, float((Up / L).mean()), pv, pt))
+            del pca_decs
+
     if not args.profile and not args.no_cpu_baseline:
         import oracle
         cores = min(len(os.sched_getaffinity(0)), 16)
