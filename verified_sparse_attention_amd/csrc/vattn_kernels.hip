@@ -1249,13 +1249,16 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 // ===========================================================================
 // combine: merge chunk partials; counts and statistics
 // ===========================================================================
-constexpr int kCombineThreads = 256;
+// 1024 threads: the weighted sum over chunks takes one round of loads per
+// thread for up to 64 chunks at d = 128 (8 groups of chunks per dimension)
+constexpr int kCombineThreads = 1024;
 
-__global__ __launch_bounds__(kCombineThreads) void k_combine(Plan P) {
-    constexpr int NW = kCombineThreads / 64;
+template <int kThreads>  // per block
+__global__ __launch_bounds__(kThreads) void k_combine(Plan P) {
+    constexpr int NW = kThreads / 64;
     __shared__ float wsh[kMaxChunks];
     __shared__ float rm[NW], rl[NW];
-    __shared__ float accs[kCombineThreads];
+    __shared__ float accs[kThreads];
     const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq;
     const int L = P.seq_lens[b];
@@ -1577,7 +1580,10 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
         default: rc = launch_g<8>(p, st, mk); break;
     }
     if (rc) return rc;
-    hipLaunchKernelGGL(k_combine, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
+    if (p.B * p.Hq >= kManyHeads)
+        hipLaunchKernelGGL(k_combine<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+    else
+        hipLaunchKernelGGL(k_combine<kCombineThreads>, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
     if ((rc = mk.mark(6))) return rc;
     if (p.idx) {
         if (p.B * p.Hq >= kManyHeads)

@@ -10,7 +10,7 @@ constexpr int kPredThreads = 1024;   // predictor + chunk top-k
 constexpr int kSelectThreads = 1024; // per-head exact top-k and base threshold
 constexpr int kBudgetThreads = 1024;  // per-head statistics, budget and final threshold
 constexpr int kManyHeads = 1024;     // from this many query heads (B * Hq) on, the per-head
-constexpr int kHeadThreadsMany = 256; // select, budget and emit run 256-thread blocks, several per CU
+constexpr int kHeadThreadsMany = 256; // select, budget, combine and emit run 256-thread blocks, several per CU
 constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
 constexpr int kEmitQuads = 8;       // token quads per lane and pass of the index-set emission
