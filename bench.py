@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-kv", action="store_true",
                     help="also time the step with K/V in pinned host memory (adds a host_kv object)")
+    ap.add_argument("--pca-basis", action="store_true",
+                    help="also time and rate-check the workload with per-KV-head PCA predictor bases "
+                         "(adds a pca_basis object; its decodes would otherwise mix into a kernel-trace profile)")
     return ap.parse_args()
 
 
@@ -360,7 +363,7 @@ def main():
         # of every sequence, as a basis fitted at prefill; host eigensolve):
         # step time, union density and the (eps, delta) rate.  Context only; the
         # headline value above uses the workload's random basis.
-        if kt0 is not None and k0.dtype == torch.bfloat16:
+        if args.pca_basis and kt0 is not None and k0.dtype == torch.bfloat16:
             gram = vsa.key_gram(k0, bt, (sl // 2).contiguous(), w.max_seq_len)
             _, evec = torch.linalg.eigh(gram.double().cpu())
             p_pca = evec[:, :, -r:].flip(-1).float().contiguous().to(dev)  # [Hkv, d, r], descending
