@@ -112,6 +112,21 @@ SMALL_CASES = {
         name="per_head_g8_premerge", B=1, Hq=16, Hkv=2, d=128, seq_lens=(40000,), kv_dtype="bf16",
         recipe="lowrank", predictor=1, rank=32, sinks=64, window=64, topk_ppm=20000,
         proj_per_head=True, data_seed=21),
+    # kernel instances the cases above leave out: d = 64 with bf16 and G = 8,
+    # fp32 at d = 128 with G = 8 (exact predictor) and G = 4 (low rank), and a
+    # rank equal to the head dim
+    "d64_bf16_g8": lambda: synthetic.make(
+        name="d64_bf16_g8", B=2, Hq=16, Hkv=2, d=64, seq_lens=(3000, 1700), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=16, sinks=16, window=32, topk_ppm=25000, data_seed=22),
+    "d128_f32_g8_exact": lambda: synthetic.make(
+        name="d128_f32_g8_exact", B=1, Hq=8, Hkv=1, d=128, seq_lens=(2500,), kv_dtype="f32",
+        recipe="planted", predictor=0, sinks=8, window=16, topk_abs=50, data_seed=23),
+    "d128_f32_g4_lowrank": lambda: synthetic.make(
+        name="d128_f32_g4_lowrank", B=2, Hq=8, Hkv=2, d=128, seq_lens=(3100, 900), kv_dtype="f32",
+        recipe="outlier", predictor=1, rank=32, sinks=16, window=16, topk_ppm=25000, data_seed=24),
+    "d64_bf16_rank_eq_d": lambda: synthetic.make(
+        name="d64_bf16_rank_eq_d", B=1, Hq=2, Hkv=2, d=64, seq_lens=(4000,), kv_dtype="bf16",
+        recipe="normal", predictor=1, rank=64, sinks=8, window=8, topk_ppm=20000, data_seed=25),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
