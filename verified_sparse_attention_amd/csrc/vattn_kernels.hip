@@ -1522,12 +1522,16 @@ template <int ROW, typename T, int G>
 static int launch_predict(const Plan& p, hipStream_t st) {
     const size_t lds = predict_lds_bytes(G, p.d, ROW, p.cp);
     auto kern = k_predict<ROW, T, G>;
-    static bool attr_set = false;  // per kernel instance; the limit never changes
-    if (!attr_set) {
+    // the dynamic LDS limit is raised once per kernel instance and device
+    constexpr int kDevices = 64;
+    static bool attr_set[kDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev >= kDevices || !attr_set[dev]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         if (e != hipSuccess) return static_cast<int>(e);
-        attr_set = true;
+        if (dev < kDevices) attr_set[dev] = true;
     }
     hipLaunchKernelGGL(kern, dim3(p.ncp, p.B * p.Hkv), dim3(kPredThreads), lds, st, p);
     return 0;
