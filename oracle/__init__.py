@@ -75,6 +75,8 @@ def _load():
             lib.orc_token_key.argtypes = [C.c_uint64, C.c_int, C.c_int, C.c_int]
             lib.orc_project_rows.restype = None
             lib.orc_project_rows.argtypes = [P, C.c_int64, C.c_int, P, C.c_int, P]
+            lib.orc_sign_rows.restype = None
+            lib.orc_sign_rows.argtypes = [P, C.c_int64, C.c_int, P, P]
             _lib = lib
     return _lib
 
@@ -136,6 +138,17 @@ def project_rows(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
     return out
 
 
+def sign_rows(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """Key signatures: bit j set when pdot(K_i, P[:, j]) > 0, P of shape [d, 32]."""
+    k_rows = np.ascontiguousarray(k_rows, dtype=np.float32)
+    proj = np.ascontiguousarray(proj, dtype=np.float32)
+    n, d = k_rows.shape
+    assert proj.shape == (d, 32)
+    out = np.zeros(n, dtype=np.uint32)
+    _load().orc_sign_rows(_ptr(k_rows), n, d, _ptr(proj), _ptr(out))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
@@ -147,10 +160,10 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
 
     q: [B,Hq,d] float32.  k_cache/v_cache: [num_blocks,Hkv,16,d] float32, or
     uint16 holding bf16 bit patterns.  block_table [B,max_blocks] int32,
-    seq_lens [B] int32, proj [d,r] float32 (low-rank predictor; or [Hkv,d,r], one basis per
-    KV head) or None.
+    seq_lens [B] int32, proj [d,r] float32 (low-rank or signature predictor; or [Hkv,d,r],
+    one basis per KV head) or None.
     cfg keys: sinks, window, topk_abs, topk_ppm, base_ppm, force_budget,
-    predictor (0 exact, 1 low-rank), rank, eps, delta, seed.
+    predictor (0 exact, 1 low-rank, 2 32-bit signatures with rank 32), rank, eps, delta, seed.
     groups: iterable of (b, g) to evaluate (default all).  Returns a dict of
     numpy arrays (rows of groups not evaluated are zero / -1).
     """

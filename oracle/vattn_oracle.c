@@ -16,8 +16,11 @@
  * The sampled tail is weighted by the inverse sampling probability.
  * The top-k predictor ranks tokens with attention scores computed in a
  * low-dimensional key space (pith.science page "Loki: Low-rank Keys for
- * Efficient Sparse Attention", abstract), or with exact scores ("oracle top-k",
- * same blog post, section "Performance and Efficiency").
+ * Efficient Sparse Attention", abstract), with exact scores ("oracle top-k",
+ * same blog post, section "Performance and Efficiency"), or by hash
+ * signatures (HashAttention, named as a top-k method in the same section):
+ * here 32 random-hyperplane sign bits of the projected query and key
+ * (Charikar's SimHash, untrained), scored by the number of equal bits.
  *
  * The pages fix no arithmetic order.  Every floating-point quantity that
  * decides a discrete outcome (which tokens are top-k, the budget) is defined
@@ -49,8 +52,8 @@ typedef struct {
     int32_t topk_ppm;     /* k = ceil(L * ppm / 1e6)                        */
     int32_t base_ppm;     /* base sample = ceil(N_tail * ppm / 1e6), >= 2   */
     int32_t force_budget; /* < 0: CLT budget; >= 0: fixed n = min(N_t, .)   */
-    int32_t predictor;    /* 0 exact scores, 1 low-rank keys               */
-    int32_t rank;         /* r, low-rank width                             */
+    int32_t predictor;    /* 0 exact scores, 1 low-rank keys, 2 signatures */
+    int32_t rank;         /* r, low-rank width (32 signature bits for 2)   */
     double eps, delta;    /* accuracy target, failure probability          */
     double z32;           /* Phi^-1(1 - delta/2) rounded to fp32 (caller)  */
     uint64_t seed;        /* Philox key                                    */
@@ -198,6 +201,26 @@ void orc_project_rows(const float* k_rows, int64_t nrows, int d, const float* pr
 }
 
 /* ------------------------------------------------------------------ */
+/* Key signatures: bit j of S_i is set when pdot(K_i, P[:, j], d) > 0, */
+/* for the 32 columns of P ([d][32]).                                  */
+/* ------------------------------------------------------------------ */
+void orc_sign_rows(const float* k_rows, int64_t nrows, int d, const float* proj, uint32_t* out) {
+    for (int64_t i = 0; i < nrows; ++i) {
+        uint32_t w = 0;
+        for (int j = 0; j < 32; ++j)
+            if (orc_pdot(k_rows + i * d, 1, proj + j, 32, d) > 0.0f) w |= 1u << j;
+        out[i] = w;
+    }
+}
+
+/* Bits set in a word, one at a time. */
+static int orc_popcount(uint32_t w) {
+    int c = 0;
+    for (; w; w >>= 1) c += (int)(w & 1u);
+    return c;
+}
+
+/* ------------------------------------------------------------------ */
 /* Decode                                                               */
 /* ------------------------------------------------------------------ */
 typedef struct {
@@ -289,7 +312,8 @@ static void attend_fp64(const float* q, const float* K, const float* V, int d, c
 
 /* One query head h of sequence b (KV head g), given the group's rows. */
 static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const float* K,
-                        const float* V, const float* Kt /* [L][r] fp32 or NULL */) {
+                        const float* V, const float* Kt /* [L][r] fp32 or NULL */,
+                        const uint32_t* Ks /* [L] key signatures or NULL */) {
     const orc_cfg* cfg = cx->cfg;
     const int d = cx->d, r = cfg->rank;
     const int64_t bh = (int64_t)b * cx->Hq + h;
@@ -341,16 +365,23 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
 
     /* predictor scores over the middle */
     float* qt = NULL;
-    if (cfg->predictor == 1) {
+    uint32_t qsig = 0;
+    if (cfg->predictor == 1 || cfg->predictor == 2) {
         qt = (float*)malloc(sizeof(float) * r);
         const float* P = cx->proj + (size_t)(cx->proj_heads > 1 ? g : 0) * d * r;  /* the group's basis */
         for (int j = 0; j < r; ++j) qt[j] = orc_pdot(qs, 1, P + j, r, d);
+        /* the query's signature: the same sign test on its projection */
+        if (cfg->predictor == 2)
+            for (int j = 0; j < 32; ++j)
+                if (qt[j] > 0.0f) qsig |= 1u << j;
     }
     orc_item* items = (orc_item*)malloc(sizeof(orc_item) * (nM > 0 ? nM : 1));
     for (int t = 0; t < nM; ++t) {
         int i = m_lo + t;
-        float s = cfg->predictor == 1 ? orc_pdot(qt, 1, Kt + (int64_t)i * r, 1, r)
-                                      : orc_pdot(qs, 1, K + (int64_t)i * d, 1, d);
+        float s;
+        if (cfg->predictor == 1) s = orc_pdot(qt, 1, Kt + (int64_t)i * r, 1, r);
+        else if (cfg->predictor == 2) s = (float)(32 - orc_popcount(qsig ^ Ks[i]));  /* equal bits */
+        else s = orc_pdot(qs, 1, K + (int64_t)i * d, 1, d);
         if (cx->pred_scores) cx->pred_scores[bh * cx->max_seq_len + i] = s;
         /* descending score == ascending complement of the order key */
         items[t].k = (uint64_t)(~orc_okey(s));
@@ -477,8 +508,13 @@ static void decode_group(const orc_ctx* cx, int b, int g) {
         for (int64_t t = 0; t < (int64_t)L * r; ++t) Kt[t] = bf16_to_f32(kt16[t]);
         free(kt16);
     }
-    for (int hl = 0; hl < G; ++hl) decode_head(cx, b, g * G + hl, g, L, K, V, Kt);
-    free(K); free(V); free(Kt);
+    uint32_t* Ks = NULL;
+    if (cx->cfg->predictor == 2 && L > 0) {
+        Ks = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)L);
+        orc_sign_rows(K, L, d, cx->proj + (size_t)(cx->proj_heads > 1 ? g : 0) * d * 32, Ks);
+    }
+    for (int hl = 0; hl < G; ++hl) decode_head(cx, b, g * G + hl, g, L, K, V, Kt, Ks);
+    free(K); free(V); free(Kt); free(Ks);
 }
 
 /*
@@ -495,6 +531,8 @@ int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks
     if (!cfg || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse) return 1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d % 8 != 0 || d > 512) return 2;
     if (cfg->predictor == 1 && (!proj || cfg->rank % 8 != 0 || cfg->rank > d)) return 3;
+    if (cfg->predictor == 2 && (!proj || cfg->rank != 32 || cfg->rank > d)) return 3;
+    if (cfg->predictor < 0 || cfg->predictor > 2) return 3;
     if (proj_heads != 1 && proj_heads != Hkv) return 3;
     if (idx && idx_cap < max_seq_len) return 4;
     orc_init_constants();

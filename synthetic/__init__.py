@@ -156,6 +156,7 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
     if recipe == "outlier":
         outlier_idx = torch.stack([torch.randperm(d, generator=gen)[:outlier_channels]
                                    for _ in range(Hkv)])
+    assert predictor != 2 or rank == 32, "signatures have 32 bits"
     hidden_proj = None
     if recipe == "hidden":
         assert predictor == 1
@@ -228,13 +229,15 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
     v_cache = _to_paged(rows_v, bt, seq_lens, num_blocks, dt)
     if hidden_proj is not None:
         proj = hidden_proj
-    elif predictor == 1 and proj_per_head:  # a seeded orthonormal basis for every KV head
+    elif predictor in (1, 2) and proj_per_head:  # a seeded orthonormal basis for every KV head
         proj = torch.stack([orthonormal(d, rank, gen) for _ in range(Hkv)])
     else:
-        proj = orthonormal(d, rank, gen) if predictor == 1 else None
+        # predictor 2: the 32 hyperplanes of the signatures (random directions,
+        # taken orthonormal like the low-rank basis)
+        proj = orthonormal(d, rank, gen) if predictor in (1, 2) else None
     cfg = dict(sinks=sinks, window=window, topk_abs=topk_abs, topk_ppm=topk_ppm,
                base_ppm=base_ppm, force_budget=force_budget, predictor=predictor,
-               rank=rank if predictor == 1 else 0, eps=eps, delta=delta, seed=seed)
+               rank=rank if predictor in (1, 2) else 0, eps=eps, delta=delta, seed=seed)
     return Workload(name=name, q=q.contiguous(), k_cache=k_cache, v_cache=v_cache,
                     block_table=bt, seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                     proj=proj, cfg=cfg, max_seq_len=msl, meta=dict(kinds=kinds, recipe=recipe, plants=plants))
