@@ -9,9 +9,10 @@
  *      + sliding window (last `window` tokens, the newest included)
  *      + the k best tokens of the middle by a predictor score.  The predictor
  *      is either exact scaled scores ("oracle top-k", same post, section
- *      "Performance and Efficiency") or scores in a rank-r key space (pith.science
+ *      "Performance and Efficiency"), scores in a rank-r key space (pith.science
  *      page "Loki: Low-rank Keys for Efficient Sparse Attention", abstract),
- *      one basis for all heads or one per KV head;
+ *      one basis for all heads or one per KV head, or the shared bits of
+ *      32-bit hash signatures (HashAttention-style, same post and section);
  *   2. a uniform sample without replacement of the remaining tail, of N_t tokens.
  *      A base sample of n_b tokens estimates the spread of exp(s - m) over the
  *      tail.  The final size n is the central-limit budget
@@ -65,8 +66,10 @@ typedef enum {
 typedef enum { VATTN_F32 = 0, VATTN_BF16 = 1 } vattn_dtype;
 
 typedef enum {
-    VATTN_PRED_EXACT = 0,  /* top-k on exact scores q_s . K_i (reads K)          */
-    VATTN_PRED_LOWRANK = 1 /* top-k on (q_s P) . Kt_i with Kt = bf16(K P) (reads Kt) */
+    VATTN_PRED_EXACT = 0,   /* top-k on exact scores q_s . K_i (reads K)          */
+    VATTN_PRED_LOWRANK = 1, /* top-k on (q_s P) . Kt_i with Kt = bf16(K P) (reads Kt) */
+    VATTN_PRED_HASH = 2     /* top-k on the bits shared by 32-bit signatures of q_s */
+                            /* and K_i (reads k_sig, 4 bytes per token)            */
 } vattn_predictor;
 
 /* Decode configuration (host struct, read once per call). */
@@ -79,7 +82,8 @@ typedef struct {
                           /* in [1, 1e6]; 50000 (5%) is the usual value               */
     int32_t force_budget; /* -1: CLT budget; >= 0: n = min(N_t, force_budget)          */
     int32_t predictor;    /* vattn_predictor                                          */
-    int32_t rank;         /* r for VATTN_PRED_LOWRANK: 16, 32 or 64, <= d              */
+    int32_t rank;         /* r for VATTN_PRED_LOWRANK: 16, 32 or 64, <= d; 32 for      */
+                          /* VATTN_PRED_HASH (signature bits)                         */
     double eps;           /* > 0: relative accuracy target of the denominator         */
     double delta;         /* in (0, 1): failure probability                           */
     uint64_t seed;        /* Philox4x32-10 key; callers vary it per step and layer     */
@@ -98,7 +102,7 @@ typedef struct {
     const uint16_t* k_lowrank;  /* [num_blocks, Hkv, 16, r] bf16 bits (LOWRANK only;  */
                                 /* produced by vattn_project_keys), else NULL         */
     const float* proj;          /* [d, r] fp32, or [Hkv, d, r] (proj_heads = Hkv)     */
-                                /* (LOWRANK only), else NULL                          */
+                                /* (LOWRANK and HASH, r = 32 for HASH), else NULL     */
     const int32_t* block_table; /* [B, max_blocks] page ids                           */
     const int32_t* seq_lens;    /* [B] tokens in each sequence, 0 <= L <= max_seq_len  */
     int32_t B;                  /* host: batch, >= 1                                  */
@@ -113,6 +117,8 @@ typedef struct {
                                 /*   basis per KV head (its query heads' low-rank     */
                                 /*   queries and its low-rank keys use it); else      */
                                 /*   VATTN_E_SHAPE                                    */
+    const uint32_t* k_sig;      /* [num_blocks, Hkv, 16] key signatures (HASH only;   */
+                                /* produced by vattn_sign_keys), else ignored         */
 } vattn_inputs;
 
 /* Outputs.  out and lse are required; the others are optional (NULL = skip). */
@@ -195,6 +201,34 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
                              void* k_cache, void* v_cache, uint16_t* k_lowrank, const float* proj,
                              int32_t kv_dtype, int32_t num_blocks, int32_t Hkv, int32_t d, int32_t r,
                              int32_t proj_heads, void* hip_stream);
+
+/* Key signatures for the HASH predictor.  HashAttention (named as a top-k
+ * method in the edgentiq vAttention post, section "Performance and
+ * Efficiency") ranks tokens by bit signatures of query and key; with no
+ * trained hash the signatures here are random-hyperplane sign bits (Charikar's
+ * SimHash): bit j of k_sig[p][g][t] is set when pdot(K[p][g][t][:], P_g[:, j])
+ * > 0, j < 32, with P_g = proj ([d, 32] fp32, proj_heads 0 or 1) or proj[g]
+ * ([Hkv, d, 32], proj_heads = Hkv), and the same pdot as vattn_project_keys.
+ * The decode signs q_s the same way and scores a token by the number of equal
+ * bits (0 .. 32), lower index first among equal scores.
+ * k_cache: [num_blocks, Hkv, 16, d] kv_dtype; k_sig: [num_blocks, Hkv, 16]
+ * uint32 (output, 16-byte aligned).  Errors as for vattn_project_keys, before
+ * any launch.  Asynchronous on hip_stream. */
+vattn_status vattn_sign_keys(const void* k_cache, int32_t kv_dtype, const float* proj, uint32_t* k_sig,
+                             int32_t num_blocks, int32_t Hkv, int32_t d, int32_t proj_heads,
+                             void* hip_stream);
+
+/* vattn_append_kv for the HASH predictor: writes the newest token's K and V
+ * rows as vattn_append_kv does, and its signature
+ *   k_sig[page][g][slot] = signature of k_new[b][g][:] under P_g
+ * exactly as vattn_sign_keys computes it.  Arguments, errors and undefined
+ * behaviour as for vattn_append_kv, with k_sig ([num_blocks, Hkv, 16] uint32)
+ * and proj ([d, 32] or [Hkv, d, 32]) both required. */
+vattn_status vattn_append_kv_sig(const void* k_new, const void* v_new, const int32_t* pos,
+                                 const int32_t* block_table, int32_t B, int32_t max_blocks,
+                                 void* k_cache, void* v_cache, uint32_t* k_sig, const float* proj,
+                                 int32_t kv_dtype, int32_t num_blocks, int32_t Hkv, int32_t d,
+                                 int32_t proj_heads, void* hip_stream);
 
 /* Key Gram matrices for a per-head predictor basis.  The Loki page (abstract)
  * finds that key vectors lie in a much lower-dimensional space; a KV head's

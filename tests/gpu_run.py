@@ -30,7 +30,7 @@ class GpuCase:
 
     def __init__(self, w, want_idx=True, device="cuda:0", kv_host=False):
         """kv_host: K and V stay in pinned (device-mapped) host memory; the
-        low-rank keys are projected from a device copy and kept in HBM."""
+        low-rank keys (or key signatures) are made from a device copy and kept in HBM."""
         self.w = w
         dev = torch.device(device)
         self.q = w.q.to(dev)
@@ -39,6 +39,7 @@ class GpuCase:
         self.proj = w.proj.to(dev) if w.proj is not None else None
         kd = w.k_cache.to(dev)
         self.kt = vsa.project_keys(kd, self.proj) if w.cfg["predictor"] == 1 else None
+        self.ks = vsa.sign_keys(kd, self.proj) if w.cfg["predictor"] == 2 else None
         if kv_host:
             torch.cuda.synchronize()
             del kd
@@ -53,7 +54,7 @@ class GpuCase:
             self.v = w.v_cache.to(dev)
         self.dec = vsa.Decoder(self.q, self.k, self.v, self.bt, self.sl, vsa.Config.from_dict(w.cfg),
                                max_seq_len=w.max_seq_len, k_lowrank=self.kt, proj=self.proj,
-                               want_idx=want_idx, want_group_counts=True)
+                               want_idx=want_idx, want_group_counts=True, k_sig=self.ks)
 
     def run(self, seed=None):
         if seed is not None:

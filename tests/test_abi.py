@@ -81,6 +81,7 @@ BAD = [
     ("proj_heads", dict(proj_heads=3), {}, 2),  # neither one basis nor one per KV head
     ("rank", {}, dict(rank=24), 6),
     ("rank_gt_d", dict(d=64), dict(rank=128), 6),
+    ("hash_rank", {}, dict(predictor=2, rank=16), 6),  # signatures have 32 bits
 ]
 
 
@@ -140,6 +141,42 @@ def test_append_kv_argument_checks(lib):
     assert call(d=64, r=128) == 6     # rank above the head dim
     assert call(kc=P(260)) == 2        # misaligned
     assert call(ph=3) == 2             # neither one basis nor one per KV head
+
+
+def test_hash_predictor_argument_checks(lib):
+    P = C.c_void_p
+    cfg = _cfg(predictor=2, rank=32)
+    inp = _inputs(k_sig=256)
+    need = lib.vattn_workspace_size(C.byref(inp), C.byref(cfg))
+    assert need > 0
+    assert _decode(lib, _inputs(k_sig=None), cfg, ws=256) == 1
+    assert _decode(lib, _inputs(k_sig=256, proj=None), cfg, ws=256) == 1
+    assert _decode(lib, _inputs(k_sig=264), cfg, ws=256) == 2  # misaligned signatures
+    assert _decode(lib, inp, cfg, ws=256, ws_bytes=need - 1) == 5
+
+    def sign(**kw):
+        a = dict(k=P(256), dt=1, proj=P(256), ks=P(256), nb=4, Hkv=2, d=128, ph=1)
+        a.update(kw)
+        return lib.vattn_sign_keys(a["k"], a["dt"], a["proj"], a["ks"], a["nb"], a["Hkv"], a["d"], a["ph"], None)
+    assert sign(k=None) == 1 and sign(proj=None) == 1 and sign(ks=None) == 1
+    assert sign(dt=3) == 3
+    assert sign(d=96) == 6
+    assert sign(nb=0) == 2
+    assert sign(ph=3) == 2
+    assert sign(ks=P(260)) == 2
+
+    def app(**kw):
+        a = dict(kn=P(256), vn=P(256), pos=P(256), bt=P(256), B=2, mb=4, kc=P(256), vc=P(256), ks=P(256),
+                 proj=P(256), dt=1, nb=8, Hkv=2, d=128, ph=1)
+        a.update(kw)
+        return lib.vattn_append_kv_sig(a["kn"], a["vn"], a["pos"], a["bt"], a["B"], a["mb"], a["kc"], a["vc"],
+                                       a["ks"], a["proj"], a["dt"], a["nb"], a["Hkv"], a["d"], a["ph"], None)
+    assert app(ks=None) == 1 and app(proj=None) == 1 and app(kn=None) == 1
+    assert app(dt=2) == 3
+    assert app(B=0) == 2
+    assert app(ph=5) == 2
+    assert app(d=80) == 6
+    assert app(ks=P(264)) == 2
 
 
 def test_key_gram_argument_checks(lib):

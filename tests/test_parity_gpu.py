@@ -127,6 +127,23 @@ SMALL_CASES = {
     "d64_bf16_rank_eq_d": lambda: synthetic.make(
         name="d64_bf16_rank_eq_d", B=1, Hq=2, Hkv=2, d=64, seq_lens=(4000,), kv_dtype="bf16",
         recipe="normal", predictor=1, rank=64, sinks=8, window=8, topk_ppm=20000, data_seed=25),
+    # the hash-signature predictor: 32-bit key signatures, scores 0..32 with
+    # many ties (ranked by index), every group size, both dtypes and head
+    # dims, one hyperplane set per KV head, and the pre-merge path
+    "hash_g4_bf16_ragged": lambda: synthetic.make(
+        name="hash_g4_bf16_ragged", B=3, Hq=16, Hkv=4, d=128, seq_lens=(5000, 2500, 777),
+        kv_dtype="bf16", recipe="outlier", predictor=2, rank=32, sinks=32, window=64,
+        topk_ppm=25000, shuffle=True, data_seed=40),
+    "hash_g8_per_head_premerge": lambda: synthetic.make(
+        name="hash_g8_per_head_premerge", B=1, Hq=16, Hkv=2, d=128, seq_lens=(40000,), kv_dtype="bf16",
+        recipe="planted", predictor=2, rank=32, sinks=64, window=64, topk_ppm=20000,
+        proj_per_head=True, data_seed=41),
+    "hash_d64_f32_g2": lambda: synthetic.make(
+        name="hash_d64_f32_g2", B=2, Hq=4, Hkv=2, d=64, seq_lens=(3000, 1500), kv_dtype="f32",
+        recipe="planted", predictor=2, rank=32, sinks=8, window=16, topk_ppm=20000, data_seed=42),
+    "hash_g1_d64_bf16": lambda: synthetic.make(
+        name="hash_g1_d64_bf16", B=2, Hq=2, Hkv=2, d=64, seq_lens=(9000, 33), kv_dtype="bf16",
+        recipe="normal", predictor=2, rank=32, sinks=8, window=8, topk_ppm=25000, data_seed=43),
     "mixed_ragged_shuffled": lambda: synthetic.make(
         name="mixed_ragged_shuffled", B=4, Hq=8, Hkv=2, d=128, seq_lens=(1100, 3333, 2048, 1500),
         kv_dtype="bf16", recipe="mixed", predictor=1, rank=32, sinks=64, window=64,
@@ -256,6 +273,66 @@ def test_project_keys_bit_exact():
             assert np.array_equal(kt[:, g], want), g
 
 
+def test_sign_keys_bit_exact():
+    import torch
+    import verified_sparse_attention_amd as vsa
+    _, log = _gpu()
+    for (d, dt, per_head) in ((128, torch.bfloat16, False), (64, torch.float32, False),
+                              (128, torch.float32, True), (64, torch.bfloat16, True)):
+        log("[parity] sign_keys d=%d %s per_head=%s" % (d, dt, per_head))
+        gen = torch.Generator().manual_seed(d * 5000 + int(per_head))
+        Hkv = 3
+        k = (torch.randn(37, Hkv, 16, d, generator=gen) * 2.0).to(dt)
+        k[0, 0, 0] = 0.0  # a zero key: no bit set
+        P = (torch.stack([synthetic.orthonormal(d, 32, gen) for _ in range(Hkv)]) if per_head
+             else synthetic.orthonormal(d, 32, gen))
+        ks = vsa.sign_keys(k.cuda(), P.cuda()).cpu().numpy().view(np.uint32)
+        assert ks.shape == (37, Hkv, 16)
+        for g in range(Hkv):
+            rows = k[:, g].float().reshape(-1, d).numpy()
+            want = oracle.sign_rows(rows, (P[g] if per_head else P).numpy()).reshape(37, 16)
+            assert np.array_equal(ks[:, g], want), g
+        assert ks[0, 0, 0] == 0
+
+
+def test_append_kv_sig_bit_exact():
+    """The newest token's K and V rows land at their page slot and its
+    signature equals the oracle's; every other word is untouched."""
+    import torch
+    import verified_sparse_attention_amd as vsa
+    _, log = _gpu()
+    for (d, dt, per_head) in ((128, torch.bfloat16, False), (64, torch.float32, True)):
+        log("[parity] append_kv_sig d=%d %s per_head=%s" % (d, dt, per_head))
+        gen = torch.Generator().manual_seed(9000 + d)
+        B, Hkv, max_blocks = 5, 3, 6
+        nb = B * max_blocks + 4
+        bt = torch.randperm(nb, generator=gen)[:B * max_blocks].reshape(B, max_blocks).to(torch.int32)
+        pos = torch.tensor([0, 17, 95, -1, 40], dtype=torch.int32)
+        k_cache = torch.randn(nb, Hkv, 16, d, generator=gen).to(dt)
+        v_cache = torch.randn(nb, Hkv, 16, d, generator=gen).to(dt)
+        k_new = (torch.randn(B, Hkv, d, generator=gen) * 2.0).to(dt)
+        v_new = torch.randn(B, Hkv, d, generator=gen).to(dt)
+        P = (torch.stack([synthetic.orthonormal(d, 32, gen) for _ in range(Hkv)]) if per_head
+             else synthetic.orthonormal(d, 32, gen))
+        ks0 = torch.randint(-2 ** 31, 2 ** 31 - 1, (nb, Hkv, 16), generator=gen, dtype=torch.int32)
+        kc, vc, ks = k_cache.cuda(), v_cache.cuda(), ks0.cuda()
+        vsa.append_kv_sig(k_new.cuda(), v_new.cuda(), pos.cuda(), bt.cuda(), kc, vc, ks, P.cuda())
+        torch.cuda.synchronize()
+        want_k, want_v, want_s = k_cache.clone(), v_cache.clone(), ks0.numpy().view(np.uint32).copy()
+        for b in range(B):
+            p = int(pos[b])
+            if p < 0:
+                continue
+            page, slot = int(bt[b, p // 16]), p % 16
+            want_k[page, :, slot] = k_new[b]
+            want_v[page, :, slot] = v_new[b]
+            for g in range(Hkv):
+                Pg = (P[g] if per_head else P).numpy()
+                want_s[page, g, slot] = oracle.sign_rows(k_new[b, g:g + 1].float().numpy(), Pg)[0]
+        assert torch.equal(kc.cpu(), want_k) and torch.equal(vc.cpu(), want_v)
+        assert np.array_equal(ks.cpu().numpy().view(np.uint32), want_s)
+
+
 def test_append_kv_bit_exact():
     """The newest token of each sequence lands at its page slot in K and V, and
     its low-rank row equals the oracle's projection; other rows are untouched."""
@@ -346,6 +423,8 @@ FULL = {
     "flat_128k": (lambda: synthetic.flat_128k(), [(0, 0), (0, 6)]),
     "ragged_b64": (lambda: synthetic.ragged_b64(), [(0, 1), (17, 4), (40, 0), (63, 7)]),
     "wide_gqa_64k": (lambda: synthetic.wide_gqa_64k(), [(1, 2), (3, 7)]),
+    "llama8b_32k_hash": (lambda: synthetic.llama8b_32k(name="llama8b_32k_hash", predictor=2),
+                         [(0, 0), (5, 3)]),
     # the longest sequence the library takes (2^20 tokens): 256 predictor
     # chunks pre-merged in parts, 1024 gather chunks, 32 emission passes
     "max_seq_1m": (lambda: synthetic.make(

@@ -22,12 +22,12 @@ LIB_PATH = os.path.join(_PKG, "libvattn.so")
 
 PAGE = 16
 F32, BF16 = 0, 1
-PRED_EXACT, PRED_LOWRANK = 0, 1
+PRED_EXACT, PRED_LOWRANK, PRED_HASH = 0, 1, 2
 
 STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
 EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
-           "vattn_append_kv", "vattn_key_gram_workspace_size", "vattn_key_gram", "vattn_z_from_delta",
+           "vattn_append_kv", "vattn_sign_keys", "vattn_append_kv_sig", "vattn_key_gram_workspace_size", "vattn_key_gram", "vattn_z_from_delta",
            "vattn_status_string")
 NUM_STAGES = 7
 STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
@@ -51,7 +51,8 @@ class vattn_inputs(C.Structure):
                 ("k_lowrank", C.c_void_p), ("proj", C.c_void_p), ("block_table", C.c_void_p),
                 ("seq_lens", C.c_void_p), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
                 ("d", C.c_int32), ("max_blocks", C.c_int32), ("num_blocks", C.c_int32),
-                ("max_seq_len", C.c_int32), ("kv_dtype", C.c_int32), ("proj_heads", C.c_int32)]
+                ("max_seq_len", C.c_int32), ("kv_dtype", C.c_int32), ("proj_heads", C.c_int32),
+                ("k_sig", C.c_void_p)]
 
 
 class vattn_outputs(C.Structure):
@@ -88,6 +89,12 @@ def load():
         lib.vattn_append_kv.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                         C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+        lib.vattn_sign_keys.restype = C.c_int
+        lib.vattn_sign_keys.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p] + [C.c_int32] * 4 + \
+            [C.c_void_p]
+        lib.vattn_append_kv_sig.restype = C.c_int
+        lib.vattn_append_kv_sig.argtypes = [C.c_void_p] * 4 + [C.c_int32] * 2 + [C.c_void_p] * 4 + \
+            [C.c_int32] * 5 + [C.c_void_p]
         lib.vattn_key_gram_workspace_size.restype = C.c_size_t
         lib.vattn_key_gram_workspace_size.argtypes = [C.c_int32] * 4
         lib.vattn_key_gram.restype = C.c_int
@@ -145,11 +152,12 @@ def _kv_dtype(t):
     raise TypeError("kv cache dtype must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowrank=None, proj=None):
+def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowrank=None, proj=None,
+                k_sig=None):
     """Fill a vattn_inputs from torch tensors (no copies; all must be contiguous)."""
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seq_lens", seq_lens), ("k_lowrank", k_lowrank),
-                    ("proj", proj)):
+                    ("proj", proj), ("k_sig", k_sig)):
         if t is not None and not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
     B, Hq, d = q.shape
@@ -157,7 +165,8 @@ def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowra
                         None if k_lowrank is None else k_lowrank.data_ptr(),
                         None if proj is None else proj.data_ptr(), block_table.data_ptr(),
                         seq_lens.data_ptr(), B, Hq, k_cache.shape[1], d, block_table.shape[1],
-                        k_cache.shape[0], int(max_seq_len), _kv_dtype(k_cache), _proj_heads(proj))
+                        k_cache.shape[0], int(max_seq_len), _kv_dtype(k_cache), _proj_heads(proj),
+                        None if k_sig is None else k_sig.data_ptr())
 
 
 def _proj_heads(proj):
@@ -183,13 +192,13 @@ class Decoder:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_len,
                  k_lowrank=None, proj=None, want_idx=False, want_counts=True, want_stats=True,
-                 want_group_counts=False, workspace=None):
+                 want_group_counts=False, workspace=None, k_sig=None):
         import torch
         load()
         self.cfg = cfg
         self.inputs = make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
-                                  k_lowrank, proj)
-        self._keep = (q, k_cache, v_cache, block_table, seq_lens, k_lowrank, proj)
+                                  k_lowrank, proj, k_sig)
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, k_lowrank, proj, k_sig)
         dev = q.device
         B, Hq, d = q.shape
         self.out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
@@ -245,10 +254,10 @@ class Decoder:
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_len, k_lowrank=None,
-           proj=None, want_idx=False, stream=None):
+           proj=None, want_idx=False, stream=None, k_sig=None):
     """One decode step; returns the Decoder holding out, lse, idx, counts, stats."""
     dec = Decoder(q, k_cache, v_cache, block_table, seq_lens, cfg, max_seq_len=max_seq_len,
-                  k_lowrank=k_lowrank, proj=proj, want_idx=want_idx)
+                  k_lowrank=k_lowrank, proj=proj, want_idx=want_idx, k_sig=k_sig)
     return dec(stream)
 
 
@@ -279,6 +288,35 @@ def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, 
                                 _stream_handle(stream))
     if rc != 0:
         raise VattnError(rc, "vattn_append_kv")
+
+
+def sign_keys(k_cache, proj, k_sig=None, stream=None):
+    """Key signatures for the hash predictor: bit j set when K . P[:, j] > 0
+    ([num_blocks, Hkv, 16] as int32 words); proj [d, 32], or [Hkv, d, 32]."""
+    import torch
+    nb, Hkv, page, d = k_cache.shape
+    if proj.shape[-1] != 32:
+        raise ValueError("signatures take 32 hyperplanes, got %d" % proj.shape[-1])
+    if k_sig is None:
+        k_sig = torch.empty(nb, Hkv, page, dtype=torch.int32, device=k_cache.device)
+    rc = load().vattn_sign_keys(_ptr(k_cache), _kv_dtype(k_cache), _ptr(proj), _ptr(k_sig), nb, Hkv, d,
+                                _proj_heads(proj), _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_sign_keys")
+    return k_sig
+
+
+def append_kv_sig(k_new, v_new, pos, block_table, k_cache, v_cache, k_sig, proj, stream=None):
+    """append_kv for the hash predictor: the newest token's K and V rows and its
+    signature under proj ([d, 32] or [Hkv, d, 32])."""
+    B, Hkv, d = k_new.shape
+    nb = k_cache.shape[0]
+    rc = load().vattn_append_kv_sig(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), B,
+                                    block_table.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_sig),
+                                    _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, _proj_heads(proj),
+                                    _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_append_kv_sig")
 
 
 def key_gram(k_cache, block_table, seq_lens, max_seq_len, gram=None, workspace=None, stream=None):

@@ -40,6 +40,11 @@ double normal_isf(double p) {
     return upper ? z : -z;
 }
 
+// Width of the predictor's query rows: r (low rank), 32 (signature bits) or d (exact).
+int pred_row(const vattn_inputs* in, const vattn_cfg* cfg) {
+    return cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : cfg->predictor == VATTN_PRED_HASH ? 32 : in->d;
+}
+
 struct Shape {
     int G, cp, ncp, kcap, cg, ncg, words, nparts, kcap2;
 };
@@ -61,7 +66,10 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
     if (cfg->topk_ppm < 0 || cfg->topk_ppm > 1000000) return VATTN_E_CFG;
     if (cfg->base_ppm < 1 || cfg->base_ppm > 1000000) return VATTN_E_CFG;
     if (cfg->force_budget < -1) return VATTN_E_CFG;
-    if (cfg->predictor != VATTN_PRED_EXACT && cfg->predictor != VATTN_PRED_LOWRANK) return VATTN_E_CFG;
+    if (cfg->predictor != VATTN_PRED_EXACT && cfg->predictor != VATTN_PRED_LOWRANK &&
+        cfg->predictor != VATTN_PRED_HASH)
+        return VATTN_E_CFG;
+    if (cfg->predictor == VATTN_PRED_HASH && cfg->rank != 32) return VATTN_E_UNSUPPORTED;
     if (cfg->predictor == VATTN_PRED_LOWRANK) {
         if (cfg->rank != 16 && cfg->rank != 32 && cfg->rank != 64) return VATTN_E_UNSUPPORTED;
         if (cfg->rank > in->d) return VATTN_E_CFG;
@@ -74,7 +82,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
         // and within the workgroup LDS limit).  Below that bound, aim for one
         // chunk per compute unit over the whole batch, but keep chunks of at
         // least 2048 tokens so the chunk top-k stays a small fraction of them.
-        const int prow = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+        const int prow = pred_row(in, cfg);
         int cpmax = vattn::kPredKeys / G;
         while (cpmax > vattn::kPage &&
                vattn::predict_lds_bytes(G, in->d, prow, cpmax) > static_cast<size_t>(vattn::kMaxLds))
@@ -184,13 +192,15 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     if (!out || !out->out || !out->lse) return VATTN_E_NULL;
     if (!in->q || !in->k_cache || !in->v_cache || !in->block_table || !in->seq_lens) return VATTN_E_NULL;
     if (cfg->predictor == VATTN_PRED_LOWRANK && (!in->k_lowrank || !in->proj)) return VATTN_E_NULL;
+    if (cfg->predictor == VATTN_PRED_HASH && (!in->k_sig || !in->proj)) return VATTN_E_NULL;
     if (!aligned(in->q, 16) || !aligned(in->k_cache, 16) || !aligned(in->v_cache, 16) ||
-        (in->k_lowrank && !aligned(in->k_lowrank, 16)) || (in->proj && !aligned(in->proj, 4)))
+        (in->k_lowrank && !aligned(in->k_lowrank, 16)) || (in->proj && !aligned(in->proj, 4)) ||
+        (cfg->predictor == VATTN_PRED_HASH && !aligned(in->k_sig, 16)))
         return VATTN_E_SHAPE;
     if (out->idx && out->idx_cap < in->max_seq_len) return VATTN_E_SHAPE;
     const Layout L = layout(in, s);
     if (!workspace || !aligned(workspace, kAlign) || ws_bytes < L.total) return VATTN_E_WORKSPACE;
-    const int prow = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+    const int prow = pred_row(in, cfg);
     if (vattn::predict_lds_bytes(s.G, in->d, prow, s.cp) > static_cast<size_t>(vattn::kMaxLds))
         return VATTN_E_UNSUPPORTED;  // unreachable: the chunk is sized to fit
 
@@ -200,7 +210,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.Hkv = in->Hkv;
     p.G = s.G;
     p.d = in->d;
-    p.r = cfg->predictor == VATTN_PRED_LOWRANK ? cfg->rank : in->d;
+    p.r = prow;
     p.max_blocks = in->max_blocks;
     p.max_seq_len = in->max_seq_len;
     p.words = s.words;
@@ -226,8 +236,9 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.k = in->k_cache;
     p.v = in->v_cache;
     p.kt = in->k_lowrank;
+    p.ksig = cfg->predictor == VATTN_PRED_HASH ? in->k_sig : nullptr;
     p.proj = in->proj;
-    p.proj_stride = (in->proj_heads > 1 && cfg->predictor == VATTN_PRED_LOWRANK) ? in->d * cfg->rank : 0;
+    p.proj_stride = (in->proj_heads > 1 && cfg->predictor != VATTN_PRED_EXACT) ? in->d * prow : 0;
     p.bt = in->block_table;
     p.seq_lens = in->seq_lens;
     char* ws = static_cast<char*>(workspace);
@@ -316,8 +327,43 @@ vattn_status vattn_append_kv(const void* k_new, const void* v_new, const int32_t
     for (const void* q : ptrs)
         if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return VATTN_E_SHAPE;
     const int rc = vattn::launch_append(k_new, v_new, pos, block_table, B, max_blocks, k_cache, v_cache, k_lowrank,
-                                        proj, (k_lowrank && proj_heads > 1) ? d * r : 0, kv_dtype == VATTN_BF16,
-                                        Hkv, d, k_lowrank ? r : 16, hip_stream);
+                                        nullptr, proj, (k_lowrank && proj_heads > 1) ? d * r : 0,
+                                        kv_dtype == VATTN_BF16, Hkv, d, k_lowrank ? r : 16, hip_stream);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
+vattn_status vattn_sign_keys(const void* k_cache, int32_t kv_dtype, const float* proj, uint32_t* k_sig,
+                             int32_t num_blocks, int32_t Hkv, int32_t d, int32_t proj_heads, void* hip_stream) {
+    if (!k_cache || !proj || !k_sig) return VATTN_E_NULL;
+    if (proj_heads != 0 && proj_heads != 1 && proj_heads != Hkv) return VATTN_E_SHAPE;
+    if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
+    if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
+    if (!aligned(k_sig, 16) || !aligned(proj, 4)) return VATTN_E_SHAPE;
+    const long long rows = static_cast<long long>(num_blocks) * Hkv * VATTN_PAGE;
+    if ((rows + 7) / 8 > 0x7FFFFFFFLL) return VATTN_E_SHAPE;
+    const int rc = vattn::launch_sign(k_cache, kv_dtype == VATTN_BF16, proj, proj_heads > 1 ? d * 32 : 0, k_sig,
+                                      num_blocks, Hkv, d, hip_stream);
+    return rc == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
+vattn_status vattn_append_kv_sig(const void* k_new, const void* v_new, const int32_t* pos,
+                                 const int32_t* block_table, int32_t B, int32_t max_blocks, void* k_cache,
+                                 void* v_cache, uint32_t* k_sig, const float* proj, int32_t kv_dtype,
+                                 int32_t num_blocks, int32_t Hkv, int32_t d, int32_t proj_heads,
+                                 void* hip_stream) {
+    if (!k_new || !v_new || !pos || !block_table || !k_cache || !v_cache || !k_sig || !proj) return VATTN_E_NULL;
+    if (proj_heads != 0 && proj_heads != 1 && proj_heads != Hkv) return VATTN_E_SHAPE;
+    if (kv_dtype != VATTN_F32 && kv_dtype != VATTN_BF16) return VATTN_E_DTYPE;
+    if (B < 1 || max_blocks < 1 || num_blocks < 1 || Hkv < 1) return VATTN_E_SHAPE;
+    if (static_cast<long long>(B) * Hkv > 0x7FFFFFFFLL) return VATTN_E_SHAPE;
+    if (d != 64 && d != 128) return VATTN_E_UNSUPPORTED;
+    const void* ptrs[] = {k_new, v_new, k_cache, v_cache, k_sig, proj};
+    for (const void* q : ptrs)
+        if (reinterpret_cast<uintptr_t>(q) & 15u) return VATTN_E_SHAPE;
+    const int rc = vattn::launch_append(k_new, v_new, pos, block_table, B, max_blocks, k_cache, v_cache, nullptr,
+                                        k_sig, proj, proj_heads > 1 ? d * 32 : 0, kv_dtype == VATTN_BF16, Hkv, d,
+                                        16, hip_stream);
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 

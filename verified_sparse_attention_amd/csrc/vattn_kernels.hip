@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "vattn_device.hpp"
 #include "vattn_plan.hpp"
 
@@ -111,8 +113,12 @@ __device__ __forceinline__ void low_rank_query(const float* qs, const float* __r
     __syncthreads();
 }
 
+// T = uint32_t selects the signature predictor: one 32-bit word per token,
+// scored by the bits it shares with the query's signature (ROW = 32).
 template <int ROW, typename T, int G>
 __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
+    constexpr bool kSig = std::is_same<T, uint32_t>::value;
+    static_assert(!kSig || ROW == 32, "signatures have 32 bits");
     extern __shared__ __align__(16) unsigned char smem[];
     TopkShared<G>& TS = *reinterpret_cast<TopkShared<G>*>(smem);
     size_t off = align16(sizeof(TopkShared<G>));
@@ -209,8 +215,16 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
     }
 
     if (R.k > 0) {
-        // 1) low-rank queries q~ = pdot(q_s, P[:, j])
-        if (P.predictor == 1) {
+        // the heads' order-key brackets and candidate counters, reset before
+        // the barrier that ends step 1 (the stream's atomics follow it)
+        if (tid < G) {
+            TS.lo[tid] = 0xFFFFFFFFu;
+            TS.hi[tid] = 0;
+            TS.aux[tid] = 0;
+        }
+        // 1) low-rank queries q~ = pdot(q_s, P[:, j]) (the signature predictor
+        //    signs these)
+        if (P.predictor != 0) {
             float* part = reinterpret_cast<float*>(keys);  // free until the score stream
             const float* pg = P.proj + static_cast<size_t>(g) * P.proj_stride;  // the group's basis
             if (d == 128) low_rank_query<128, ROW, G>(qs, pg, qv, part, tid, nthr);
@@ -220,6 +234,68 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             __syncthreads();
         }
 
+        const int cbase = c * P.cp;
+        if constexpr (kSig) {
+            // 2') signature scores: bit j of the query's signature is q~_j > 0,
+            //     the test the key signatures were made with; a token scores
+            //     the number of equal bits.  A page's 16 words are 64
+            //     contiguous bytes: 4 tokens per lane and load.
+            uint32_t qsig[G], klo[G], khi[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int jj = 0; jj < 32; ++jj) w |= (qv[h * 32 + jj] > 0.0f ? 1u : 0u) << jj;
+                qsig[h] = w;
+                klo[h] = 0xFFFFFFFFu;
+                khi[h] = 0;
+            }
+            const uint32_t* ssrc = P.ksig + static_cast<size_t>(g) * kPage;
+            const uint32_t pstride = static_cast<uint32_t>(P.Hkv) * kPage;  // words per page
+            constexpr int SU = 4;  // loads in flight per lane
+            for (int base = 4 * tid; base < ntok; base += 4 * nthr * SU) {
+                uint4 wv[SU];
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    const int tl = base + 4 * nthr * u;
+                    if (tl < ntok) {
+                        const uint32_t pg = static_cast<uint32_t>(pages[tl / kPage]);
+                        wv[u] = *reinterpret_cast<const uint4*>(ssrc + static_cast<uint64_t>(pg) * pstride +
+                                                                tl % kPage);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    const int tl = base + 4 * nthr * u;
+                    if (tl >= ntok) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int tt = tb + tl + e;
+                        if (tt < t0 || tt >= t1) continue;
+                        const uint32_t kw = word_of(wv[u], e);
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            const uint32_t ok = okey(static_cast<float>(32 - __popc(qsig[h] ^ kw)));
+                            keys[h * ks + tt - cbase] = ok;
+                            klo[h] = min(klo[h], ok);
+                            khi[h] = max(khi[h], ok);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                uint32_t a = klo[h], bb = khi[h];
+                for (int o = 1; o < 64; o <<= 1) {
+                    a = min(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
+                    bb = max(bb, static_cast<uint32_t>(__shfl_xor(bb, o, 64)));
+                }
+                if (lane == 0) {
+                    atomicMin(&TS.lo[h], a);
+                    atomicMax(&TS.hi[h], bb);
+                }
+            }
+        } else {
         // 2) scores: LPT lanes per token row, 8 elements per lane; the G sums
         //    of a row are spread over its lanes, each finished by one lane
         constexpr int LPT = ROW / 8, TPW = 64 / LPT;
@@ -232,7 +308,6 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) qreg[h][e] = qv[h * ROW + 8 * j + e];
         const T* src = static_cast<const T*>(P.predictor == 1 ? static_cast<const void*>(P.kt) : P.k);
-        const int cbase = c * P.cp;
         const bool fin = SP::finisher(j);
         int kst[NH];  // this lane's heads' score rows, offset by the chunk start
         uint32_t klo[NH], khi[NH];  // order-key range of the stored scores
@@ -241,11 +316,6 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             kst[e] = SP::head(j, e) * ks - cbase;
             klo[e] = 0xFFFFFFFFu;
             khi[e] = 0;
-        }
-        if (tid < G) {
-            TS.lo[tid] = 0xFFFFFFFFu;
-            TS.hi[tid] = 0;
-            TS.aux[tid] = 0;
         }
         // Rows past the chunk's last page reread a row of that page and are
         // not stored.  Each iteration requests its whole batch before scoring
@@ -297,6 +367,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
                 atomicMax(&TS.hi[SP::head(j, e)], bb);
             }
         }
+        }  // score stream
         __syncthreads();
 
         // 3) chunk top-kp per head, written as candidates (any order)
@@ -1452,6 +1523,44 @@ __global__ __launch_bounds__(256) void k_project(const KVT* __restrict__ k, cons
 }
 
 // ===========================================================================
+// key signatures: bit j of S_i is pdot(K_i, P[:, j]) > 0 for the 32 columns of
+// P, with the pdot of the projection above.  A block holds 8 rows of one
+// (page, KV head); a wave's 64 lanes are the 32 hyperplanes of two rows, so
+// one ballot forms both signatures.
+// ===========================================================================
+template <typename KVT, int D>
+__global__ __launch_bounds__(256) void k_sign(const KVT* __restrict__ k, const float* __restrict__ proj,
+                                              uint32_t* __restrict__ ksig, long long nrows, int Hkv,
+                                              int proj_stride) {
+    constexpr int RPB = 8;
+    static_assert(kPage % RPB == 0, "a block's rows share their KV head");
+    __shared__ float ps[D * 32];
+    __shared__ float kr[RPB][D];
+    const long long r0 = static_cast<long long>(blockIdx.x) * RPB;
+    const float* pg = proj + static_cast<size_t>((r0 / kPage) % Hkv) * proj_stride;  // the head's hyperplanes
+    for (int x = threadIdx.x; x < D * 32; x += 256) ps[x] = pg[x];
+    for (int x = threadIdx.x; x < RPB * D; x += 256) {
+        const int rr = x / D, e = x - rr * D;
+        const long long row = r0 + rr;
+        float v = 0.f;
+        if (row < nrows) {
+            if constexpr (sizeof(KVT) == 2) {
+                v = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(k)[row * D + e]) << 16);
+            } else {
+                v = reinterpret_cast<const float*>(k)[row * D + e];
+            }
+        }
+        kr[rr][e] = v;
+    }
+    __syncthreads();
+    const int rr = threadIdx.x / 32, jj = threadIdx.x % 32;
+    const long long row = r0 + rr;
+    const float s = pdot_serial<D>(kr[rr], 1, ps + jj, 32);
+    const uint64_t m = __ballot(s > 0.0f);  // every lane takes part
+    if (jj == 0 && row < nrows) ksig[row] = static_cast<uint32_t>(m >> (32 * (rr & 1)));
+}
+
+// ===========================================================================
 // append: the newest token of each sequence into the paged caches, with its
 // low-rank key row (same pdot and rounding as the projection above)
 // ===========================================================================
@@ -1459,8 +1568,8 @@ template <typename KVT, int D, int RK>
 __global__ __launch_bounds__(64) void k_append(const KVT* __restrict__ k_new, const KVT* __restrict__ v_new,
                                                const int32_t* __restrict__ pos, const int32_t* __restrict__ bt,
                                                int max_blocks, int Hkv, KVT* __restrict__ kc, KVT* __restrict__ vc,
-                                               uint16_t* __restrict__ kt, const float* __restrict__ proj,
-                                               int proj_stride) {
+                                               uint16_t* __restrict__ kt, uint32_t* __restrict__ ksig,
+                                               const float* __restrict__ proj, int proj_stride) {
     __shared__ float kr[D];
     const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv, lane = threadIdx.x;
     const int p = pos[b];
@@ -1479,8 +1588,15 @@ __global__ __launch_bounds__(64) void k_append(const KVT* __restrict__ k_new, co
             kr[e] = kv;
         }
     }
-    if (kt == nullptr) return;  // block-uniform
+    if (kt == nullptr && ksig == nullptr) return;  // block-uniform
     __syncthreads();
+    if (ksig != nullptr) {  // signature: lanes 0..31 test one hyperplane each
+        const float s = lane < 32 ? pdot_serial<D>(kr, 1, proj + static_cast<size_t>(g) * proj_stride + lane, 32)
+                                  : 0.0f;
+        const uint64_t m = __ballot(s > 0.0f);
+        if (lane == 0) ksig[row] = static_cast<uint32_t>(m);
+        return;
+    }
     for (int j = lane; j < RK; j += 64) {
         const float s = pdot_serial<D>(kr, 1, proj + static_cast<size_t>(g) * proj_stride + j, RK);
         uint32_t u = __float_as_uint(s);
@@ -1542,7 +1658,9 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
     int rc = 0;
     if ((rc = mk.mark(0))) return rc;
     // 1. predictor + chunk candidates
-    if (p.predictor == 1) {
+    if (p.predictor == 2) {
+        rc = launch_predict<32, uint32_t, G>(p, st);
+    } else if (p.predictor == 1) {
         switch (p.r) {
             case 16: rc = launch_predict<16, uint16_t, G>(p, st); break;
             case 32: rc = launch_predict<32, uint16_t, G>(p, st); break;
@@ -1776,30 +1894,45 @@ int launch_project(const void* k_cache, int kv_bf16, const float* proj, int proj
 
 template <typename KVT, int D>
 static void launch_append_t(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                            int max_blocks, void* kc, void* vc, uint16_t* kt, const float* proj, int proj_stride,
-                            int Hkv, int r, hipStream_t st) {
+                            int max_blocks, void* kc, void* vc, uint16_t* kt, uint32_t* ksig, const float* proj,
+                            int proj_stride, int Hkv, int r, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(B * Hkv));
     const KVT* kn = static_cast<const KVT*>(k_new);
     const KVT* vn = static_cast<const KVT*>(v_new);
     KVT* kcc = static_cast<KVT*>(kc);
     KVT* vcc = static_cast<KVT*>(vc);
     switch (r) {
-        case 16: hipLaunchKernelGGL((k_append<KVT, D, 16>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
-        case 32: hipLaunchKernelGGL((k_append<KVT, D, 32>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
-        default: hipLaunchKernelGGL((k_append<KVT, D, 64>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, proj, proj_stride); break;
+        case 16: hipLaunchKernelGGL((k_append<KVT, D, 16>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, ksig, proj, proj_stride); break;
+        case 32: hipLaunchKernelGGL((k_append<KVT, D, 32>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, ksig, proj, proj_stride); break;
+        default: hipLaunchKernelGGL((k_append<KVT, D, 64>), grid, dim3(64), 0, st, kn, vn, pos, bt, max_blocks, Hkv, kcc, vcc, kt, ksig, proj, proj_stride); break;
     }
 }
 
 int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int proj_stride,
-                  int kv_bf16, int Hkv, int d, int r, void* stream) {
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, uint32_t* ksig, const float* proj,
+                  int proj_stride, int kv_bf16, int Hkv, int d, int r, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d == 128) {
-        if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
-        else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
+        if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
+        else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
     } else {
-        if (kv_bf16) launch_append_t<uint16_t, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
-        else launch_append_t<float, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, proj, proj_stride, Hkv, r, st);
+        if (kv_bf16) launch_append_t<uint16_t, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
+        else launch_append_t<float, 64>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_sign(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint32_t* ksig,
+                int num_blocks, int Hkv, int d, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const long long nrows = static_cast<long long>(num_blocks) * Hkv * kPage;
+    const dim3 grid(static_cast<unsigned>((nrows + 7) / 8));
+    if (d == 128) {
+        if (kv_bf16) hipLaunchKernelGGL((k_sign<uint16_t, 128>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(k_cache), proj, ksig, nrows, Hkv, proj_stride);
+        else hipLaunchKernelGGL((k_sign<float, 128>), grid, dim3(256), 0, st, static_cast<const float*>(k_cache), proj, ksig, nrows, Hkv, proj_stride);
+    } else {
+        if (kv_bf16) hipLaunchKernelGGL((k_sign<uint16_t, 64>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(k_cache), proj, ksig, nrows, Hkv, proj_stride);
+        else hipLaunchKernelGGL((k_sign<float, 64>), grid, dim3(256), 0, st, static_cast<const float*>(k_cache), proj, ksig, nrows, Hkv, proj_stride);
     }
     return static_cast<int>(hipGetLastError());
 }

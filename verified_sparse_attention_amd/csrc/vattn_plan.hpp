@@ -54,6 +54,7 @@ struct Plan {
     const void* k;
     const void* v;
     const uint16_t* kt;
+    const uint32_t* ksig;  // [num_blocks][Hkv][16] key signatures (signature predictor)
     const float* proj;
     int proj_stride;  // floats between the KV heads' bases (0: one basis for all)
     const int32_t* bt;
@@ -98,7 +99,9 @@ size_t predict_lds_bytes(int G, int d, int row, int cp);
 int launch_gram(const uint16_t* k_cache, const int32_t* bt, const int32_t* seq_lens, int B, int max_blocks,
                 int Hkv, int d, int max_seq_len, float* gram, float* part, void* stream);
 int launch_append(const void* k_new, const void* v_new, const int32_t* pos, const int32_t* bt, int B,
-                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, const float* proj, int proj_stride,
-                  int kv_bf16, int Hkv, int d, int r, void* stream);
+                  int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, uint32_t* ksig, const float* proj,
+                  int proj_stride, int kv_bf16, int Hkv, int d, int r, void* stream);
+int launch_sign(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint32_t* ksig,
+                int num_blocks, int Hkv, int d, void* stream);
 
 }  // namespace vattn
