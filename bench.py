@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--pca-basis", action="store_true",
                     help="also time and rate-check the workload with per-KV-head PCA predictor bases "
                          "(adds a pca_basis object; its decodes would otherwise mix into a kernel-trace profile)")
+    ap.add_argument("--hash", action="store_true",
+                    help="also time and rate-check the workload with the hash-signature predictor "
+                         "(adds a hash_predictor object)")
     return ap.parse_args()
 
 
@@ -404,6 +407,62 @@ def main():
             log("pca basis: %.4f ms/step, union density %.3f, eps violations %d / %d"
                 % (pca_ms, float((Up / L).mean()), pv, pt))
             del pca_decs
+
+        # ---- the same workload with the hash-signature predictor (32 sign
+        # bits per key under the workload's random directions, 4 bytes per
+        # token instead of a rank-r row): step and per-kernel time, union
+        # density and the (eps, delta) rate.  Context only.
+        if args.hash and proj is not None and r == 32:
+            hcfg = vsa.Config.from_dict(dict(w.cfg, predictor=vsa.PRED_HASH, rank=32))
+            hdecs = [vsa.Decoder(q, k, v, bt, sl, hcfg, max_seq_len=w.max_seq_len, proj=proj,
+                                 k_sig=vsa.sign_keys(k, proj), want_group_counts=True, workspace=ws)
+                     for (k, v, _) in inst]
+            for s in range(warm):
+                hdecs[s % n_inst].set_seed(40_000 + s)
+                hdecs[s % n_inst]()
+            torch.cuda.synchronize()
+            h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            h0.record()
+            for s in range(steps):
+                hdecs[s % n_inst].set_seed(50_000 + s)
+                hdecs[s % n_inst]()
+            h1.record()
+            torch.cuda.synchronize()
+            hash_ms = h0.elapsed_time(h1) / steps
+            hev = HipEvents((nst + 1) * steps)
+            hst = np.zeros(nst)
+            for s in range(steps):
+                hdecs[s % n_inst].set_seed(50_000 + s)
+                hdecs[s % n_inst].profiled(hev.ev[(nst + 1) * s:(nst + 1) * (s + 1)])
+            torch.cuda.synchronize()
+            for s in range(steps):
+                for k in range(nst):
+                    hst[k] += hev.elapsed((nst + 1) * s + k, (nst + 1) * s + k + 1)
+            hev.close()
+            hst /= steps
+            hv = ht = 0
+            hd = hdecs[0]
+            for s in range(args.rate_seeds):
+                hd.set_seed(2_000_000 + s)
+                hd()
+                rel = (torch.exp(hd.lse.double() - lse_dense) - 1.0).abs()
+                hv += int((rel > w.cfg["eps"]).sum())
+                ht += rel.numel()
+            torch.cuda.synchronize()
+            Uh = hd.group_counts[:, :, 0].double().cpu().numpy()
+            hpred_bytes = float(w.Hkv * (L * 4 + np.ceil(L / 16) * 4).sum())
+            result["hash_predictor"] = {
+                "ms_per_step": round(hash_ms, 5), "value": round(heads_tokens / (hash_ms * 1e-3), 1),
+                "unit": "heads·tokens/s", "union_density": round(float((Uh / L).mean()), 4),
+                "stage_us": {names[k]: round(float(hst[k]) * 1e3, 2) for k in range(nst)},
+                "predict_bytes": hpred_bytes,
+                "eps_violation": {"rate": round(hv / ht, 5), "violations": hv, "trials": ht,
+                                  "seeds": args.rate_seeds, "delta": w.cfg["delta"]},
+                "note": "same workload, top-k from 32-bit random-hyperplane key signatures "
+                        "(vattn_sign_keys) scored by shared bits"}
+            log("hash predictor: %.4f ms/step, predict %.1f us, union density %.3f, eps violations %d / %d"
+                % (hash_ms, hst[0] * 1e3, float((Uh / L).mean()), hv, ht))
+            del hdecs
 
     if not args.profile and not args.no_cpu_baseline:
         import oracle

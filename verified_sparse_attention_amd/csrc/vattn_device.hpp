@@ -348,21 +348,35 @@ struct SelShared {
     uint64_t prefix[NH];
     uint64_t thr[NH];
     uint32_t rem[NH];
+    uint32_t first[NH];  // the pass at which each problem starts
     uint32_t active;
 };
 
 // With `exact`, thr[h] is raised to the smallest selected key itself: needed
 // when `items` enumerates only part of a larger population (one bucket of it),
 // where a prefix threshold could also admit keys that were never visited.
+// With `kand` / `kor` (the AND and the OR of problem h's keys, in LDS), the
+// digits above the highest bit where its keys differ are known already: the
+// problem starts at the digit holding that bit.
 template <int NH, class Items>
 __device__ __forceinline__ void block_select(SelShared<NH>& S, const uint32_t (&want)[NH], Items&& items,
-                             bool exact = false) {
+                             bool exact = false, const uint64_t* kand = nullptr,
+                             const uint64_t* kor = nullptr) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     if (tid == 0) {
         uint32_t act = 0;
         for (int h = 0; h < NH; ++h) {
-            S.prefix[h] = 0;
+            uint64_t pre = 0;
+            uint32_t p0 = 0;
+            if (kand != nullptr && want[h] > 0) {
+                const uint64_t diff = kand[h] ^ kor[h];
+                const int hb = diff ? 63 - __clzll(static_cast<long long>(diff)) : 0;
+                p0 = static_cast<uint32_t>((63 - hb) / 8);  // digit 56 - 8 p0 .. 63 - 8 p0 holds hb
+                if (p0 > 0) pre = kand[h] & ~((1ull << (64 - 8 * p0)) - 1ull);
+            }
+            S.prefix[h] = pre;
+            S.first[h] = p0;
             S.thr[h] = 0;
             S.rem[h] = want[h];
             if (want[h] > 0) act |= 1u << h;
@@ -371,8 +385,13 @@ __device__ __forceinline__ void block_select(SelShared<NH>& S, const uint32_t (&
     }
     __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
-        const uint32_t act = S.active;
-        if (act == 0) break;  // block-uniform: read after a barrier
+        const uint32_t live = S.active;
+        if (live == 0) break;  // block-uniform: read after a barrier
+        uint32_t act = 0;      // the live problems whose first digit has come
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            if (((live >> h) & 1u) && S.first[h] <= static_cast<uint32_t>(pass)) act |= 1u << h;
+        if (act == 0) continue;  // block-uniform
         const int shift = 56 - 8 * pass;
         for (int x = tid; x < NH * 256; x += nthr) (&S.hist[0][0])[x] = 0;
         uint64_t pre[NH];
@@ -518,6 +537,7 @@ struct TopkShared {
     float vmin[NH], scale[NH];  // per-head bucket map, read by the visitors
     uint32_t mode[NH];          // 0 idle, 1 select, 2 emit everything
     uint32_t want[NH];
+    uint64_t kand[NH], kor[NH];  // AND / OR of a crowded boundary bucket's keys
 };
 
 // Score back from its order key.
@@ -637,13 +657,48 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
         uint32_t fw[NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h) fw[h] = ((fmask >> h) & 1u) ? T.want[h] - T.above[h] : 0u;
+        if (tid < NH) {
+            T.kand[tid] = ~0ull;
+            T.kor[tid] = 0ull;
+        }
+        __syncthreads();
+        // the bits the bucket's keys share (equal scores share the whole score
+        // half): the radix select skips the digits above the first that differs
+        {
+            uint64_t ka[NH], ko[NH];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                ka[h] = ~0ull;
+                ko[h] = 0ull;
+            }
+            items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+                if (((fmask >> h) & 1u) && topk_bucket(ok, vmn[h], scl[h]) == bst[h]) {
+                    const uint64_t key = topk_key(ok, idx);
+                    ka[h] &= key;
+                    ko[h] |= key;
+                }
+            });
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                if (!((fmask >> h) & 1u)) continue;
+                uint64_t a = ka[h], o = ko[h];
+                for (int m = 1; m < 64; m <<= 1) {
+                    a &= shfl_xor_u64(a, m);
+                    o |= shfl_xor_u64(o, m);
+                }
+                if (lane == 0) {
+                    atomicAnd(reinterpret_cast<unsigned long long*>(&T.kand[h]), static_cast<unsigned long long>(a));
+                    atomicOr(reinterpret_cast<unsigned long long*>(&T.kor[h]), static_cast<unsigned long long>(o));
+                }
+            }
+        }
         __syncthreads();
         block_select<NH>(T.S, fw, [&](auto&& visit) __attribute__((always_inline)) {
             items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
                 if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h])
                     visit(h, topk_key(ok, idx));
             });
-        }, true);
+        }, true, T.kand, T.kor);
         __syncthreads();
         items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
             if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h] &&
