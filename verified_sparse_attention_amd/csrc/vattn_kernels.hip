@@ -372,6 +372,100 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
 
         // 3) chunk top-kp per head, written as candidates (any order)
         const int kp = min(R.k, t1 - t0);
+        const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+        if constexpr (kSig) {
+            // 3') integer scores 0..32: the boundary score s* (the largest v
+            //     with at least kp keys >= v) by a binary search on block-wide
+            //     counts, then every key above s* and the kp - above tokens at
+            //     s* with the lowest indices.  Each thread owns a contiguous
+            //     token range, so a block scan ranks the ties in index order.
+            const int o0 = t0 - cbase, o1 = t1 - cbase, oa = o0 & ~3;
+            const int span = (((o1 - oa) + nthr - 1) / nthr + 3) & ~3;
+            const int my0 = oa + tid * span, my1 = min(my0 + span, o1);
+            uint32_t* red = &TS.S.hist[0][0];  // [2][nwaves][G] partial counts (free here)
+            auto count_cmp = [&](const uint32_t (&th)[G], uint32_t (&above)[G], uint32_t (&equal)[G]) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) above[h] = equal[h] = 0;
+                for (int o = my0; o < my1; o += 4) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const uint4 kk = *reinterpret_cast<const uint4*>(keys + h * ks + o);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t k = word_of(kk, e);
+                            const bool in = o + e >= o0 && o + e < o1;
+                            above[h] += (in && k > th[h]) ? 1u : 0u;
+                            equal[h] += (in && k == th[h]) ? 1u : 0u;
+                        }
+                    }
+                }
+            };
+            auto block_sum = [&](uint32_t (&v)[G], int buf) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    uint32_t x = v[h];
+                    for (int m = 1; m < 64; m <<= 1) x += static_cast<uint32_t>(__shfl_xor(x, m, 64));
+                    if (lane == 0) red[(buf * nwaves + wave) * G + h] = x;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    uint32_t x = 0;
+                    for (int w2 = 0; w2 < nwaves; ++w2) x += red[(buf * nwaves + w2) * G + h];
+                    v[h] = x;
+                }
+            };
+            int slo[G], shi[G];
+            uint32_t th[G], ca[G], ce[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                slo[h] = 0;   // count(score >= 0) = all >= kp
+                shi[h] = 33;  // count(score >= 33) = 0 < kp
+            }
+            for (int it = 0; it < 6; ++it) {  // 33 values: six halvings
+#pragma unroll
+                for (int h = 0; h < G; ++h) th[h] = okey(static_cast<float>((slo[h] + shi[h]) / 2));
+                count_cmp(th, ca, ce);
+#pragma unroll
+                for (int h = 0; h < G; ++h) ca[h] += ce[h];  // keys >= mid
+                block_sum(ca, it & 1);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const int mid = (slo[h] + shi[h]) / 2;
+                    if (ca[h] >= static_cast<uint32_t>(kp)) slo[h] = mid;
+                    else shi[h] = mid;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) th[h] = okey(static_cast<float>(slo[h]));
+            count_cmp(th, ca, ce);
+            uint64_t* __restrict__ cand = P.cand;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                uint32_t tot;
+                const uint32_t ex = block_excl_scan(ca[h] | (ce[h] << 16), wsum, tot);
+                const uint32_t need = static_cast<uint32_t>(kp) - (tot & 0xFFFFu);  // ties to take, >= 1
+                uint32_t pos = (ex & 0xFFFFu) + min(ex >> 16, need);
+                uint32_t tie = ex >> 16;  // ties before this thread's range
+                uint64_t* out = cand + ((bh0 + h) * P.ncp + c) * P.kcap;
+                for (int o = my0; o < my1; o += 4) {
+                    const uint4 kk = *reinterpret_cast<const uint4*>(keys + h * ks + o);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t k = word_of(kk, e);
+                        if (o + e < o0 || o + e >= o1) continue;
+                        const bool take = k > th[h] || (k == th[h] && tie++ < need);
+                        if (take && pos < static_cast<uint32_t>(kp))
+                            out[pos++] = topk_key(k, static_cast<uint32_t>(cbase + o + e));
+                    }
+                }
+                if (tid == 0) {
+                    uint32_t* cr = P.crange + ((bh0 + h) * P.ncp + c) * 2;
+                    cr[0] = th[h];  // the smallest emitted order key
+                    cr[1] = TS.hi[h];
+                }
+            }
+        } else {
         uint32_t want[G], total[G], lo[G], hi[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -380,7 +474,6 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             lo[h] = TS.lo[h];
             hi[h] = TS.hi[h];
         }
-        const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
         const int ncp = P.ncp, kcap = P.kcap;
         uint64_t* __restrict__ cand = P.cand;
         // each visit reads 4 consecutive keys of every head with one 16-byte
@@ -410,6 +503,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             cr[0] = TS.thr[tid] ? static_cast<uint32_t>(TS.thr[tid] >> 32) : lo[tid];
             cr[1] = hi[tid];
         }
+        }  // chunk top-k
     }
 }
 
