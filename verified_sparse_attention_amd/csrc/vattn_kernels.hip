@@ -375,14 +375,14 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
         if constexpr (kSig) {
             // 3') integer scores 0..32: the boundary score s* (the largest v
-            //     with at least kp keys >= v) by a binary search on block-wide
-            //     counts, then every key above s* and the kp - above tokens at
+            //     with at least kp keys >= v) by a search on block-wide counts
+            //     (three thresholds per sweep), then every key above s* and the kp - above tokens at
             //     s* with the lowest indices.  Each thread owns a contiguous
             //     token range, so a block scan ranks the ties in index order.
             const int o0 = t0 - cbase, o1 = t1 - cbase, oa = o0 & ~3;
             const int span = (((o1 - oa) + nthr - 1) / nthr + 3) & ~3;
             const int my0 = oa + tid * span, my1 = min(my0 + span, o1);
-            uint32_t* red = &TS.S.hist[0][0];  // [2][nwaves][G] partial counts (free here)
+            uint32_t* red = &TS.S.hist[0][0];  // [2][nwaves][3G] partial counts (free here)
             auto count_cmp = [&](const uint32_t (&th)[G], uint32_t (&above)[G], uint32_t (&equal)[G]) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) above[h] = equal[h] = 0;
@@ -400,20 +400,21 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
                     }
                 }
             };
-            auto block_sum = [&](uint32_t (&v)[G], int buf) {
+            // block-wide sums of 3G per-thread counts (double-buffered by pass)
+            constexpr int NC = 3 * G;
+            auto block_sum = [&](uint32_t (&v)[NC], int buf) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    uint32_t x = v[h];
-                    for (int m = 1; m < 64; m <<= 1) x += static_cast<uint32_t>(__shfl_xor(x, m, 64));
-                    if (lane == 0) red[(buf * nwaves + wave) * G + h] = x;
+                for (int x = 0; x < NC; ++x) {
+                    uint32_t y = v[x];
+                    for (int m = 1; m < 64; m <<= 1) y += static_cast<uint32_t>(__shfl_xor(y, m, 64));
+                    if (lane == 0) red[(buf * nwaves + wave) * NC + x] = y;
                 }
                 __syncthreads();
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    uint32_t x = 0;
-                    for (int w2 = 0; w2 < nwaves; ++w2) x += red[(buf * nwaves + w2) * G + h];
-                    v[h] = x;
-                }
+                for (int x = 0; x < NC; ++x) v[x] = 0;
+                for (int w2 = 0; w2 < nwaves; ++w2)
+#pragma unroll
+                    for (int x = 0; x < NC; ++x) v[x] += red[(buf * nwaves + w2) * NC + x];
             };
             int slo[G], shi[G];
             uint32_t th[G], ca[G], ce[G];
@@ -422,18 +423,41 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
                 slo[h] = 0;   // count(score >= 0) = all >= kp
                 shi[h] = 33;  // count(score >= 33) = 0 < kp
             }
-            for (int it = 0; it < 6; ++it) {  // 33 values: six halvings
+            // three probes per pass split [slo, shi) in quarters: 33 -> 9 -> 3 -> 1
+            for (int it = 0; it < 3; ++it) {
+                uint32_t pth[NC], cnt[NC];
 #pragma unroll
-                for (int h = 0; h < G; ++h) th[h] = okey(static_cast<float>((slo[h] + shi[h]) / 2));
-                count_cmp(th, ca, ce);
+                for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int h = 0; h < G; ++h) ca[h] += ce[h];  // keys >= mid
-                block_sum(ca, it & 1);
+                    for (int j = 0; j < 3; ++j)
+                        pth[3 * h + j] = okey(static_cast<float>(slo[h] + (shi[h] - slo[h]) * (j + 1) / 4));
+#pragma unroll
+                for (int x = 0; x < NC; ++x) cnt[x] = 0;
+                for (int o = my0; o < my1; o += 4) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const uint4 kk = *reinterpret_cast<const uint4*>(keys + h * ks + o);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t k = word_of(kk, e);
+                            const bool in = o + e >= o0 && o + e < o1;
+#pragma unroll
+                            for (int j = 0; j < 3; ++j) cnt[3 * h + j] += (in && k >= pth[3 * h + j]) ? 1u : 0u;
+                        }
+                    }
+                }
+                block_sum(cnt, it & 1);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const int mid = (slo[h] + shi[h]) / 2;
-                    if (ca[h] >= static_cast<uint32_t>(kp)) slo[h] = mid;
-                    else shi[h] = mid;
+                    int nlo = slo[h], nhi = shi[h];
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        const int m = slo[h] + (shi[h] - slo[h]) * (j + 1) / 4;
+                        if (cnt[3 * h + j] >= static_cast<uint32_t>(kp)) nlo = max(nlo, m);
+                        else nhi = min(nhi, m);
+                    }
+                    slo[h] = nlo;
+                    shi[h] = nhi;
                 }
             }
 #pragma unroll
