@@ -585,15 +585,17 @@ def test_pca_bases_from_the_gram():
     assert ov_pca > 0.7 and ov_pca > ov_rand + 0.3  # measured on the CPU: 0.81 against 0.19
 
 
-def test_graph_replay():
+@pytest.mark.parametrize("name", ["gqa4_bf16_ragged", "hash_g4_bf16_ragged"])
+def test_graph_replay(name):
     """A decode captured in a HIP graph (no allocation, no memset inside) and
     replayed with new queries written into the same buffer gives, on every
     replay, exactly the eager result for those queries.  The configuration,
-    seed included, is part of the captured launch."""
+    seed included, is part of the captured launch.  Low-rank and hash-signature
+    predictors."""
     import torch
     GpuCase, log = _gpu()
-    log("[parity] graph replay")
-    case = GpuCase(SMALL_CASES["gqa4_bf16_ragged"]())
+    log("[parity] graph replay %s" % name)
+    case = GpuCase(SMALL_CASES[name]())
     gen = torch.Generator().manual_seed(77)
     qs = [torch.randn(case.q.shape, generator=gen).cuda() for _ in range(3)]
     keys = ("idx", "counts", "stats", "out", "lse")
