@@ -387,15 +387,17 @@ def test_deterministic_repeat():
         assert np.array_equal(a[key], b[key]), key
 
 
-def test_concurrent_streams():
+@pytest.mark.parametrize("pair", [("gqa4_bf16_ragged", "flat_small"), ("hash_g4_bf16_ragged", "flat_small")])
+def test_concurrent_streams(pair):
     """Two decodes with their own workspaces, launched alternately on two
     streams so their kernels can overlap, give exactly what each gives alone:
-    the library keeps no state between or across calls."""
+    the library keeps no state between or across calls (also with a low-rank
+    and a hash-signature decode side by side)."""
     import torch
     GpuCase, log = _gpu()
-    log("[parity] two streams")
-    ca = GpuCase(SMALL_CASES["gqa4_bf16_ragged"]())
-    cb = GpuCase(SMALL_CASES["flat_small"]())
+    log("[parity] two streams %s + %s" % pair)
+    ca = GpuCase(SMALL_CASES[pair[0]]())
+    cb = GpuCase(SMALL_CASES[pair[1]]())
     ref_a, ref_b = ca.run(5), cb.run(9)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     main = torch.cuda.current_stream()
