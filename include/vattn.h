@@ -31,8 +31,14 @@
  *    the null stream).  No entry point synchronizes.
  *  - Errors are returned as vattn_status; nothing aborts or throws across the
  *    ABI.  Every host-checkable condition is validated before any launch; on a
- *    non-OK return nothing has been enqueued (except VATTN_E_HIP, which reports
- *    a failed launch).
+ *    non-OK return nothing has been enqueued, except VATTN_E_HIP: a launch
+ *    failed, and no kernel that consumes its output was enqueued after it.
+ *    VATTN_E_HIP is also returned, before any launch, when the calling thread
+ *    already has a HIP error pending from earlier calls (the error stays
+ *    pending for the caller to read).
+ *  - Thread safety: calls from several host threads may run concurrently as
+ *    long as they do not share a workspace or outputs; the library keeps no
+ *    mutable state besides a once-per-device kernel attribute flag (atomic).
  *  - Undefined (not checked on the device): seq_lens[b] > max_seq_len,
  *    block_table entries outside [0, num_blocks) for pages below
  *    ceil(seq_lens[b] / 16), non-finite values in q, K, V, P.

@@ -28,19 +28,31 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vattn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a separately built copy (the sanitizer build of the tests) may be named here
+_LIB_OVERRIDE = os.environ.get("VATTN_ORACLE_LIB")
 _lock = threading.Lock()
 _lib = None
+
+
+_CFLAGS = ["-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"]
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
+        subprocess.run(["gcc"] + _CFLAGS + ["-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(path: str) -> str:
+    """The same oracle under AddressSanitizer and UndefinedBehaviorSanitizer
+    (every report fatal), for the tests; a process loading it must preload
+    gcc's libasan (see tests/test_oracle_sanitized.py)."""
+    subprocess.run(["gcc"] + _CFLAGS + ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                                        "-fno-sanitize-recover=all", "-o", path, _SRC, "-lm"], check=True)
+    return path
 
 
 class OrcCfg(C.Structure):
@@ -54,9 +66,12 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-                build(force=True)
-            lib = C.CDLL(_LIB)
+            if _LIB_OVERRIDE:
+                lib = C.CDLL(_LIB_OVERRIDE)
+            else:
+                if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                    build(force=True)
+                lib = C.CDLL(_LIB)
             P = C.c_void_p
             lib.orc_decode.restype = C.c_int
             lib.orc_decode.argtypes = [C.POINTER(OrcCfg)] + [C.c_int] * 7 + [P] * 4 + [C.c_int] + \
@@ -209,6 +224,8 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
                             _ptr(seq_lens), _ptr(garr), ng, int(nthreads), _ptr(out), _ptr(lse),
                             _ptr(lse_dense), _ptr(out_dense), _ptr(idx), max_seq_len,
                             _ptr(counts), _ptr(stats), _ptr(pred))
+    if rc == 5:
+        raise ValueError("oracle refused a non-finite input (q, the basis, or a cached K or V row)")
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     res = dict(out=out, lse=lse, counts=counts, stats=stats, z32=c.z32)

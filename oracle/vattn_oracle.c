@@ -492,13 +492,27 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
     free(s_exact); free(list); free(w);
 }
 
-static void decode_group(const orc_ctx* cx, int b, int g) {
+/* 1 when every one of the n values is finite (the pages define the step on
+ * real scores; non-finite inputs have no reading and are refused). */
+static int all_finite(const float* x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        if (!isfinite(x[i])) return 0;
+    return 1;
+}
+
+/* One (b, g) group; returns 0, or 5 when a cached K or V row of the group is
+ * not finite (the group's outputs are then left untouched). */
+static int decode_group(const orc_ctx* cx, int b, int g) {
     const int d = cx->d, G = cx->Hq / cx->Hkv;
     int L = cx->seq_lens[b];
     float* K = (float*)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * d);
     float* V = (float*)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * d);
     load_rows(cx, cx->k_cache, b, g, L, K);
     load_rows(cx, cx->v_cache, b, g, L, V);
+    if (!all_finite(K, (int64_t)L * d) || !all_finite(V, (int64_t)L * d)) {
+        free(K); free(V);
+        return 5;
+    }
     float* Kt = NULL;
     if (cx->cfg->predictor == 1 && L > 0) {
         int r = cx->cfg->rank;
@@ -515,12 +529,14 @@ static void decode_group(const orc_ctx* cx, int b, int g) {
     }
     for (int hl = 0; hl < G; ++hl) decode_head(cx, b, g * G + hl, g, L, K, V, Kt, Ks);
     free(K); free(V); free(Kt); free(Ks);
+    return 0;
 }
 
 /*
  * Full decode over the (b, g) groups in `groups` (b*Hkv + g), or all groups
  * when groups is NULL.  Outputs of groups not evaluated are left untouched.
- * Returns 0 on success, nonzero on invalid arguments.
+ * Returns 0 on success, nonzero on invalid arguments: 5 when q, the basis or a
+ * cached K or V row that a decode reads is not finite (outputs then undefined).
  */
 int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks, int kv_bf16,
                int max_seq_len, const float* q, const void* k_cache, const void* v_cache,
@@ -535,16 +551,21 @@ int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks
     if (cfg->predictor < 0 || cfg->predictor > 2) return 3;
     if (proj_heads != 1 && proj_heads != Hkv) return 3;
     if (idx && idx_cap < max_seq_len) return 4;
+    if (!all_finite(q, (int64_t)B * Hq * d)) return 5;
+    if ((cfg->predictor == 1 || cfg->predictor == 2) &&
+        !all_finite(proj, (int64_t)proj_heads * d * cfg->rank))
+        return 5;
     orc_init_constants();
     orc_ctx cx = {cfg, B, Hq, Hkv, d, max_blocks, kv_bf16, max_seq_len, q, k_cache, v_cache,
                   proj, proj_heads, block_table, seq_lens, out, lse, lse_dense, out_dense, idx, idx_cap,
                   counts, stats, pred_scores};
     int total = groups ? n_groups : B * Hkv;
     if (nthreads < 1) nthreads = 1;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
     for (int t = 0; t < total; ++t) {
         int bg = groups ? groups[t] : t;
-        decode_group(&cx, bg / Hkv, bg % Hkv);
+        bad |= decode_group(&cx, bg / Hkv, bg % Hkv);
     }
-    return 0;
+    return bad ? 5 : 0;
 }

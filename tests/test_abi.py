@@ -240,3 +240,81 @@ def test_profiled_entry_point_argument_checks(lib):
     assert len(vsa.STAGES) == vsa.NUM_STAGES
     text = open(HEADER).read()
     assert re.search(r"#define VATTN_NUM_STAGES %d\b" % vsa.NUM_STAGES, text)
+
+
+# ---------------------------------------------------------------------------
+# Binding checks: dtypes and shapes the C ABI cannot see behind raw pointers
+# (a wrong one would make the kernels read past a buffer).  CPU tensors: every
+# check fails before any device work.
+# ---------------------------------------------------------------------------
+def _tensors(**over):
+    import torch
+    B, Hq, Hkv, d, nb, r = 2, 8, 2, 128, 20, 32
+    t = dict(q=torch.zeros(B, Hq, d), k_cache=torch.zeros(nb, Hkv, 16, d, dtype=torch.bfloat16),
+             v_cache=torch.zeros(nb, Hkv, 16, d, dtype=torch.bfloat16),
+             block_table=torch.zeros(B, 10, dtype=torch.int32), seq_lens=torch.zeros(B, dtype=torch.int32),
+             k_lowrank=torch.zeros(nb, Hkv, 16, r, dtype=torch.int16), proj=torch.zeros(d, r),
+             k_sig=None)
+    t.update(over)
+    return t
+
+
+@pytest.mark.parametrize("over,cfg_kw,msg", [
+    (lambda torch: dict(q=torch.zeros(2, 8, 128, dtype=torch.bfloat16)), {}, "q must be float32"),
+    (lambda torch: dict(q=torch.zeros(2, 8, 64)), {}, "k_cache must be"),
+    (lambda torch: dict(proj=torch.zeros(128, 16)), {}, "proj must have 32 columns"),
+    (lambda torch: dict(proj=torch.zeros(64, 32)), {}, "proj must have d = 128"),
+    (lambda torch: dict(proj=torch.zeros(3, 128, 32)), {}, "Hkv = 2"),
+    (lambda torch: dict(k_lowrank=torch.zeros(20, 2, 16, 16, dtype=torch.int16)), {}, "r = 32"),
+    (lambda torch: dict(k_lowrank=torch.zeros(19, 2, 16, 32, dtype=torch.int16)), {}, "matching k_cache"),
+    (lambda torch: dict(block_table=torch.zeros(2, 10, dtype=torch.int64)), {}, "block_table must be int32"),
+    (lambda torch: dict(seq_lens=torch.zeros(2, dtype=torch.int64)), {}, "seq_lens must be int32"),
+    (lambda torch: dict(v_cache=torch.zeros(20, 2, 16, 128)), {}, "v_cache must match"),
+    (lambda torch: dict(k_lowrank=None), {}, "needs k_lowrank and proj"),
+    (lambda torch: dict(k_sig=torch.zeros(20, 2, 15, dtype=torch.int32)), {"predictor": vsa.PRED_HASH},
+     "k_sig must be"),
+    (lambda torch: dict(), {"predictor": vsa.PRED_HASH}, "needs k_sig and proj"),
+])
+def test_binding_rejects_bad_tensors(over, cfg_kw, msg):
+    import torch
+    t = _tensors(**over(torch))
+    cfg = vsa.Config(**dict(dict(sinks=16, window=16, rank=32), **cfg_kw))
+    with pytest.raises(ValueError, match=msg):
+        vsa.make_inputs(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"], 160,
+                        k_lowrank=t["k_lowrank"], proj=t["proj"], k_sig=t["k_sig"], cfg=cfg)
+
+
+def test_binding_accepts_good_tensors():
+    t = _tensors()
+    inp = vsa.make_inputs(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"], 160,
+                          k_lowrank=t["k_lowrank"], proj=t["proj"], cfg=vsa.Config(rank=32))
+    assert (inp.B, inp.Hq, inp.Hkv, inp.d, inp.max_blocks, inp.num_blocks) == (2, 8, 2, 128, 10, 20)
+    with pytest.raises(ValueError, match="shorter than max_seq_len"):
+        vsa.make_inputs(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"], 161,
+                        k_lowrank=t["k_lowrank"], proj=t["proj"], cfg=vsa.Config(rank=32))
+
+
+def test_binding_rejects_bad_maintenance_tensors():
+    import torch
+    t = _tensors()
+    B, Hkv, d = 2, 2, 128
+    k_new = torch.zeros(B, Hkv, d, dtype=torch.bfloat16)
+    pos = torch.zeros(B, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k_new must be"):
+        vsa.append_kv(k_new.float(), k_new, pos, t["block_table"], t["k_cache"], t["v_cache"])
+    with pytest.raises(ValueError, match="pos must be int32"):
+        vsa.append_kv(k_new, k_new, pos.long(), t["block_table"], t["k_cache"], t["v_cache"])
+    with pytest.raises(ValueError, match="k_lowrank must be"):
+        vsa.append_kv(k_new, k_new, pos, t["block_table"], t["k_cache"], t["v_cache"],
+                      k_lowrank=torch.zeros(20, 2, 16, 16, dtype=torch.int16), proj=t["proj"])
+    with pytest.raises(ValueError, match="k_sig must be"):
+        vsa.append_kv_sig(k_new, k_new, pos, t["block_table"], t["k_cache"], t["v_cache"],
+                          torch.zeros(20, 2, 16, dtype=torch.int64), t["proj"])
+    with pytest.raises(ValueError, match="proj must be"):
+        vsa.project_keys(t["k_cache"], torch.zeros(64, 32))
+    with pytest.raises(ValueError, match="k_lowrank must be"):
+        vsa.project_keys(t["k_cache"], t["proj"], k_lowrank=torch.zeros(20, 2, 16, 16, dtype=torch.int16))
+    with pytest.raises(ValueError, match="k_sig must be"):
+        vsa.sign_keys(t["k_cache"], t["proj"], k_sig=torch.zeros(20, 2, 16, dtype=torch.int16))
+    with pytest.raises(ValueError, match="seq_lens must be int32"):
+        vsa.key_gram(t["k_cache"], t["block_table"], t["seq_lens"].long(), 160)

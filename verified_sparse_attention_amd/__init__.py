@@ -152,15 +152,97 @@ def _kv_dtype(t):
     raise TypeError("kv cache dtype must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowrank=None, proj=None,
-                k_sig=None):
-    """Fill a vattn_inputs from torch tensors (no copies; all must be contiguous)."""
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def check_tensors(q, k_cache, v_cache, block_table, seq_lens, k_lowrank=None, proj=None, k_sig=None,
+                  cfg=None):
+    """Dtype and shape checks the C ABI cannot make from raw pointers: a wrong
+    dtype or a short buffer would make the kernels read past it."""
+    import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seq_lens", seq_lens), ("k_lowrank", k_lowrank),
                     ("proj", proj), ("k_sig", k_sig)):
         if t is not None and not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
+    _require(q.dtype == torch.float32 and q.dim() == 3, "q must be float32 [B, Hq, d]")
     B, Hq, d = q.shape
+    _require(k_cache.dim() == 4 and k_cache.shape[2] == PAGE and k_cache.shape[3] == d,
+             "k_cache must be [num_blocks, Hkv, 16, d] with d = %d" % d)
+    _require(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype,
+             "v_cache must match k_cache in shape and dtype")
+    _kv_dtype(k_cache)
+    nb, Hkv = k_cache.shape[0], k_cache.shape[1]
+    _require(Hkv >= 1 and Hq % Hkv == 0, "Hq (%d) must be a multiple of Hkv (%d)" % (Hq, Hkv))
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+             "block_table must be int32 [B, max_blocks]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1 and seq_lens.shape[0] == B,
+             "seq_lens must be int32 [B]")
+    pred = cfg.predictor if cfg is not None else None
+    width = None
+    if cfg is not None:
+        width = cfg.rank if pred == PRED_LOWRANK else 32 if pred == PRED_HASH else None
+    if proj is not None:
+        _require(proj.dtype == torch.float32 and proj.dim() in (2, 3), "proj must be float32 [d, r] or [Hkv, d, r]")
+        _require(proj.shape[-2] == d, "proj must have d = %d rows" % d)
+        _require(proj.dim() == 2 or proj.shape[0] == Hkv, "proj [Hkv, d, r] must have Hkv = %d bases" % Hkv)
+        if width is not None:
+            _require(proj.shape[-1] == width, "proj must have %d columns for this predictor" % width)
+    if k_lowrank is not None:
+        _require(k_lowrank.dtype in (torch.int16, torch.bfloat16) and k_lowrank.dim() == 4 and
+                 tuple(k_lowrank.shape[:3]) == (nb, Hkv, PAGE),
+                 "k_lowrank must be 16-bit [num_blocks, Hkv, 16, r] matching k_cache")
+        if pred == PRED_LOWRANK:
+            _require(k_lowrank.shape[3] == cfg.rank, "k_lowrank must have r = %d columns" % cfg.rank)
+    if k_sig is not None:
+        _require(k_sig.dtype in (torch.int32, torch.uint32) and tuple(k_sig.shape) == (nb, Hkv, PAGE),
+                 "k_sig must be 32-bit [num_blocks, Hkv, 16] matching k_cache")
+    if pred == PRED_LOWRANK:
+        _require(k_lowrank is not None and proj is not None, "the low-rank predictor needs k_lowrank and proj")
+    if pred == PRED_HASH:
+        _require(k_sig is not None and proj is not None, "the hash predictor needs k_sig and proj")
+
+
+def _check_cache(k_cache, proj=None, width=None):
+    import torch
+    _require(k_cache.is_contiguous() and k_cache.dim() == 4 and k_cache.shape[2] == PAGE,
+             "k_cache must be a contiguous [num_blocks, Hkv, 16, d] tensor")
+    _kv_dtype(k_cache)
+    nb, Hkv, _, d = k_cache.shape
+    if proj is not None:
+        _require(proj.is_contiguous() and proj.dtype == torch.float32 and proj.dim() in (2, 3) and
+                 proj.shape[-2] == d and (proj.dim() == 2 or proj.shape[0] == Hkv),
+                 "proj must be contiguous float32 [d, r] or [Hkv, d, r] with d = %d" % d)
+        if width is not None:
+            _require(proj.shape[-1] == width, "proj must have %d columns" % width)
+    return nb, Hkv, d
+
+
+def _check_append(k_new, v_new, pos, block_table, k_cache, v_cache):
+    import torch
+    nb, Hkv, d = _check_cache(k_cache)
+    _require(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype and v_cache.is_contiguous(),
+             "v_cache must match k_cache")
+    _require(k_new.dim() == 3 and tuple(k_new.shape[1:]) == (Hkv, d) and k_new.dtype == k_cache.dtype and
+             k_new.is_contiguous(), "k_new must be contiguous [B, Hkv, d] in the cache dtype")
+    _require(v_new.shape == k_new.shape and v_new.dtype == k_new.dtype and v_new.is_contiguous(),
+             "v_new must match k_new")
+    B = k_new.shape[0]
+    _require(pos.dtype == torch.int32 and tuple(pos.shape) == (B,), "pos must be int32 [B]")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B and
+             block_table.is_contiguous(), "block_table must be contiguous int32 [B, max_blocks]")
+    return nb, Hkv, d
+
+
+def make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, k_lowrank=None, proj=None,
+                k_sig=None, cfg=None):
+    """Fill a vattn_inputs from torch tensors (no copies; all must be contiguous,
+    with the dtypes and shapes of include/vattn.h)."""
+    check_tensors(q, k_cache, v_cache, block_table, seq_lens, k_lowrank, proj, k_sig, cfg)
+    B, Hq, d = q.shape
+    _require(block_table.shape[1] * PAGE >= int(max_seq_len), "block_table rows are shorter than max_seq_len")
     return vattn_inputs(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                         None if k_lowrank is None else k_lowrank.data_ptr(),
                         None if proj is None else proj.data_ptr(), block_table.data_ptr(),
@@ -197,7 +279,7 @@ class Decoder:
         load()
         self.cfg = cfg
         self.inputs = make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
-                                  k_lowrank, proj, k_sig)
+                                  k_lowrank, proj, k_sig, cfg)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, k_lowrank, proj, k_sig)
         dev = q.device
         B, Hq, d = q.shape
@@ -265,10 +347,13 @@ def project_keys(k_cache, proj, k_lowrank=None, stream=None):
     """Low-rank key cache bf16(K P) for the low-rank predictor (as int16 bit patterns);
     proj [d, r], or [Hkv, d, r] for one basis per KV head."""
     import torch
-    nb, Hkv, page, d = k_cache.shape
+    nb, Hkv, d = _check_cache(k_cache, proj)
+    page = PAGE
     r = proj.shape[-1]
     if k_lowrank is None:
         k_lowrank = torch.empty(nb, Hkv, page, r, dtype=torch.int16, device=k_cache.device)
+    _require(k_lowrank.dtype in (torch.int16, torch.bfloat16) and tuple(k_lowrank.shape) == (nb, Hkv, page, r) and
+             k_lowrank.is_contiguous(), "k_lowrank must be contiguous 16-bit [num_blocks, Hkv, 16, r]")
     rc = load().vattn_project_keys(_ptr(k_cache), _kv_dtype(k_cache), _ptr(proj), _ptr(k_lowrank),
                                    nb, Hkv, d, r, _proj_heads(proj), _stream_handle(stream))
     if rc != 0:
@@ -279,9 +364,14 @@ def project_keys(k_cache, proj, k_lowrank=None, stream=None):
 def append_kv(k_new, v_new, pos, block_table, k_cache, v_cache, k_lowrank=None, proj=None, stream=None):
     """Writes each sequence's newest token (k_new, v_new: [B, Hkv, d]) at position pos[b]
     of the paged caches, and its low-rank key row when k_lowrank/proj are given."""
-    B, Hkv, d = k_new.shape
-    nb = k_cache.shape[0]
+    import torch
+    nb, Hkv, d = _check_append(k_new, v_new, pos, block_table, k_cache, v_cache)
+    B = k_new.shape[0]
+    _check_cache(k_cache, proj)
     r = proj.shape[-1] if proj is not None else 0
+    if k_lowrank is not None:
+        _require(k_lowrank.dtype in (torch.int16, torch.bfloat16) and tuple(k_lowrank.shape) == (nb, Hkv, PAGE, r),
+                 "k_lowrank must be 16-bit [num_blocks, Hkv, 16, r] with r = proj's columns")
     rc = load().vattn_append_kv(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), B,
                                 block_table.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_lowrank),
                                 _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, r, _proj_heads(proj),
@@ -294,11 +384,14 @@ def sign_keys(k_cache, proj, k_sig=None, stream=None):
     """Key signatures for the hash predictor: bit j set when K . P[:, j] > 0
     ([num_blocks, Hkv, 16] as int32 words); proj [d, 32], or [Hkv, d, 32]."""
     import torch
-    nb, Hkv, page, d = k_cache.shape
     if proj.shape[-1] != 32:
         raise ValueError("signatures take 32 hyperplanes, got %d" % proj.shape[-1])
+    nb, Hkv, d = _check_cache(k_cache, proj, 32)
+    page = PAGE
     if k_sig is None:
         k_sig = torch.empty(nb, Hkv, page, dtype=torch.int32, device=k_cache.device)
+    _require(k_sig.dtype in (torch.int32, torch.uint32) and tuple(k_sig.shape) == (nb, Hkv, page) and
+             k_sig.is_contiguous(), "k_sig must be contiguous 32-bit [num_blocks, Hkv, 16]")
     rc = load().vattn_sign_keys(_ptr(k_cache), _kv_dtype(k_cache), _ptr(proj), _ptr(k_sig), nb, Hkv, d,
                                 _proj_heads(proj), _stream_handle(stream))
     if rc != 0:
@@ -309,8 +402,12 @@ def sign_keys(k_cache, proj, k_sig=None, stream=None):
 def append_kv_sig(k_new, v_new, pos, block_table, k_cache, v_cache, k_sig, proj, stream=None):
     """append_kv for the hash predictor: the newest token's K and V rows and its
     signature under proj ([d, 32] or [Hkv, d, 32])."""
-    B, Hkv, d = k_new.shape
-    nb = k_cache.shape[0]
+    import torch
+    nb, Hkv, d = _check_append(k_new, v_new, pos, block_table, k_cache, v_cache)
+    B = k_new.shape[0]
+    _check_cache(k_cache, proj, 32)
+    _require(k_sig.dtype in (torch.int32, torch.uint32) and tuple(k_sig.shape) == (nb, Hkv, PAGE),
+             "k_sig must be 32-bit [num_blocks, Hkv, 16]")
     rc = load().vattn_append_kv_sig(_ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), B,
                                     block_table.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_sig),
                                     _ptr(proj), _kv_dtype(k_cache), nb, Hkv, d, _proj_heads(proj),
@@ -325,8 +422,11 @@ def key_gram(k_cache, block_table, seq_lens, max_seq_len, gram=None, workspace=N
     can be taken as its r leading eigenvectors.  gram and workspace (uint8) may be
     passed in to reuse them."""
     import torch
-    nb, Hkv, page, d = k_cache.shape
+    nb, Hkv, d = _check_cache(k_cache)
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+             "block_table must be contiguous int32 [B, max_blocks]")
     B, max_blocks = block_table.shape
+    _require(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens must be int32 [B]")
     lib = load()
     need = int(lib.vattn_key_gram_workspace_size(B, Hkv, d, int(max_seq_len)))
     if need == 0:
@@ -338,6 +438,8 @@ def key_gram(k_cache, block_table, seq_lens, max_seq_len, gram=None, workspace=N
         raise ValueError("workspace too small: need %d bytes" % need)
     if gram is None:
         gram = torch.empty(Hkv, d, d, dtype=torch.float32, device=k_cache.device)
+    _require(gram.dtype == torch.float32 and tuple(gram.shape) == (Hkv, d, d) and gram.is_contiguous(),
+             "gram must be contiguous float32 [Hkv, d, d]")
     rc = lib.vattn_key_gram(_ptr(k_cache), _kv_dtype(k_cache), _ptr(block_table), _ptr(seq_lens), B, max_blocks,
                             nb, Hkv, d, int(max_seq_len), _ptr(gram), C.c_void_p(wp), need, _stream_handle(stream))
     if rc != 0:

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "vattn_device.hpp"
@@ -1735,20 +1736,25 @@ struct Marks {
     }
 };
 
+// Status of the launch just enqueued (clears it): every stage is checked
+// before a kernel that consumes its output is enqueued.
+static int launched() { return static_cast<int>(hipGetLastError()); }
+
 template <int D, typename KVT, int G>
 static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) {
     const dim3 grid_c(p.ncg, p.B * p.Hkv);         // (chunk, group)
     const dim3 grid_h(p.Hkv, p.ncg, p.B);          // (KV head, chunk, sequence)
     int rc = 0;
     hipLaunchKernelGGL((k_base<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
-    if ((rc = mk.mark(3))) return rc;
+    if ((rc = launched()) || (rc = mk.mark(3))) return rc;
     // with many heads the per-head kernels run smaller blocks, several per CU
     if (p.B * p.Hq >= kManyHeads)
         hipLaunchKernelGGL(k_budget<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
     else
         hipLaunchKernelGGL(k_budget<kBudgetThreads>, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
-    if ((rc = mk.mark(4))) return rc;
+    if ((rc = launched()) || (rc = mk.mark(4))) return rc;
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
+    if ((rc = launched())) return rc;
     return mk.mark(5);
 }
 
@@ -1756,19 +1762,21 @@ template <int ROW, typename T, int G>
 static int launch_predict(const Plan& p, hipStream_t st) {
     const size_t lds = predict_lds_bytes(G, p.d, ROW, p.cp);
     auto kern = k_predict<ROW, T, G>;
-    // the dynamic LDS limit is raised once per kernel instance and device
+    // the dynamic LDS limit is raised once per kernel instance and device; the
+    // flags are atomics so concurrent callers on several host threads are safe
+    // (setting the attribute twice is harmless)
     constexpr int kDevices = 64;
-    static bool attr_set[kDevices] = {};
+    static std::atomic<bool> attr_set[kDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    if (dev >= kDevices || !attr_set[dev]) {
+    if (dev >= kDevices || !attr_set[dev].load(std::memory_order_acquire)) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         if (e != hipSuccess) return static_cast<int>(e);
-        if (dev < kDevices) attr_set[dev] = true;
+        if (dev < kDevices) attr_set[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3(p.ncp, p.B * p.Hkv), dim3(kPredThreads), lds, st, p);
-    return 0;
+    return launched();
 }
 
 template <int G>
@@ -1793,12 +1801,13 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
     // 2. exact top-k, bitmap, base threshold
     if (p.nparts > 0) {
         hipLaunchKernelGGL(k_premerge, dim3(p.B * p.Hq, p.nparts), dim3(kSelectThreads), 0, st, p);
+        if ((rc = launched())) return rc;
         hipLaunchKernelGGL(k_select<true>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
     } else {
         hipLaunchKernelGGL(k_select<false>, dim3(p.B * p.Hq),
                            dim3(p.B * p.Hq >= kManyHeads ? kHeadThreadsMany : kSelectThreads), 0, st, p);
     }
-    if ((rc = mk.mark(2))) return rc;
+    if ((rc = launched()) || (rc = mk.mark(2))) return rc;
     // 3-5. base scores, budget, gather
     if (p.d == 128)
         rc = p.kv_bf16 ? launch_chunk_kernels<128, uint16_t, G>(p, st, mk)
@@ -1812,7 +1821,10 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
 int launch_decode(const Plan& p, void* stream, void* const* events) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Marks mk{events, st};
-    int rc = 0;
+    // an error the calling thread left pending is reported, not taken for one
+    // of this call's launches, and nothing is enqueued behind it
+    int rc = static_cast<int>(hipPeekAtLastError());
+    if (rc) return rc;
     switch (p.G) {
         case 1: rc = launch_g<1>(p, st, mk); break;
         case 2: rc = launch_g<2>(p, st, mk); break;
@@ -1824,15 +1836,15 @@ int launch_decode(const Plan& p, void* stream, void* const* events) {
         hipLaunchKernelGGL(k_combine<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
     else
         hipLaunchKernelGGL(k_combine<kCombineThreads>, dim3(p.B * p.Hq), dim3(kCombineThreads), 0, st, p);
-    if ((rc = mk.mark(6))) return rc;
+    if ((rc = launched()) || (rc = mk.mark(6))) return rc;
     if (p.idx) {
         if (p.B * p.Hq >= kManyHeads)
             hipLaunchKernelGGL(k_emit<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
         else
             hipLaunchKernelGGL(k_emit<kEmitThreads>, dim3(p.B * p.Hq), dim3(kEmitThreads), 0, st, p);
+        if ((rc = launched())) return rc;
     }
-    if ((rc = mk.mark(7))) return rc;
-    return static_cast<int>(hipGetLastError());
+    return mk.mark(7);
 }
 
 // ===========================================================================
@@ -1959,6 +1971,7 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ p
 int launch_gram(const uint16_t* k_cache, const int32_t* bt, const int32_t* seq_lens, int B, int max_blocks,
                 int Hkv, int d, int max_seq_len, float* gram, float* part, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (const int rc = static_cast<int>(hipPeekAtLastError())) return rc;  // pending from the caller
     const int nchunk = (max_seq_len + kGramChunk - 1) / kGramChunk;
     const dim3 grid(static_cast<unsigned>(nchunk), static_cast<unsigned>(B * Hkv));
     if (d == 128)
@@ -1999,6 +2012,7 @@ static void launch_project_t(const void* k, const float* proj, uint16_t* kt, lon
 int launch_project(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint16_t* kt,
                    int num_blocks, int Hkv, int d, int r, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (const int rc = static_cast<int>(hipPeekAtLastError())) return rc;  // pending from the caller
     const long long nrows = static_cast<long long>(num_blocks) * Hkv * kPage;
     if (d == 128) {
         if (kv_bf16) launch_project_t<uint16_t, 128>(k_cache, proj, kt, nrows, r, Hkv, proj_stride, st);
@@ -2030,6 +2044,7 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* pos, cons
                   int max_blocks, void* k_cache, void* v_cache, uint16_t* kt, uint32_t* ksig, const float* proj,
                   int proj_stride, int kv_bf16, int Hkv, int d, int r, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (const int rc = static_cast<int>(hipPeekAtLastError())) return rc;  // pending from the caller
     if (d == 128) {
         if (kv_bf16) launch_append_t<uint16_t, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
         else launch_append_t<float, 128>(k_new, v_new, pos, bt, B, max_blocks, k_cache, v_cache, kt, ksig, proj, proj_stride, Hkv, r, st);
@@ -2043,6 +2058,7 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* pos, cons
 int launch_sign(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint32_t* ksig,
                 int num_blocks, int Hkv, int d, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (const int rc = static_cast<int>(hipPeekAtLastError())) return rc;  // pending from the caller
     const long long nrows = static_cast<long long>(num_blocks) * Hkv * kPage;
     const dim3 grid(static_cast<unsigned>((nrows + 7) / 8));
     if (d == 128) {
