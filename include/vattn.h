@@ -157,6 +157,28 @@ size_t vattn_workspace_size(const vattn_inputs* in, const vattn_cfg* cfg);
 vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
                           void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of the library's static device scratch (one copy per GPU, held until
+ * the process ends) that vattn_decode_noalloc uses in place of a workspace. */
+#define VATTN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* vattn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The kernels' scratch space is a static device array
+ * of VATTN_NOALLOC_SCRATCH_BYTES bytes inside the library; its device address
+ * is looked up on the first call on each device (with that device current),
+ * after which no call makes any allocating HIP or library call.  The caller
+ * still passes inputs and outputs exactly as for vattn_decode, with the same
+ * results.  Returns VATTN_E_WORKSPACE, before any HIP call, when
+ * vattn_workspace_size(in, cfg) exceeds VATTN_NOALLOC_SCRATCH_BYTES (e.g.
+ * 8 sequences x 32K tokens x 32 query heads need 104 MiB and fit; 64 x 16K
+ * do not); other errors as for vattn_decode.  Every call on one GPU shares that
+ * GPU's array and leaves it holding its contents (no call needs it cleared):
+ * two calls that overlap on one GPU (other streams, other host threads) race
+ * and give undefined results, so such callers serialise them or use
+ * vattn_decode with separate workspaces.  Asynchronous on hip_stream. */
+vattn_status vattn_decode_noalloc(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
+                                  void* hip_stream);
+
 /* Kernels of one decode step, in launch order (for vattn_decode_profiled). */
 #define VATTN_NUM_STAGES 7 /* predict, select, base, budget, gather, combine, emit */
 

@@ -26,10 +26,11 @@ PRED_EXACT, PRED_LOWRANK, PRED_HASH = 0, 1, 2
 
 STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
-EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_profiled", "vattn_project_keys",
+EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_noalloc", "vattn_decode_profiled", "vattn_project_keys",
            "vattn_append_kv", "vattn_sign_keys", "vattn_append_kv_sig", "vattn_key_gram_workspace_size", "vattn_key_gram", "vattn_z_from_delta",
            "vattn_status_string")
 NUM_STAGES = 7
+NOALLOC_SCRATCH_BYTES = 128 << 20  # VATTN_NOALLOC_SCRATCH_BYTES
 STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
 
 
@@ -78,6 +79,9 @@ def load():
         lib.vattn_decode.restype = C.c_int
         lib.vattn_decode.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg),
                                      C.POINTER(vattn_outputs), C.c_void_p, C.c_size_t, C.c_void_p]
+        lib.vattn_decode_noalloc.restype = C.c_int
+        lib.vattn_decode_noalloc.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg),
+                                             C.POINTER(vattn_outputs), C.c_void_p]
         lib.vattn_decode_profiled.restype = C.c_int
         lib.vattn_decode_profiled.argtypes = [C.POINTER(vattn_inputs), C.POINTER(vattn_cfg),
                                               C.POINTER(vattn_outputs), C.c_void_p, C.c_size_t,
@@ -274,9 +278,12 @@ class Decoder:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, cfg: Config, *, max_seq_len,
                  k_lowrank=None, proj=None, want_idx=False, want_counts=True, want_stats=True,
-                 want_group_counts=False, workspace=None, k_sig=None):
+                 want_group_counts=False, workspace=None, k_sig=None, noalloc=False):
+        """noalloc: launch through vattn_decode_noalloc (the library's static
+        device scratch; no workspace is allocated here)."""
         import torch
         load()
+        self.noalloc = noalloc
         self.cfg = cfg
         self.inputs = make_inputs(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
                                   k_lowrank, proj, k_sig, cfg)
@@ -293,11 +300,16 @@ class Decoder:
         self.ws_bytes = workspace_size(self.inputs, cfg)
         if self.ws_bytes == 0:
             raise VattnError(4, "vattn_workspace_size (invalid shapes or cfg)")
-        if workspace is None:
+        if noalloc:
+            if self.ws_bytes > NOALLOC_SCRATCH_BYTES:
+                raise VattnError(5, "vattn_decode_noalloc (needs %d bytes of scratch, the static array holds %d)"
+                                 % (self.ws_bytes, NOALLOC_SCRATCH_BYTES))
+            workspace = torch.empty(0, dtype=torch.uint8, device=dev)  # never used
+        elif workspace is None:
             workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=dev)
         base = workspace.data_ptr()
         self.ws_ptr = (base + 255) // 256 * 256
-        if workspace.numel() - (self.ws_ptr - base) < self.ws_bytes:
+        if not noalloc and workspace.numel() - (self.ws_ptr - base) < self.ws_bytes:
             raise ValueError("workspace too small: need %d bytes" % self.ws_bytes)
         self.workspace = workspace
         self.outputs = vattn_outputs(self.out.data_ptr(), self.lse.data_ptr(),
@@ -314,6 +326,12 @@ class Decoder:
         self._ccfg.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
 
     def __call__(self, stream=None):
+        if self.noalloc:
+            rc = load().vattn_decode_noalloc(C.byref(self.inputs), C.byref(self._ccfg), C.byref(self.outputs),
+                                             _stream_handle(stream))
+            if rc != 0:
+                raise VattnError(rc, "vattn_decode_noalloc")
+            return self
         rc = load().vattn_decode(C.byref(self.inputs), C.byref(self._ccfg), C.byref(self.outputs),
                                  C.c_void_p(self.ws_ptr), self.ws_bytes, _stream_handle(stream))
         if rc != 0:

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "vattn.h"
 #include "vattn_plan.hpp"
@@ -278,6 +279,51 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
 vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
                           void* workspace, size_t ws_bytes, void* hip_stream) {
     return decode_impl(in, cfg, out, workspace, ws_bytes, hip_stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Static device scratch for vattn_decode_noalloc.  In host code `scratch` is
+// only a stand-in for the device array: its device address (one per GPU, each
+// holding its own copy) is looked up once per device with that device current
+// and kept in scratch_ptr, which is what the kernels receive.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[VATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // guarded by scratch_mu
+
+// The current device's copy of `scratch`, looked up on its first use.
+vattn_status current_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VATTN_E_HIP;
+    if (dev >= kMaxDevices) return VATTN_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return VATTN_E_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return VATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+vattn_status vattn_decode_noalloc(const vattn_inputs* in, const vattn_cfg* cfg, vattn_outputs* out,
+                                  void* hip_stream) {
+    Shape s{};
+    const vattn_status st = check(in, cfg, &s);
+    if (st != VATTN_OK) return st;
+    if (layout(in, s).total > VATTN_NOALLOC_SCRATCH_BYTES) return VATTN_E_WORKSPACE;  // before any HIP call
+    void* ws = nullptr;
+    const vattn_status sst = current_scratch(&ws);
+    if (sst != VATTN_OK) return sst;
+    return decode_impl(in, cfg, out, ws, VATTN_NOALLOC_SCRATCH_BYTES, hip_stream, nullptr);
 }
 
 vattn_status vattn_decode_profiled(const vattn_inputs* in, const vattn_cfg* cfg,
