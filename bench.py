@@ -8,10 +8,14 @@ eps = delta = 0.05.  Inputs are synthetic and resident in HBM before timing.
 Three copies of the caches are rotated so that no step finds its keys in the
 last-level cache.  The sampling seed changes every step.
 
-Prints one JSON line: heads*tokens/s, the roofline of the dominant kernel
-(per-kernel HIP events over the timed steps; algorithmic bytes from the
-kernel's own token counts), the (eps, delta) violation rate against a dense
-fp32 reference, and the CPU oracle timed on the host cores.
+Prints one JSON line: heads*tokens/s (mean, and the median / p10 / p90 of the
+per-step times), the roofline of the dominant kernel (per-kernel HIP events
+over the timed steps; algorithmic bytes from the kernel's own token counts),
+the whole step's algorithmic HBM rate, a plain device-copy ceiling, the
+(eps, delta) violation rate over 1000 seeds against dense fp64 attention, the
+same rate, step time and HBM rate for the other long-context workloads (flat
+128K, ragged batch of 64, 70B-shaped 64K with an eps sweep), and the CPU oracle
+timed on the host cores.
 """
 import argparse
 import ctypes as C
@@ -26,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode heads·tokens/s at 32K ctx; achieved HBM GB/s; ε-violation rate"
+HOST_CORE_CAP = 16  # the host CPU share of one GPU on the measurement boxes
 
 
 def parse():
@@ -35,17 +40,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--profile", action="store_true",
-                    help="few steps, no CPU baseline or rate (for rocprofv3 runs)")
-    ap.add_argument("--rate-seeds", type=int, default=100)
+                    help="the headline steps only, few of them (for rocprofv3 runs)")
+    ap.add_argument("--rate-seeds", type=int, default=1000,
+                    help="seeds of the (eps, delta) rate of every workload")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other long-context workloads (flat 128K, ragged B64, 70B-shaped 64K)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--base-sweep", default="",
+                    help="comma-separated workloads whose (eps, delta) rate, union density and step time "
+                         "are also measured at base-sample rates of 5, 10 and 20%% of the tail")
     ap.add_argument("--host-kv", action="store_true",
                     help="also time the step with K/V in pinned host memory (adds a host_kv object)")
     ap.add_argument("--pca-basis", action="store_true",
-                    help="also time and rate-check the workload with per-KV-head PCA predictor bases "
-                         "(adds a pca_basis object; its decodes would otherwise mix into a kernel-trace profile)")
+                    help="also time and rate-check the workload with per-KV-head PCA predictor bases")
     ap.add_argument("--hash", action="store_true",
-                    help="also time and rate-check the workload with the hash-signature predictor "
-                         "(adds a hash_predictor object)")
+                    help="also time and rate-check the workload with the hash-signature predictor")
     return ap.parse_args()
 
 
@@ -75,6 +84,198 @@ class HipEvents:
             self.rt.hipEventDestroy(C.c_void_p(h))
 
 
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def clopper_pearson(k, n, conf=0.95):
+    """Two-sided exact binomial interval of a rate k / n."""
+    from scipy.stats import beta
+    a = (1.0 - conf) / 2
+    lo = 0.0 if k == 0 else float(beta.ppf(a, k, n - k + 1))
+    hi = 1.0 if k == n else float(beta.ppf(1 - a, k + 1, n - k))
+    return lo, hi
+
+
+class Device:
+    """One workload on the device: queries, block table, lengths, basis and
+    `copies` independent copies of the K, V and low-rank key caches."""
+
+    def __init__(self, w, dev, copies):
+        import torch
+        import verified_sparse_attention_amd as vsa
+        self.w = w
+        self.q = w.q.to(dev)
+        self.bt = w.block_table.to(dev)
+        self.sl = w.seq_lens.to(dev)
+        self.proj = w.proj.to(dev) if w.proj is not None else None
+        k0, v0 = w.k_cache.to(dev), w.v_cache.to(dev)
+        kt0 = vsa.project_keys(k0, self.proj) if w.cfg["predictor"] == 1 else None
+        ks0 = vsa.sign_keys(k0, self.proj) if w.cfg["predictor"] == 2 else None
+        self.inst = [(k0, v0, kt0, ks0)]
+        for _ in range(copies - 1):
+            self.inst.append(tuple(None if t is None else t.clone() for t in (k0, v0, kt0, ks0)))
+        torch.cuda.synchronize()
+
+    def decoders(self, cfg_dict=None, group_counts=False, workspace=None):
+        import verified_sparse_attention_amd as vsa
+        cfg = dict(self.w.cfg if cfg_dict is None else cfg_dict)
+        out = []
+        ws = workspace
+        for (k, v, kt, ks) in self.inst:
+            d = vsa.Decoder(self.q, k, v, self.bt, self.sl, vsa.Config.from_dict(cfg), max_seq_len=self.w.max_seq_len,
+                            k_lowrank=kt, proj=self.proj, k_sig=ks, want_group_counts=group_counts, workspace=ws)
+            ws = d.workspace
+            out.append(d)
+        return out
+
+
+def time_steps(decs, steps, warm, seed0):
+    """Mean ms per step over exactly `steps` decodes (one event before the first
+    and after every step, so per-step times come from the same run)."""
+    import numpy as np
+    import torch
+    n = len(decs)
+    for s in range(warm):
+        decs[s % n].set_seed(seed0 + 100_000 + s)
+        decs[s % n]()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record()
+    for s in range(steps):
+        dd = decs[s % n]
+        dd.set_seed(seed0 + s)
+        dd()
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return ev[0].elapsed_time(ev[steps]) / steps, per, t_wall
+
+
+def step_spread(per):
+    import numpy as np
+    return {"median_ms": round(float(np.median(per)), 5), "p10_ms": round(float(np.quantile(per, 0.1)), 5),
+            "p90_ms": round(float(np.quantile(per, 0.9)), 5)}
+
+
+def dense_reference(D):
+    """Dense softmax attention in fp64 over every cached token (torch on the
+    device, contiguous operands): the exact quantity the sparse step estimates.
+    Returns lse [B, Hq] and out [B, Hq, d] as fp64 device tensors."""
+    import math
+    import torch
+    w = D.w
+    k, v = D.inst[0][0], D.inst[0][1]
+    B, Hq, Hkv, d = w.B, w.Hq, w.Hkv, w.d
+    G = Hq // Hkv
+    lse = torch.full((B, Hq), -float("inf"), dtype=torch.float64, device=D.q.device)
+    out = torch.zeros(B, Hq, d, dtype=torch.float64, device=D.q.device)
+    with torch.no_grad():
+        for b in range(B):
+            L = int(w.seq_lens[b])
+            if L == 0:
+                continue
+            pages = D.bt[b, :(L + 15) // 16].long()
+            Kb = k[pages].permute(1, 0, 2, 3).reshape(Hkv, -1, d)[:, :L].double().contiguous()
+            qb = (D.q[b].double() / math.sqrt(d)).view(Hkv, G, d).transpose(1, 2).contiguous()
+            s = torch.bmm(Kb, qb).transpose(1, 2).contiguous()  # [Hkv, G, L]
+            del Kb
+            lse[b] = torch.logsumexp(s, dim=-1).reshape(Hq)
+            p = torch.softmax(s, dim=-1)
+            del s
+            Vb = v[pages].permute(1, 0, 2, 3).reshape(Hkv, -1, d)[:, :L].double().contiguous()
+            out[b] = torch.bmm(p, Vb).reshape(Hq, d)
+            del p, Vb
+    return lse, out
+
+
+def rate_run(dec, lse_dense, out_dense, eps, seeds, seed0):
+    """(eps, delta) violations of the denominator over `seeds` decodes, the
+    output-level error and the mean budget and group-union size."""
+    import numpy as np
+    import torch
+    w_shape = tuple(dec.lse.shape)
+    dev = dec.lse.device
+    lse_all = torch.empty((seeds,) + w_shape, dtype=torch.float32, device=dev)
+    oerr = torch.empty((seeds,) + w_shape, dtype=torch.float64, device=dev)
+    nsum = torch.zeros(w_shape, dtype=torch.float64, device=dev)
+    usum = None
+    dn = out_dense.norm(dim=-1)
+    live = torch.isfinite(lse_dense)
+    for s in range(seeds):
+        dec.set_seed(seed0 + s)
+        dec()
+        lse_all[s].copy_(dec.lse)
+        oerr[s] = (dec.out.double() - out_dense).norm(dim=-1) / dn
+        nsum += dec.counts[..., 3].double()
+        if dec.group_counts is not None:
+            g = dec.group_counts[..., 0].double()
+            usum = g if usum is None else usum + g
+    torch.cuda.synchronize()
+    rel = (torch.exp(lse_all.double() - lse_dense) - 1.0).abs()[:, live]
+    viol = int((rel > eps).sum())
+    trials = int(rel.numel())
+    lo, hi = clopper_pearson(viol, trials)
+    e = oerr[:, live].flatten().cpu().numpy()
+    res = {"eps": eps, "rate": round(viol / trials, 5), "violations": viol, "trials": trials, "seeds": seeds,
+           "cp95": [round(lo, 5), round(hi, 5)],
+           "mean_budget": round(float((nsum / seeds)[live].mean()), 1),
+           "output_error": {"rate_above_eps": round(float((e > eps).mean()), 5),
+                            "median": round(float(np.median(e)), 5), "p99": round(float(np.quantile(e, 0.99)), 5)}}
+    return res, (None if usum is None else usum / seeds)
+
+
+def algorithmic_bytes(w, U):
+    """Bytes one step must move: the predictor stream (K~ rows or signatures,
+    plus the page ids) and the K and V rows of each group's union."""
+    import numpy as np
+    L = w.seq_lens.numpy().astype(np.float64)[:, None]
+    row = w.d * w.k_cache.element_size()
+    pred = w.cfg["predictor"]
+    pred_row = w.cfg["rank"] * 2 if pred == 1 else 4 if pred == 2 else row
+    pred_bytes = float(w.Hkv * (L[:, 0] * pred_row + np.ceil(L[:, 0] / 16) * 4).sum())
+    return pred_bytes, pred_bytes + float((U * 2 * row).sum())
+
+
+def workload_leg(name, mk, eps_list, steps, warm, seeds, dev):
+    """Step time, HBM rate and (eps, delta) rates of one more workload."""
+    import numpy as np
+    import torch
+    t0 = time.perf_counter()
+    w = mk()
+    D = Device(w, dev, 3)
+    log("%s: B=%d Hq=%d Hkv=%d L<=%d (inputs %.1f s)" % (name, w.B, w.Hq, w.Hkv, w.max_seq_len,
+                                                          time.perf_counter() - t0))
+    lse_d, out_d = dense_reference(D)
+    res = {"batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.max_seq_len,
+           "total_tokens": int(w.seq_lens.sum()), "heads_tokens_per_step": w.heads_tokens(),
+           "eps_sweep": []}
+    L = w.seq_lens.numpy().astype(np.float64)[:, None]
+    for eps in (eps_list or [w.cfg["eps"]]):
+        cfg = dict(w.cfg, eps=eps)
+        decs = D.decoders(cfg)
+        ms, per, _ = time_steps(decs, steps, warm, 0)
+        gdec = D.decoders(cfg, group_counts=True, workspace=decs[0].workspace)[0]
+        r, U = rate_run(gdec, lse_d, out_d, eps, seeds, 1_000_000)
+        pred_b, step_b = algorithmic_bytes(w, U.cpu().numpy())
+        gbs = step_b / (ms * 1e-3) / 1e9
+        r.update({"ms_per_step": round(ms, 5), **step_spread(per),
+                  "heads_tokens_per_s": round(w.heads_tokens() / (ms * 1e-3), 1),
+                  "step_hbm": {"algorithmic_bytes": round(step_b), "achieved_GBps": round(gbs, 1),
+                               "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                  "union_density": round(float((U.cpu().numpy() / L).mean()), 4)})
+        res["eps_sweep"].append(r)
+        log("%s eps=%g: %.4f ms/step (%.0f GB/s), union density %.3f, violations %d / %d = %.4f, delta %g"
+            % (name, eps, ms, gbs, r["union_density"], r["violations"], r["trials"], r["rate"], w.cfg["delta"]))
+        del decs, gdec
+    res["delta"] = w.cfg["delta"]
+    del D
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -90,9 +291,6 @@ def main():
     import synthetic
     import verified_sparse_attention_amd as vsa
 
-    def log(msg):
-        print("[bench] " + msg, file=sys.stderr, flush=True)
-
     dev = torch.device("cuda:0")
     w = synthetic.WORKLOADS[args.workload]()
     G = w.Hq // w.Hkv
@@ -101,25 +299,13 @@ def main():
     r = w.cfg["rank"]
     log("workload %s: B=%d Hq=%d Hkv=%d d=%d L=%d kv=%s" % (w.name, w.B, w.Hq, w.Hkv, d,
                                                             w.max_seq_len, w.k_cache.dtype))
-    q = w.q.to(dev)
-    bt = w.block_table.to(dev)
-    sl = w.seq_lens.to(dev)
-    proj = w.proj.to(dev) if w.proj is not None else None
-    k0 = w.k_cache.to(dev)
-    v0 = w.v_cache.to(dev)
-    kt0 = vsa.project_keys(k0, proj) if w.cfg["predictor"] == 1 else None
     n_inst = 3
-    inst = [(k0, v0, kt0)] + [(k0.clone(), v0.clone(), kt0.clone() if kt0 is not None else None)
-                              for _ in range(n_inst - 1)]
-    decs, pdecs = [], []
-    ws = None
-    for (k, v, kt) in inst:
-        for lst, gc in ((decs, False), (pdecs, True)):
-            dd = vsa.Decoder(q, k, v, bt, sl, vsa.Config.from_dict(w.cfg), max_seq_len=w.max_seq_len,
-                             k_lowrank=kt, proj=proj, want_group_counts=gc, workspace=ws)
-            ws = dd.workspace
-            lst.append(dd)
-    torch.cuda.synchronize()
+    D = Device(w, dev, n_inst)
+    q, bt, sl, proj = D.q, D.bt, D.sl, D.proj
+    k0, v0, kt0 = D.inst[0][0], D.inst[0][1], D.inst[0][2]
+    decs = D.decoders()
+    ws = decs[0].workspace
+    pdecs = D.decoders(group_counts=True, workspace=ws)
 
     steps, warm = (min(args.steps, 5), min(args.warmup, 2)) if args.profile else (args.steps, args.warmup)
     if args.profile:
@@ -131,28 +317,12 @@ def main():
         cal_dst.copy_(cal_src)
         torch.cuda.synchronize()
         del cal_src, cal_dst
-    for s in range(warm):
-        decs[s % n_inst].set_seed(10_000 + s)
-        decs[s % n_inst]()
-    torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` decode steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record()
-    for s in range(steps):
-        dd = decs[s % n_inst]
-        dd.set_seed(s)
-        dd()
-    e1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_per_step = e0.elapsed_time(e1) / steps
+    ms_per_step, per_step, t_wall = time_steps(decs, steps, warm, 0)
     heads_tokens = w.heads_tokens()
     value = heads_tokens / (ms_per_step * 1e-3)
-    log("%.4f ms/step, %.4g heads*tokens/s (wall %.4f ms/step)" % (ms_per_step, value,
-                                                                   t_wall * 1e3 / steps))
+    log("%.4f ms/step, %.4g heads*tokens/s (wall %.4f ms/step)" % (ms_per_step, value, t_wall * 1e3 / steps))
 
     # ---- per-kernel durations with events on the launch stream, same steps
     nst = vsa.NUM_STAGES
@@ -179,14 +349,12 @@ def main():
     # ---- algorithmic bytes per launch (mean over the timed steps)
     ncg = (w.max_seq_len + 1023) // 1024
     row = d * esize
-    pred_row = r * 2 if w.cfg["predictor"] == 1 else row
-    pred_bytes = float(w.Hkv * (L * pred_row + np.ceil(L / 16) * 4).sum())
+    pred_bytes, step_bytes = algorithmic_bytes(w, U)
     base_bytes = float((Bc * row + Bc * G * 4).sum())
     # V rows of the union, K rows not scored by the base pass, cached scores,
     # chunk partials written
     gather_bytes = float((U * row + (U - Bc) * row + Bc * G * 4).sum()
                          + w.B * w.Hq * ncg * (d + 2) * 4)
-    step_bytes = pred_bytes + float((U * 2 * row).sum())
     per_kernel_bytes = {"predict": pred_bytes, "base": base_bytes, "gather": gather_bytes}
     names = vsa.STAGES
     dom = int(np.argmax(stage_ms))
@@ -196,6 +364,10 @@ def main():
     log("mean |U_g| %.0f (density %.3f), |B_g| %.0f" % (U.mean(), (U / L).mean(), Bc.mean()))
     dom_bytes = per_kernel_bytes.get(dom_name)
     achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9 if dom_bytes else None
+    kernel_frac = {}
+    for k_, b_ in per_kernel_bytes.items():
+        t_ = stage_ms[names.index(k_)] * 1e-3
+        kernel_frac[k_] = round(b_ / t_ / 1e9 / HBM_PEAK_GBS, 4) if t_ > 0 else None
 
     # HBM bytes per launch from the committed counter summary, if it was taken
     # with the current kernel sources
@@ -215,6 +387,22 @@ def main():
                 "kernel_us": round(float(stage_ms[dom]) * 1e3, 2)}
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # ---- a plain device copy (read + write of 1 GiB): the box's practical ceiling
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log("device copy %.0f GB/s (read + write)" % copy_gbs)
+
     result = {"metric": METRIC, "value": round(value, 1), "unit": "heads·tokens/s", "n_gpus": 1,
               "steps": steps, "warmup": warm, "ms_per_step": round(ms_per_step, 5),
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -223,23 +411,24 @@ def main():
                          "head_dim": d, "seq_len": w.max_seq_len,
                          "kv_dtype": "bf16" if esize == 2 else "f32", "predictor_rank": r,
                          "sinks": w.cfg["sinks"], "window": w.cfg["window"],
-                         "topk_ppm": w.cfg["topk_ppm"], "eps": w.cfg["eps"], "delta": w.cfg["delta"],
+                         "topk_ppm": w.cfg["topk_ppm"], "base_ppm": w.cfg["base_ppm"],
+                         "eps": w.cfg["eps"], "delta": w.cfg["delta"],
                          "cache_copies_rotated": n_inst},
+              "step_time": step_spread(per_step),
               "roofline": roofline,
               "step_hbm": {"algorithmic_bytes": round(step_bytes), "achieved_GBps": round(step_gbs, 1),
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                           "union_density": round(float((U / L).mean()), 4)},
+                           "union_density": round(float((U / L).mean()), 4),
+                           "kernel_frac": kernel_frac},
+              "copy_ceiling_GBps": round(copy_gbs, 1),
               "stage_us": stages}
 
     # ---- key-side maintenance: append each sequence's newest token (K, V and
     # its low-rank key row).  Rewriting the current newest token with its own
     # values keeps the caches unchanged.
-    if kt0 is not None:
+    if kt0 is not None and not args.profile:
         pos = (sl - 1).to(torch.int32)
-        rows = []
-        for b in range(w.B):
-            p_ = int(w.seq_lens[b]) - 1
-            rows.append(int(w.block_table[b, p_ // 16]))
+        rows = [int(w.block_table[b, (int(w.seq_lens[b]) - 1) // 16]) for b in range(w.B)]
         pages = torch.tensor(rows, device=dev).long()
         slots = (pos.long() % 16)
         k_new = k0[pages, :, slots].contiguous()
@@ -283,6 +472,7 @@ def main():
                               "TFLOPs": round(g_flops / g_us / 1e6, 1),
                               "note": "calibration of per-KV-head predictor bases, not part of the decode step"}
         log("key gram %.1f us (%.0f GB/s)" % (g_us, g_bytes / g_us / 1e3))
+        del gram, gws
 
     if args.host_kv and not args.profile:
         # ---- host-resident K/V: the caches in pinned, device-mapped host memory,
@@ -335,125 +525,69 @@ def main():
         del hdec, kh, vh, dst
 
     if not args.profile:
-        # ---- (eps, delta): denominator relative error vs a dense fp32 reference
-        with torch.no_grad():
-            lse_dense = torch.empty(w.B, w.Hq, dtype=torch.float64, device=dev)
-            out_dense = torch.empty(w.B, w.Hq, d, dtype=torch.float64, device=dev)
-            scale = 1.0 / np.sqrt(d)
-            for b in range(w.B):
-                Lb = int(w.seq_lens[b])
-                pages = bt[b, :(Lb + 15) // 16].long()
-                Kb = k0[pages].permute(1, 0, 2, 3).reshape(w.Hkv, -1, d)[:, :Lb].float()
-                Kb = Kb.repeat_interleave(G, 0).contiguous()
-                s_ = torch.bmm(Kb, (q[b].float() * scale).unsqueeze(-1).contiguous()).squeeze(-1)
-                lse_dense[b] = torch.logsumexp(s_.double(), dim=-1)
-                Vb = v0[pages].permute(1, 0, 2, 3).reshape(w.Hkv, -1, d)[:, :Lb].double()
-                Vb = Vb.repeat_interleave(G, 0).contiguous()
-                p_ = torch.softmax(s_.double(), dim=-1).unsqueeze(1).contiguous()
-                out_dense[b] = torch.bmm(p_, Vb).squeeze(1)
-                del Kb, s_, Vb, p_
-        dn = out_dense.norm(dim=-1)
+        # ---- (eps, delta): denominator relative error against dense fp64 attention
+        lse_dense, out_dense = dense_reference(D)
+        er, _ = rate_run(decs[0], lse_dense, out_dense, w.cfg["eps"], args.rate_seeds, 1_000_000)
+        result["eps_violation"] = {k_: er[k_] for k_ in ("rate", "violations", "trials", "seeds", "cp95")}
+        result["eps_violation"].update({"delta": w.cfg["delta"], "reference": "dense attention in fp64"})
+        result["output_error"] = dict(er["output_error"], note="the budget bounds the denominator only; "
+                                      "this is the measured relative L2 error of the outputs against dense fp64")
+        log("eps violations %d / %d = %.4f (95%% CI %s); output rel. error median %.4f"
+            % (er["violations"], er["trials"], er["rate"], er["cp95"], er["output_error"]["median"]))
 
-        def out_rel(dec):
-            # relative L2 error of each head's output against dense attention
-            return (dec.out.double() - out_dense).norm(dim=-1) / dn
-
-        def out_summary(errs):
-            e = torch.cat(errs).flatten().cpu().numpy()
-            return {"rate_above_eps": round(float((e > w.cfg["eps"]).mean()), 5),
-                    "median": round(float(np.median(e)), 5), "p99": round(float(np.quantile(e, 0.99)), 5),
-                    "reference": "dense attention, fp64 softmax and V products"}
-
-        viol = trials = 0
-        oerr = []
-        dd = decs[0]
-        for s in range(args.rate_seeds):
-            dd.set_seed(1_000_000 + s)
-            dd()
-            rel = (torch.exp(dd.lse.double() - lse_dense) - 1.0).abs()
-            viol += int((rel > w.cfg["eps"]).sum())
-            trials += rel.numel()
-            oerr.append(out_rel(dd))
-        torch.cuda.synchronize()
-        result["eps_violation"] = {"rate": round(viol / trials, 5), "violations": viol,
-                                   "trials": trials, "seeds": args.rate_seeds,
-                                   "delta": w.cfg["delta"], "reference": "dense fp32 scores, fp64 logsumexp"}
-        result["output_error"] = dict(out_summary(oerr), note="the budget bounds the denominator only; "
-                                      "this is the measured relative L2 error of the outputs")
-        log("eps violations %d / %d; output rel. error median %.4f, above eps %.4f"
-            % (viol, trials, result["output_error"]["median"], result["output_error"]["rate_above_eps"]))
+        # ---- the other long-context workloads: throughput, HBM rate and the
+        # (eps, delta) rate at full size (the 70B-shaped one over an eps sweep)
+        if not args.no_configs and args.workload == "llama8b_32k":
+            result["workloads"] = {}
+            legs = [("flat_128k", synthetic.flat_128k, None), ("ragged_b64", synthetic.ragged_b64, None),
+                    ("wide_gqa_64k", synthetic.wide_gqa_64k, [0.01, 0.02, 0.05, 0.1])]
+            for name, mk, eps_list in legs:
+                result["workloads"][name] = workload_leg(name, mk, eps_list, max(10, steps // 2), warm,
+                                                         args.rate_seeds, dev)
+        # ---- the base-sample rate: 5, 10, 20% of the tail
+        for name in [x for x in args.base_sweep.split(",") if x]:
+            sweep = []
+            for bp in (50000, 100000, 200000):
+                mk = synthetic.WORKLOADS[name]
+                res = workload_leg("%s base %d%%" % (name, bp // 10000), lambda mk=mk, bp=bp: mk(base_ppm=bp),
+                                   None, 20, warm, args.rate_seeds, dev)
+                sweep.append(dict(res["eps_sweep"][0], base_ppm=bp))
+            result.setdefault("base_sweep", {})[name] = sweep
 
         # ---- the same workload with a per-KV-head PCA predictor basis (the r
         # leading eigenvectors of each head's key Gram matrix over the first half
-        # of every sequence, as a basis fitted at prefill; host eigensolve):
-        # step time, union density and the (eps, delta) rate.  Context only; the
-        # headline value above uses the workload's random basis.
+        # of every sequence, as a basis fitted at prefill; host eigensolve).
+        # Context only; the headline value above uses the workload's random basis.
         if args.pca_basis and kt0 is not None and k0.dtype == torch.bfloat16:
             gram = vsa.key_gram(k0, bt, (sl // 2).contiguous(), w.max_seq_len)
             _, evec = torch.linalg.eigh(gram.double().cpu())
             p_pca = evec[:, :, -r:].flip(-1).float().contiguous().to(dev)  # [Hkv, d, r], descending
             pca_decs = []
-            for (k, v, _) in inst:
+            for (k, v, _, _) in D.inst:
                 pca_decs.append(vsa.Decoder(q, k, v, bt, sl, vsa.Config.from_dict(w.cfg), max_seq_len=w.max_seq_len,
-                                         k_lowrank=vsa.project_keys(k, p_pca), proj=p_pca,
-                                         want_group_counts=True, workspace=ws))
-            for s in range(warm):
-                pca_decs[s % n_inst].set_seed(20_000 + s)
-                pca_decs[s % n_inst]()
-            torch.cuda.synchronize()
-            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            p0.record()
-            for s in range(steps):
-                pca_decs[s % n_inst].set_seed(30_000 + s)
-                pca_decs[s % n_inst]()
-            p1.record()
-            torch.cuda.synchronize()
-            pca_ms = p0.elapsed_time(p1) / steps
-            pv = pt = 0
-            perr = []
-            pd = pca_decs[0]
-            for s in range(args.rate_seeds):
-                pd.set_seed(1_000_000 + s)
-                pd()
-                rel = (torch.exp(pd.lse.double() - lse_dense) - 1.0).abs()
-                pv += int((rel > w.cfg["eps"]).sum())
-                pt += rel.numel()
-                perr.append(out_rel(pd))
-            torch.cuda.synchronize()
-            Up = pd.group_counts[:, :, 0].double().cpu().numpy()
+                                            k_lowrank=vsa.project_keys(k, p_pca), proj=p_pca,
+                                            want_group_counts=True, workspace=ws))
+            pca_ms, pper, _ = time_steps(pca_decs, steps, warm, 30_000)
+            pr, Up = rate_run(pca_decs[0], lse_dense, out_dense, w.cfg["eps"], args.rate_seeds, 1_000_000)
             result["pca_basis"] = {
                 "ms_per_step": round(pca_ms, 5), "value": round(heads_tokens / (pca_ms * 1e-3), 1),
-                "unit": "heads·tokens/s", "union_density": round(float((Up / L).mean()), 4),
-                "eps_violation": {"rate": round(pv / pt, 5), "violations": pv, "trials": pt,
-                                  "seeds": args.rate_seeds, "delta": w.cfg["delta"]},
-                "output_error": out_summary(perr),
+                "unit": "heads·tokens/s", "union_density": round(float((Up.cpu().numpy() / L).mean()), 4),
+                "eps_violation": {k_: pr[k_] for k_ in ("rate", "violations", "trials", "seeds", "cp95")},
+                "output_error": pr["output_error"],
                 "note": "same workload with a per-KV-head basis: the %d leading eigenvectors of vattn_key_gram "
                         "over the first half of each sequence (a Loki-style basis fitted at prefill)" % r}
-            log("pca basis: %.4f ms/step, union density %.3f, eps violations %d / %d"
-                % (pca_ms, float((Up / L).mean()), pv, pt))
+            log("pca basis: %.4f ms/step, eps violations %d / %d" % (pca_ms, pr["violations"], pr["trials"]))
             del pca_decs
 
         # ---- the same workload with the hash-signature predictor (32 sign
         # bits per key under the workload's random directions, 4 bytes per
-        # token instead of a rank-r row): step and per-kernel time, union
-        # density and the (eps, delta) rate.  Context only.
+        # token instead of a rank-r row).  Context only.
         if args.hash and proj is not None and r == 32:
             hcfg = vsa.Config.from_dict(dict(w.cfg, predictor=vsa.PRED_HASH, rank=32))
             hdecs = [vsa.Decoder(q, k, v, bt, sl, hcfg, max_seq_len=w.max_seq_len, proj=proj,
                                  k_sig=vsa.sign_keys(k, proj), want_group_counts=True, workspace=ws)
-                     for (k, v, _) in inst]
-            for s in range(warm):
-                hdecs[s % n_inst].set_seed(40_000 + s)
-                hdecs[s % n_inst]()
-            torch.cuda.synchronize()
-            h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            h0.record()
-            for s in range(steps):
-                hdecs[s % n_inst].set_seed(50_000 + s)
-                hdecs[s % n_inst]()
-            h1.record()
-            torch.cuda.synchronize()
-            hash_ms = h0.elapsed_time(h1) / steps
+                     for (k, v, _, _) in D.inst]
+            hash_ms, hper, _ = time_steps(hdecs, steps, warm, 50_000)
             hev = HipEvents((nst + 1) * steps)
             hst = np.zeros(nst)
             for s in range(steps):
@@ -465,46 +599,52 @@ def main():
                     hst[k] += hev.elapsed((nst + 1) * s + k, (nst + 1) * s + k + 1)
             hev.close()
             hst /= steps
-            hv = ht = 0
-            herr = []
-            hd = hdecs[0]
-            for s in range(args.rate_seeds):
-                hd.set_seed(2_000_000 + s)
-                hd()
-                rel = (torch.exp(hd.lse.double() - lse_dense) - 1.0).abs()
-                hv += int((rel > w.cfg["eps"]).sum())
-                ht += rel.numel()
-                herr.append(out_rel(hd))
-            torch.cuda.synchronize()
-            Uh = hd.group_counts[:, :, 0].double().cpu().numpy()
-            hpred_bytes = float(w.Hkv * (L * 4 + np.ceil(L / 16) * 4).sum())
+            hr, Uh = rate_run(hdecs[0], lse_dense, out_dense, w.cfg["eps"], args.rate_seeds, 2_000_000)
+            hpred_bytes = float(w.Hkv * (L[:, 0] * 4 + np.ceil(L[:, 0] / 16) * 4).sum())
             result["hash_predictor"] = {
                 "ms_per_step": round(hash_ms, 5), "value": round(heads_tokens / (hash_ms * 1e-3), 1),
-                "unit": "heads·tokens/s", "union_density": round(float((Uh / L).mean()), 4),
+                "unit": "heads·tokens/s", "union_density": round(float((Uh.cpu().numpy() / L).mean()), 4),
                 "stage_us": {names[k]: round(float(hst[k]) * 1e3, 2) for k in range(nst)},
                 "predict_bytes": hpred_bytes,
-                "eps_violation": {"rate": round(hv / ht, 5), "violations": hv, "trials": ht,
-                                  "seeds": args.rate_seeds, "delta": w.cfg["delta"]},
-                "output_error": out_summary(herr),
+                "eps_violation": {k_: hr[k_] for k_ in ("rate", "violations", "trials", "seeds", "cp95")},
+                "output_error": hr["output_error"],
                 "note": "same workload, top-k from 32-bit random-hyperplane key signatures "
                         "(vattn_sign_keys) scored by shared bits"}
-            log("hash predictor: %.4f ms/step, predict %.1f us, union density %.3f, eps violations %d / %d"
-                % (hash_ms, hst[0] * 1e3, float((Uh / L).mean()), hv, ht))
+            log("hash predictor: %.4f ms/step, eps violations %d / %d" % (hash_ms, hr["violations"], hr["trials"]))
             del hdecs
 
     if not args.profile and not args.no_cpu_baseline:
         import oracle
-        cores = min(len(os.sched_getaffinity(0)), 16)
+        cores = min(len(os.sched_getaffinity(0)), HOST_CORE_CAP)
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+        except OSError:
+            pass
         arrays = w.oracle_arrays()
         cpu_cfg = dict(w.cfg, seed=0)
         t = time.perf_counter()
         oracle.decode(**arrays, cfg=cpu_cfg, nthreads=cores, want_idx=False)
         dt = time.perf_counter() - t
+        # single thread on a sample of the groups (the per-group work is uniform here)
+        n1 = 4
+        grp = [(b, g) for b in range(w.B) for g in range(w.Hkv)][:n1]
+        t = time.perf_counter()
+        oracle.decode(**arrays, cfg=cpu_cfg, nthreads=1, want_idx=False, groups=grp)
+        dt1 = (time.perf_counter() - t) * (w.B * w.Hkv) / n1
         result["cpu_baseline"] = {"value": round(heads_tokens / dt, 1), "unit": "heads·tokens/s",
                                   "cores": cores, "kind": "oracle",
-                                  "sample": "one full decode step of %s (all %d (batch, KV head) groups, "
-                                            "seed 0), %.2f s wall" % (w.name, w.B * w.Hkv, dt)}
-        log("cpu oracle %.2f s on %d threads" % (dt, cores))
+                                  "sample": "one full decode step of %s (all %d (batch, KV head) groups, seed 0), "
+                                            "%.2f s wall on %d threads (the host's affinity set, capped at %d, "
+                                            "the CPU share of one GPU)" % (w.name, w.B * w.Hkv, dt, cores,
+                                                                           HOST_CORE_CAP),
+                                  "cpu_model": model, "host_threads_available": len(os.sched_getaffinity(0)),
+                                  "single_thread": {"value": round(heads_tokens / dt1, 1),
+                                                    "sample": "%d of %d groups on one thread, %.2f s, scaled to "
+                                                              "the whole step" % (n1, w.B * w.Hkv, dt1 * n1 /
+                                                                                  (w.B * w.Hkv))}}
+        log("cpu oracle %.2f s on %d threads, %.2f s on one (%s)" % (dt, cores, dt1, model))
     print(json.dumps(result), flush=True)
 
 

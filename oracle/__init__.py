@@ -76,6 +76,8 @@ def _load():
             lib.orc_decode.restype = C.c_int
             lib.orc_decode.argtypes = [C.POINTER(OrcCfg)] + [C.c_int] * 7 + [P] * 4 + [C.c_int] + \
                 [P] * 3 + [C.c_int, C.c_int] + [P] * 5 + [C.c_int] + [P] * 3
+            lib.orc_dense.restype = C.c_int
+            lib.orc_dense.argtypes = [C.c_int] * 6 + [P] * 6 + [C.c_int, C.c_int, P, P]
             lib.orc_pdot.restype = C.c_float
             lib.orc_pdot.argtypes = [P, C.c_int, P, C.c_int, C.c_int]
             lib.orc_pexp.restype = C.c_float
@@ -237,3 +239,32 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
     if want_pred:
         res["pred"] = pred
     return res
+
+
+def dense(*, q, k_cache, v_cache, block_table, seq_lens, groups=None, nthreads=1, want_out=True, **_):
+    """Dense fp64 softmax attention over every cached token of every head (the
+    exact target): returns dict(lse_dense [B, Hq], out_dense [B, Hq, d] or None).
+    Takes the same arrays as decode (extra keys such as proj are ignored)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, Hq, d = q.shape
+    kv_bf16 = k_cache.dtype == np.uint16
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    Hkv = k_cache.shape[1]
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    out = np.zeros((B, Hq, d), dtype=np.float64) if want_out else None
+    if groups is None:
+        garr, ng = None, 0
+    else:
+        garr = np.array([b * Hkv + g for (b, g) in groups], dtype=np.int32)
+        ng = garr.shape[0]
+    rc = _load().orc_dense(B, Hq, Hkv, d, block_table.shape[1], int(kv_bf16), _ptr(q), _ptr(k_cache),
+                           _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(garr), ng, int(nthreads),
+                           _ptr(lse), _ptr(out))
+    if rc == 5:
+        raise ValueError("oracle refused a non-finite input (q, or a cached K or V row)")
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return dict(lse_dense=lse, out_dense=out)

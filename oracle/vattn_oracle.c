@@ -569,3 +569,50 @@ int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks
     }
     return bad ? 5 : 0;
 }
+
+/*
+ * Dense fp64 softmax attention over all L tokens of every query head of the
+ * (b, g) groups in `groups` (all when NULL): the exact quantity the sparse
+ * estimate approximates (scores q . K_i / sqrt(d), weights 1).  lse_dense
+ * [B*Hq]; out_dense [B*Hq][d] or NULL.  Returns 0, 1 or 2 for bad arguments,
+ * 5 for a non-finite input.
+ */
+int orc_dense(int B, int Hq, int Hkv, int d, int max_blocks, int kv_bf16, const float* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, const int32_t* groups,
+              int n_groups, int nthreads, double* lse_dense, double* out_dense) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !lse_dense) return 1;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0) return 2;
+    if (!all_finite(q, (int64_t)B * Hq * d)) return 5;
+    orc_ctx cx;
+    memset(&cx, 0, sizeof(cx));
+    cx.B = B; cx.Hq = Hq; cx.Hkv = Hkv; cx.d = d; cx.max_blocks = max_blocks; cx.kv_bf16 = kv_bf16;
+    cx.block_table = block_table; cx.seq_lens = seq_lens;
+    const int G = Hq / Hkv;
+    int total = groups ? n_groups : B * Hkv;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (int t = 0; t < total; ++t) {
+        int bg = groups ? groups[t] : t;
+        int b = bg / Hkv, g = bg % Hkv, L = seq_lens[b];
+        float* K = (float*)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * d);
+        float* V = (float*)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * d);
+        int* all = (int*)malloc(sizeof(int) * (L > 0 ? L : 1));
+        double* w1 = (double*)malloc(sizeof(double) * (L > 0 ? L : 1));
+        double* od = (double*)malloc(sizeof(double) * d);
+        load_rows(&cx, k_cache, b, g, L, K);
+        load_rows(&cx, v_cache, b, g, L, V);
+        if (!all_finite(K, (int64_t)L * d) || !all_finite(V, (int64_t)L * d)) {
+            bad |= 5;
+        } else {
+            for (int i = 0; i < L; ++i) { all[i] = i; w1[i] = 1.0; }
+            for (int hl = 0; hl < G; ++hl) {
+                int64_t bh = (int64_t)b * Hq + g * G + hl;
+                attend_fp64(q + bh * d, K, V, d, all, w1, L, od, &lse_dense[bh]);
+                if (out_dense) memcpy(out_dense + bh * d, od, sizeof(double) * d);
+            }
+        }
+        free(K); free(V); free(all); free(w1); free(od);
+    }
+    return bad ? 5 : 0;
+}
