@@ -119,7 +119,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, sc, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2, total;
+    size_t cand, bits, hs, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -133,8 +133,6 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHq * s.words * sizeof(uint32_t));
     L.hs = off;
     off += align_up(BHq * sizeof(vattn::HeadState));
-    L.sc = off;
-    off += align_up(BHkv * static_cast<size_t>(in->max_seq_len) * s.G * sizeof(float));
     L.cmax = off;
     off += align_up(BHq * s.ncg * sizeof(float));
     L.part = off;
@@ -246,7 +244,6 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
     p.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
     p.hs = reinterpret_cast<vattn::HeadState*>(ws + L.hs);
-    p.sc = reinterpret_cast<float*>(ws + L.sc);
     p.cmax = reinterpret_cast<float*>(ws + L.cmax);
     p.part = reinterpret_cast<float*>(ws + L.part);
     p.soff = reinterpret_cast<uint32_t*>(ws + L.soff);

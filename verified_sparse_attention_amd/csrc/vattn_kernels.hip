@@ -764,7 +764,6 @@ struct HeadView {
 
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
-    __shared__ int tok[kGatherChunk];
     __shared__ uint32_t tmeta[kGatherChunk];
     __shared__ uint32_t trow[kGatherChunk];
     __shared__ uint32_t wsum[kChunkThreads / 64];
@@ -826,7 +825,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (m4[e]) {
-            tok[pos] = 4 * qd + e;
             tmeta[pos] = m4[e];
             trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
             lmeta[pos] = m4[e];
@@ -839,7 +837,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     __syncthreads();
 
     // pinned scores for all G heads of each listed token: the G sums of a row
-    // are spread over its lanes, each finished (max, two stores) by one lane
+    // are spread over its lanes, each finished (max, store) by one lane.  The
+    // scores are stored once, in list order: the budget reads them so, and the
+    // gather finds a token's scores at its position in this (ascending) list
     constexpr int LPT = D / 8, TPW = 64 / LPT;
     using SP = Spread<G, LPT>;
     constexpr int NH = SP::NH;
@@ -858,13 +858,12 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
     const KVT* kbase = static_cast<const KVT*>(P.k);
-    float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
     float* lsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
     const int n = static_cast<int>(cnt);
     constexpr int kBU = kBaseUnroll;
     for (int base = wave * TPW * kBU; base < n; base += nwaves * TPW * kBU) {
         Raw8 kr[kBU];
-        int tk[kBU], xl[kBU];
+        int xl[kBU];
         uint32_t mk[kBU];
 #pragma unroll
         for (int u = 0; u < kBU; ++u) {
@@ -872,7 +871,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
             const bool act = x < n;
             const int xs = act ? x : 0;
             xl[u] = xs;
-            tk[u] = tok[xs];
             mk[u] = act ? tmeta[xs] : 0u;
             load_raw_nt(kbase + static_cast<size_t>(trow[xs]) * D + 8 * j, kr[u]);
         }
@@ -888,8 +886,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 #pragma unroll
                 for (int e = 0; e < NH; ++e) {
                     if ((mk[u] >> hsel[e]) & 1u) lmax[e] = fmaxf(lmax[e], sv[e]);
-                    scrow[static_cast<size_t>(tk[u]) * G + hsel[e]] = sv[e];  // by token, for the gather
-                    lsc[static_cast<size_t>(xl[u]) * G + hsel[e]] = sv[e];    // in list order, for the budget
+                    lsc[static_cast<size_t>(xl[u]) * G + hsel[e]] = sv[e];
                 }
             }
         }
@@ -1139,7 +1136,6 @@ __device__ __forceinline__ int gather_group(const Plan& P, int tid) {
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gather(Plan P) {
     constexpr int NW = kChunkThreads / 64;
-    __shared__ int tok[kGatherChunk];
     __shared__ uint32_t tmeta[kGatherChunk];
     __shared__ uint32_t trow[kGatherChunk];
     __shared__ float sp[G][kGatherChunk];  // scores, then weights
@@ -1177,7 +1173,13 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
     __syncthreads();
 
-    // membership: meta = final mask | fixed mask << 8 | score cached << 16
+    // membership: meta = final mask | fixed mask << 8 | score cached << 16.
+    // "Cached" is the base pass's own membership test (fixed, or base sample,
+    // for some head of the group), so the cached tokens of the chunk, ascending,
+    // are exactly the base pass's list and a cached token's scores sit at its
+    // rank among them.  Every cached token is listed, even one that no head's
+    // final set holds (a forced budget below the base sample): it then carries
+    // weight 0.
     uint32_t m4[4] = {0, 0, 0, 0};
     uint32_t mine = 0;
     if (live4) {
@@ -1197,34 +1199,40 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 fxm |= fx ? (1u << h) : 0u;
                 cached |= (fx || sb) ? 1u : 0u;
             }
-            m4[e] = fin ? (fin | (fxm << 8) | (cached << 16)) : 0u;
-            mine += fin ? (cached ? 0x10000u : 1u) : 0u;  // uncached count | cached count << 16
+            m4[e] = (fin || cached) ? (fin | (fxm << 8) | (cached << 16)) : 0u;
+            mine += cached ? 0x10000u : (fin ? 1u : 0u);  // uncached count | cached count << 16
         }
     }
     // list: the members whose scores still need their K rows first, [0, nu),
-    // then those with cached scores, [nu, n); both counts fit 16 bits
+    // then the cached tokens in the base pass's order, [nu, n); both counts fit
+    // 16 bits
     uint32_t cnt;
     const uint32_t pre = block_excl_scan(mine, wsum, cnt);
     const int nu = static_cast<int>(cnt & 0xFFFFu);
     uint32_t pu = pre & 0xFFFFu, pc = static_cast<uint32_t>(nu) + (pre >> 16);
+    int nfin = 0;  // members of some head's final set, for the byte accounting
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (m4[e]) {
             const uint32_t pos = ((m4[e] >> 16) & 1u) ? pc++ : pu++;
-            tok[pos] = 4 * qd + e;
             tmeta[pos] = m4[e];
             trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
+            nfin += (m4[e] & 0xFFu) ? 1 : 0;
         }
     const int n = nu + static_cast<int>(cnt >> 16);
-    if (tid == 0 && P.gcounts && n) atomicAdd(&P.gcounts[2 * bg], n);
+    if (P.gcounts) {  // block-uniform
+        for (int o = 32; o >= 1; o >>= 1) nfin += __shfl_xor(nfin, o, 64);
+        if (lane == 0 && nfin) atomicAdd(&P.gcounts[2 * bg], nfin);
+    }
     __syncthreads();
 
     // (1) scores into LDS (-inf for heads the token does not belong to).
-    // Tokens of the base pass take their cached pinned scores (independent
-    // loads, one pass); the others are scored from their K rows below.
+    // Tokens of the base pass take their pinned scores from its list (entry
+    // x - nu, contiguous loads, one pass); the others are scored from their K
+    // rows below.
     constexpr int LPT = D / 8, TPW = 64 / LPT;
     const int j = lane % LPT, slot = lane / LPT;
-    const float* scrow = P.sc + static_cast<size_t>(bg) * P.max_seq_len * G;
+    const float* bsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
     const KVT* kbase = static_cast<const KVT*>(P.k);
     {
         constexpr int PER = kGatherChunk / kChunkThreads;  // list entries per thread
@@ -1234,10 +1242,9 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         for (int e = 0; e < PER; ++e) {
             const int x = nu + tid + e * nthr;
             mm[e] = x < n ? tmeta[x] : 0u;
-            const bool cached = (mm[e] >> 16) & 1u;
-            const size_t at = static_cast<size_t>(cached ? tok[x] : 0) * G;
+            const size_t at = static_cast<size_t>(x < n ? x - nu : 0) * G;
 #pragma unroll
-            for (int h = 0; h < G; ++h) v[e][h] = cached ? scrow[at + h] : 0.0f;
+            for (int h = 0; h < G; ++h) v[e][h] = x < n ? bsc[at + h] : 0.0f;
         }
         bool over = false;
 #pragma unroll

@@ -63,13 +63,13 @@ struct Plan {
     uint64_t* cand;  // [B*Hq][ncp][kcap] composite (score key, ~index)
     uint32_t* bits;  // [B*Hq][words] fixed-set membership bitmap
     HeadState* hs;   // [B*Hq]
-    float* sc;       // [B*Hkv][max_seq_len][G] pinned exact scores (base-sample union)
     float* cmax;     // [B*Hq][ncg] chunk max of pinned scores
     float* part;     // [B*Hq][ncg][d + 2] online-softmax partials (m, l, acc[d])
     uint32_t* soff;  // [B*Hkv][ncp][kSampBins + 1] bin offsets of each chunk's middle tokens
     int32_t* slist;  // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
     float* bsc;      // [B*Hkv][ncg][cg][G] pinned scores of the base-pass members, in list order
+                     // (ascending token order within the chunk; read by budget and gather)
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token

@@ -67,6 +67,29 @@ def _find(pattern):
     return hits[0]
 
 
+def _grid_rows(trace_dir):
+    """Per (decode-step kernel, workload launch) statistics from the kernel
+    trace.  Dispatches are taken in order; every decode step starts with a
+    k_predict, whose grid names the workload's launch configuration, and the
+    step's other kernels are attributed to it.  So the headline workload's
+    select, budget and combine are told from another workload's with the same
+    number of heads."""
+    path = _find(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    acc = collections.OrderedDict()
+    tag = None
+    for r in rows:
+        st = _stage(r["Kernel_Name"])
+        if st is None or st == "k_project":
+            continue
+        grid = tuple(int(r["Grid_Size_%s" % a]) // max(int(r["Workgroup_Size_%s" % a]), 1) for a in "XYZ")
+        if st == "k_predict":
+            tag = "predict%s" % (grid,)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        acc.setdefault((_short(r["Kernel_Name"]), grid, tag), []).append(dur)
+    return acc
+
+
 def stats(args):
     path = _find(os.path.join(args.trace, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
@@ -75,13 +98,27 @@ def stats(args):
              "# command: %s" % args.cmd,
              "# kernel sources digest: %s" % _build.source_hash(),
              "# durations in microseconds; every dispatch of the run is counted "
-             "(warm-up, timed, per-stage-timed and rate-check steps)",
+             "(warm-up, timed, per-stage-timed and rate-check steps of every workload)",
              "%-40s %7s %10s %10s %10s %7s" % ("kernel", "calls", "mean_us", "min_us", "max_us", "share")]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append("%-40s %7d %10.2f %10.2f %10.2f %6.1f%%" % (
             _short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             100.0 * float(r["TotalDurationNs"]) / total))
+    try:
+        grid = _grid_rows(args.trace)
+    except SystemExit:
+        grid = {}
+    if grid:
+        lines += ["", "# decode-step kernels by workload launch: grid in workgroups, step = the k_predict grid "
+                      "of the decode step the dispatch belongs to; the headline workload's step is marked *",
+                  "%-34s %-16s %-26s %7s %9s %9s %9s" % ("kernel", "grid", "step", "calls", "mean_us",
+                                                        "median_us", "max_us")]
+        for (name, g, tag), d in sorted(grid.items(), key=lambda kv: (str(kv[0][2]), kv[0][0])):
+            d = sorted(d)
+            star = "*" if args.headline_step and tag == "predict" + args.headline_step else " "
+            lines.append("%-34s %-16s %-26s %7d %9.2f %9.2f %9.2f %s" % (
+                name, str(g), str(tag), len(d), sum(d) / len(d), d[len(d) // 2], d[-1], star))
     text = "\n".join(lines) + "\n"
     with open(args.out, "w") as f:
         f.write(text)
@@ -147,6 +184,8 @@ def main(argv=None):
     a.add_argument("--workload", required=True)
     a.add_argument("--cmd", required=True)
     a.add_argument("--out", required=True)
+    a.add_argument("--headline-step", default=None,
+                   help="the headline workload's k_predict grid in workgroups, e.g. '(4, 64, 1)'")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
