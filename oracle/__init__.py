@@ -59,7 +59,7 @@ class OrcCfg(C.Structure):
     _fields_ = [("sinks", C.c_int32), ("window", C.c_int32), ("topk_abs", C.c_int32),
                 ("topk_ppm", C.c_int32), ("base_ppm", C.c_int32), ("force_budget", C.c_int32),
                 ("predictor", C.c_int32), ("rank", C.c_int32), ("eps", C.c_double),
-                ("delta", C.c_double), ("z32", C.c_double), ("seed", C.c_uint64)]
+                ("delta", C.c_double), ("z32", C.c_double), ("seed", C.c_uint64), ("guarantee", C.c_int32)]
 
 
 def _load():
@@ -75,7 +75,7 @@ def _load():
             P = C.c_void_p
             lib.orc_decode.restype = C.c_int
             lib.orc_decode.argtypes = [C.POINTER(OrcCfg)] + [C.c_int] * 7 + [P] * 4 + [C.c_int] + \
-                [P] * 3 + [C.c_int, C.c_int] + [P] * 5 + [C.c_int] + [P] * 3
+                [P] * 3 + [C.c_int, C.c_int] + [P] * 5 + [C.c_int] + [P] * 4
             lib.orc_dense.restype = C.c_int
             lib.orc_dense.argtypes = [C.c_int] * 6 + [P] * 6 + [C.c_int, C.c_int, P, P]
             lib.orc_pdot.restype = C.c_float
@@ -180,7 +180,8 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
     seq_lens [B] int32, proj [d,r] float32 (low-rank or signature predictor; or [Hkv,d,r],
     one basis per KV head) or None.
     cfg keys: sinks, window, topk_abs, topk_ppm, base_ppm, force_budget,
-    predictor (0 exact, 1 low-rank, 2 32-bit signatures with rank 32), rank, eps, delta, seed.
+    predictor (0 exact, 1 low-rank, 2 32-bit signatures with rank 32), rank, eps, delta, seed,
+    guarantee (0 the denominator, default; 1 the denominator and the numerator).
     groups: iterable of (b, g) to evaluate (default all).  Returns a dict of
     numpy arrays (rows of groups not evaluated are zero / -1).
     """
@@ -207,7 +208,7 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
                int(cfg.get("topk_ppm", 0)), int(cfg.get("base_ppm", 50000)),
                int(cfg.get("force_budget", -1)), int(cfg["predictor"]), int(cfg.get("rank", 0)),
                float(cfg["eps"]), float(cfg["delta"]), z_for_delta(float(cfg["delta"])),
-               int(cfg["seed"]) & 0xFFFFFFFFFFFFFFFF)
+               int(cfg["seed"]) & 0xFFFFFFFFFFFFFFFF, int(cfg.get("guarantee", 0)))
     out = np.zeros((B, Hq, d), dtype=np.float64)
     lse = np.zeros((B, Hq), dtype=np.float64)
     lse_dense = np.zeros((B, Hq), dtype=np.float64) if want_dense else None
@@ -216,6 +217,7 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
     counts = np.zeros((B, Hq, 6), dtype=np.int32)
     stats = np.zeros((B, Hq, 4), dtype=np.uint64)
     pred = np.full((B, Hq, max_seq_len), np.nan, dtype=np.float32) if want_pred else None
+    nstats = np.zeros((B, Hq, 2), dtype=np.float64)
     if groups is None:
         garr, ng = None, 0
     else:
@@ -225,12 +227,12 @@ def decode(*, q, k_cache, v_cache, block_table, seq_lens, cfg: dict, proj=None,
                             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(proj), proj_heads, _ptr(block_table),
                             _ptr(seq_lens), _ptr(garr), ng, int(nthreads), _ptr(out), _ptr(lse),
                             _ptr(lse_dense), _ptr(out_dense), _ptr(idx), max_seq_len,
-                            _ptr(counts), _ptr(stats), _ptr(pred))
+                            _ptr(counts), _ptr(stats), _ptr(pred), _ptr(nstats))
     if rc == 5:
         raise ValueError("oracle refused a non-finite input (q, the basis, or a cached K or V row)")
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
-    res = dict(out=out, lse=lse, counts=counts, stats=stats, z32=c.z32)
+    res = dict(out=out, lse=lse, counts=counts, stats=stats, z32=c.z32, num_stats=nstats)
     if want_idx:
         res["idx"] = idx
     if want_dense:

@@ -30,7 +30,10 @@
  *          pairwise tree over the block partials;
  *   pexp   Cody-Waite range reduction + degree-7 Taylor polynomial in fma;
  *   stats  exact unsigned integer sums of E_i = trunc(pexp(s_i - m) * 2^40);
- *   budget fp64 expression with a fixed parenthesisation, no contraction.
+ *   budget fp64 expression with a fixed parenthesisation, no contraction;
+ *   numerator statistics (the output-level mode) fp64 sums of E_i * V_ic in a
+ *          fixed order: ascending tokens within spans of ORC_SPAN tokens from
+ *          +0, then the span partials in ascending span order.
  * The attention output itself is computed in fp64 from the chosen index set.
  *
  * Build: gcc -O2 -std=gnu11 -ffp-contract=off -fopenmp -shared -fPIC.
@@ -57,7 +60,11 @@ typedef struct {
     double eps, delta;    /* accuracy target, failure probability          */
     double z32;           /* Phi^-1(1 - delta/2) rounded to fp32 (caller)  */
     uint64_t seed;        /* Philox key                                    */
+    int32_t guarantee;    /* 0 denominator; 1 denominator and numerator    */
 } orc_cfg;
+
+/* Tokens per span of the numerator sums' summation order (see decode_head). */
+#define ORC_SPAN 1024
 
 /* ------------------------------------------------------------------ */
 /* Small exact helpers                                                 */
@@ -261,6 +268,7 @@ typedef struct {
     int32_t* counts;
     uint64_t* stats;
     float* pred_scores; /* [B*Hq][max_seq_len] predictor scores, NaN outside the middle */
+    double* nstats;     /* [B*Hq][2] numerator statistics TR, NN (output-level mode) or NULL */
 } orc_ctx;
 
 /* Copy the L rows of (b, g) out of the paged cache as fp32. */
@@ -322,7 +330,9 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
     int32_t* counts = cx->counts ? cx->counts + bh * 6 : NULL;
     uint64_t* stats = cx->stats ? cx->stats + bh * 4 : NULL;
     int32_t* idx = cx->idx ? cx->idx + bh * cx->idx_cap : NULL;
+    double* nstats = cx->nstats ? cx->nstats + bh * 2 : NULL;
 
+    if (nstats) nstats[0] = nstats[1] = 0.0;
     if (idx)
         for (int t = 0; t < cx->idx_cap; ++t) idx[t] = -1;
     if (counts) memset(counts, 0, sizeof(int32_t) * 6);
@@ -438,9 +448,61 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
         S2 += (u128)e * e;
     }
 
+    /* Numerator statistics, output-level mode only.  SkyLight's post ("vAttention
+     * Computation") promises (eps, delta) on the intermediate quantities; the
+     * edgentiq post ("How vAttention Works") calls the denominator-only budget a
+     * relaxation.  Without it the numerator N = sum_i e^{s_i - m} V_i (a vector)
+     * is held to the same CLT bound: with y_i = E_i V_i per channel c,
+     *   TR = sum_c (n_b T2_c - T1_c^2)   (n_b (n_b - 1) times the summed
+     *                                     unbiased per-channel variances of y
+     *                                     over the base sample),
+     *   NN = sum_c (n_b NF_c + N_t T1_c)^2  (n_b^2 times the squared norm of
+     *                                        the estimated numerator),
+     * T1, T2 the sums of y and y^2 over the base sample, NF the sum of y over
+     * the fixed set.  Every sum is fp64 in one fixed order (ascending tokens
+     * within spans of ORC_SPAN, then the spans in order; channels ascending for
+     * TR and NN), so an independent implementation reproduces the bits. */
+    double TR = 0.0, NN = 0.0;
+    const int use_num = cfg->guarantee == 1 && nb > 0;
+    if (use_num) {
+        char* in_base = (char*)calloc((size_t)L, 1);
+        for (int t = 0; t < nb; ++t) in_base[rho[t].i] = 1;
+        double* tot = (double*)calloc((size_t)3 * d, sizeof(double)); /* T1, T2, NF */
+        double* part = (double*)malloc(sizeof(double) * 3 * d);
+        for (int s0 = 0; s0 < L; s0 += ORC_SPAN) {
+            for (int c = 0; c < 3 * d; ++c) part[c] = 0.0;
+            int s1 = s0 + ORC_SPAN < L ? s0 + ORC_SPAN : L;
+            for (int i = s0; i < s1; ++i) {
+                if (!in_fixed[i] && !in_base[i]) continue;
+                double e = (double)orc_fixed_weight(s_exact[i] - m);
+                for (int c = 0; c < d; ++c) {
+                    double y = e * (double)V[(int64_t)i * d + c];
+                    if (in_fixed[i]) {
+                        part[2 * d + c] = part[2 * d + c] + y;
+                    } else {
+                        part[c] = part[c] + y;
+                        part[d + c] = part[d + c] + y * y;
+                    }
+                }
+            }
+            for (int c = 0; c < 3 * d; ++c) tot[c] = tot[c] + part[c];
+        }
+        for (int c = 0; c < d; ++c) {
+            double m2 = (double)nb * tot[d + c] - tot[c] * tot[c];
+            if (m2 < 0.0) m2 = 0.0;
+            double yc = (double)nb * tot[2 * d + c] + (double)NT * tot[c];
+            TR = TR + m2;
+            NN = NN + yc * yc;
+        }
+        free(in_base); free(tot); free(part);
+        if (nstats) { nstats[0] = TR; nstats[1] = NN; }
+    }
+
     /* CLT budget on the denominator: n = (z * sigma * N_t / (eps * D))^2 with
      * sigma^2 the unbiased variance of the base sample and D the base-sample
-     * denominator estimate, rearranged over the exact integers. */
+     * denominator estimate, rearranged over the exact integers.  In the
+     * output-level mode the numerator's budget (the same expression with TR
+     * for M2 and NN for Y^2) is taken when larger (flag 8). */
     int n, flags = 0;
     if (cfg->force_budget >= 0) {
         n = cfg->force_budget < NT ? cfg->force_budget : NT;
@@ -459,6 +521,18 @@ static void decode_head(const orc_ctx* cx, int b, int h, int g, int L, const flo
         } else {
             n = (int)ceil(nreal);
             if (n < nb) { n = nb; flags |= 4; }
+        }
+        if (use_num) {
+            double numN = (z * z * (double)NT * (double)NT) * (TR * (double)nb);
+            double denN = ((double)(nb - 1) * (cfg->eps * cfg->eps)) * NN;
+            int nN;
+            if (denN == 0.0) {
+                nN = numN > 0.0 ? NT : 0; /* a zero numerator estimate: any spread is unbounded relative error */
+            } else {
+                double r = numN / denN;
+                nN = r >= (double)NT ? NT : (int)ceil(r);
+            }
+            if (nN > n) { n = nN; flags |= 8; }
         }
     }
     if (n == NT) flags |= 1;
@@ -543,12 +617,13 @@ int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks
                const float* proj, int proj_heads, const int32_t* block_table, const int32_t* seq_lens,
                const int32_t* groups, int n_groups, int nthreads, double* out, double* lse,
                double* lse_dense, double* out_dense, int32_t* idx, int idx_cap,
-               int32_t* counts, uint64_t* stats, float* pred_scores) {
+               int32_t* counts, uint64_t* stats, float* pred_scores, double* nstats) {
     if (!cfg || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse) return 1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d % 8 != 0 || d > 512) return 2;
     if (cfg->predictor == 1 && (!proj || cfg->rank % 8 != 0 || cfg->rank > d)) return 3;
     if (cfg->predictor == 2 && (!proj || cfg->rank != 32 || cfg->rank > d)) return 3;
     if (cfg->predictor < 0 || cfg->predictor > 2) return 3;
+    if (cfg->guarantee != 0 && cfg->guarantee != 1) return 3;
     if (proj_heads != 1 && proj_heads != Hkv) return 3;
     if (idx && idx_cap < max_seq_len) return 4;
     if (!all_finite(q, (int64_t)B * Hq * d)) return 5;
@@ -558,7 +633,7 @@ int orc_decode(const orc_cfg* cfg, int B, int Hq, int Hkv, int d, int max_blocks
     orc_init_constants();
     orc_ctx cx = {cfg, B, Hq, Hkv, d, max_blocks, kv_bf16, max_seq_len, q, k_cache, v_cache,
                   proj, proj_heads, block_table, seq_lens, out, lse, lse_dense, out_dense, idx, idx_cap,
-                  counts, stats, pred_scores};
+                  counts, stats, pred_scores, nstats};
     int total = groups ? n_groups : B * Hkv;
     if (nthreads < 1) nthreads = 1;
     int bad = 0;

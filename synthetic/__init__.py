@@ -118,7 +118,8 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
          topk_ppm=25000, base_ppm=50000, force_budget=-1, eps=0.05, delta=0.05, seed=0,
          data_seed=1000, shuffle=False, q_std=1.0, k_std=1.0, planted=8, plant_scale=4.0,
          outlier_channels=4, outlier_scale=8.0, lowrank_dim=24, lowrank_noise=0.1,
-         peaked_frac=0.5, hidden_logit=40.0, max_seq_len=None, proj_per_head=False) -> Workload:
+         peaked_frac=0.5, hidden_logit=40.0, max_seq_len=None, proj_per_head=False, v_mean=0.0,
+         guarantee=0) -> Workload:
     """Draw one workload.
 
     recipe:
@@ -131,6 +132,11 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
       lowrank   K = Z U^T + N(0, lowrank_noise^2), U a d x lowrank_dim orthonormal
                 basis per KV head, Z ~ N(0, I)
       mixed     per (b, KV head) a seeded coin: `planted` or `flat` (k_std=q_std=0.3)
+
+    v_mean: values V = v_mean * mu_g + N(0, I), with mu_g ~ N(0, I) drawn once
+    per KV head (a shared direction, as values of real heads have; 0 gives
+    zero-mean values whose attention output nearly cancels).
+    guarantee: 0 the denominator only, 1 the denominator and the numerator.
       hidden    as normal, plus keys the low-rank predictor cannot see: for every
                 query head h one key c * u / |u| with u = q_h - P P^T q_h (the
                 part of q_h outside the predictor's span), so its predicted score
@@ -164,8 +170,14 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
     U = None
     if recipe == "lowrank":
         U = torch.stack([orthonormal(d, lowrank_dim, gen) for _ in range(Hkv)])
+    # the value means come from a generator of their own, so every other
+    # tensor of the workload is the same for any v_mean
+    v_mu = (torch.randn(Hkv, 1, d, generator=torch.Generator().manual_seed(int(data_seed) + 7919)) * v_mean
+            if v_mean else None)
     for b, L in enumerate(seq_lens):
         v = torch.randn(Hkv, L, d, generator=gen)
+        if v_mu is not None:
+            v = v + v_mu
         if recipe in ("normal", "planted", "hidden"):
             k = torch.randn(Hkv, L, d, generator=gen) * k_std
         elif recipe == "flat":
@@ -237,7 +249,7 @@ def make(*, name="custom", B=1, Hq=4, Hkv=4, d=64, seq_lens=(1024,), kv_dtype="f
         proj = orthonormal(d, rank, gen) if predictor in (1, 2) else None
     cfg = dict(sinks=sinks, window=window, topk_abs=topk_abs, topk_ppm=topk_ppm,
                base_ppm=base_ppm, force_budget=force_budget, predictor=predictor,
-               rank=rank if predictor in (1, 2) else 0, eps=eps, delta=delta, seed=seed)
+               rank=rank if predictor in (1, 2) else 0, eps=eps, delta=delta, seed=seed, guarantee=guarantee)
     return Workload(name=name, q=q.contiguous(), k_cache=k_cache, v_cache=v_cache,
                     block_table=bt, seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                     proj=proj, cfg=cfg, max_seq_len=msl, meta=dict(kinds=kinds, recipe=recipe, plants=plants))
