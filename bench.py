@@ -49,12 +49,10 @@ def parse():
     ap.add_argument("--base-sweep", default="",
                     help="comma-separated workloads whose (eps, delta) rate, union density and step time "
                          "are also measured at base-sample rates of 5, 10 and 20%% of the tail")
-    ap.add_argument("--host-kv", action="store_true",
-                    help="also time the step with K/V in pinned host memory (adds a host_kv object)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the hash-predictor, output-level and host-resident K/V legs")
     ap.add_argument("--pca-basis", action="store_true",
                     help="also time and rate-check the workload with per-KV-head PCA predictor bases")
-    ap.add_argument("--hash", action="store_true",
-                    help="also time and rate-check the workload with the hash-signature predictor")
     return ap.parse_args()
 
 
@@ -200,6 +198,7 @@ def rate_run(dec, lse_dense, out_dense, eps, seeds, seed0):
     dev = dec.lse.device
     lse_all = torch.empty((seeds,) + w_shape, dtype=torch.float32, device=dev)
     oerr = torch.empty((seeds,) + w_shape, dtype=torch.float64, device=dev)
+    nerr = torch.empty((seeds,) + w_shape, dtype=torch.float64, device=dev)
     nsum = torch.zeros(w_shape, dtype=torch.float64, device=dev)
     usum = None
     dn = out_dense.norm(dim=-1)
@@ -209,6 +208,9 @@ def rate_run(dec, lse_dense, out_dense, eps, seeds, seed0):
         dec()
         lse_all[s].copy_(dec.lse)
         oerr[s] = (dec.out.double() - out_dense).norm(dim=-1) / dn
+        # numerator N_hat against N, both in units of the dense denominator
+        ratio = torch.exp(dec.lse.double() - lse_dense)
+        nerr[s] = (dec.out.double() * ratio[..., None] - out_dense).norm(dim=-1) / dn
         nsum += dec.counts[..., 3].double()
         if dec.group_counts is not None:
             g = dec.group_counts[..., 0].double()
@@ -219,11 +221,14 @@ def rate_run(dec, lse_dense, out_dense, eps, seeds, seed0):
     trials = int(rel.numel())
     lo, hi = clopper_pearson(viol, trials)
     e = oerr[:, live].flatten().cpu().numpy()
+    ne = nerr[:, live].flatten().cpu().numpy()
     res = {"eps": eps, "rate": round(viol / trials, 5), "violations": viol, "trials": trials, "seeds": seeds,
            "cp95": [round(lo, 5), round(hi, 5)],
            "mean_budget": round(float((nsum / seeds)[live].mean()), 1),
            "output_error": {"rate_above_eps": round(float((e > eps).mean()), 5),
-                            "median": round(float(np.median(e)), 5), "p99": round(float(np.quantile(e, 0.99)), 5)}}
+                            "median": round(float(np.median(e)), 5), "p99": round(float(np.quantile(e, 0.99)), 5)},
+           "numerator_error": {"rate_above_eps": round(float((ne > eps).mean()), 5),
+                               "median": round(float(np.median(ne)), 5)}}
     return res, (None if usum is None else usum / seeds)
 
 
@@ -434,12 +439,19 @@ def main():
         k_new = k0[pages, :, slots].contiguous()
         v_new = v0[pages, :, slots].contiguous()
         n_app = 200
-        vsa.append_kv(k_new, v_new, pos, bt, k0, v0, k_lowrank=kt0, proj=proj)
+        vsa.append_kv(k_new, v_new, pos, bt, k0, v0, k_lowrank=kt0, proj=proj)  # checks the arguments once
         torch.cuda.synchronize()
+        lib = vsa.load()
+        cargs = (C.c_void_p(k_new.data_ptr()), C.c_void_p(v_new.data_ptr()), C.c_void_p(pos.data_ptr()),
+                 C.c_void_p(bt.data_ptr()), w.B, bt.shape[1], C.c_void_p(k0.data_ptr()), C.c_void_p(v0.data_ptr()),
+                 C.c_void_p(kt0.data_ptr()), C.c_void_p(proj.data_ptr()), vsa.BF16 if esize == 2 else vsa.F32,
+                 k0.shape[0], w.Hkv, d, r, 1 if proj.dim() == 2 else w.Hkv,
+                 C.c_void_p(torch.cuda.current_stream().cuda_stream))
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
         for _ in range(n_app):
-            vsa.append_kv(k_new, v_new, pos, bt, k0, v0, k_lowrank=kt0, proj=proj)
+            if lib.vattn_append_kv(*cargs) != 0:
+                raise RuntimeError("vattn_append_kv failed")
         a1.record()
         torch.cuda.synchronize()
         app_us = a0.elapsed_time(a1) / n_app * 1e3
@@ -474,24 +486,29 @@ def main():
         log("key gram %.1f us (%.0f GB/s)" % (g_us, g_bytes / g_us / 1e3))
         del gram, gws
 
-    if args.host_kv and not args.profile:
+    if not args.no_legs and not args.profile and args.workload == "llama8b_32k":
         # ---- host-resident K/V: the caches in pinned, device-mapped host memory,
         # read by the kernels over the host link (the low-rank keys and the
         # workspace stay in HBM).  Compared with moving the whole K/V over the
-        # same link, measured as a plain host-to-device copy.
-        kh = w.k_cache.pin_memory()
-        vh = w.v_cache.pin_memory()
+        # same link, measured as a plain host-to-device copy.  The first two
+        # sequences of the workload (a launch of its own, so a kernel trace
+        # tells these steps from the headline's).
+        hw = synthetic.WORKLOADS[args.workload](B=2)
+        hD = Device(hw, dev, 1)
+        kh = hw.k_cache.pin_memory()
+        vh = hw.v_cache.pin_memory()
         rt = C.CDLL("libamdhip64.so.7")
         rt.hipHostGetDevicePointer.argtypes = [C.POINTER(C.c_void_p), C.c_void_p, C.c_uint]
         for t_ in (kh, vh):  # the kernels read the host addresses: the device must map them alike
             a_ = C.c_void_p()
             if rt.hipHostGetDevicePointer(C.byref(a_), C.c_void_p(t_.data_ptr()), 0) != 0 or a_.value != t_.data_ptr():
                 raise RuntimeError("pinned host memory is not mapped at the same device address")
-        hdec = vsa.Decoder(q, kh, vh, bt, sl, vsa.Config.from_dict(w.cfg), max_seq_len=w.max_seq_len,
-                           k_lowrank=kt0, proj=proj, workspace=ws)
+        hdec = vsa.Decoder(hD.q, kh, vh, hD.bt, hD.sl, vsa.Config.from_dict(hw.cfg), max_seq_len=hw.max_seq_len,
+                           k_lowrank=hD.inst[0][2], proj=hD.proj, workspace=ws, want_group_counts=True)
         hdec.set_seed(7)
         hdec()
         torch.cuda.synchronize()
+        hU = hdec.group_counts[..., 0].double().cpu().numpy()
         n_h = 5
         h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         h0.record()
@@ -501,9 +518,9 @@ def main():
         h1.record()
         torch.cuda.synchronize()
         host_ms = h0.elapsed_time(h1) / n_h
-        kv_bytes = 2 * w.k_cache.numel() * esize
+        kv_bytes = 2 * hw.k_cache.numel() * esize
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dst = torch.empty_like(v0)
+        dst = torch.empty_like(hD.inst[0][1])
         dst.copy_(vh, non_blocking=True)
         torch.cuda.synchronize()
         c0.record()
@@ -513,22 +530,25 @@ def main():
         torch.cuda.synchronize()
         link_gbs = 3 * vh.numel() * esize / (c0.elapsed_time(c1) * 1e-3) / 1e9
         dense_ms = kv_bytes / (link_gbs * 1e9) * 1e3
-        union_bytes = float((U * 2 * row).sum())
+        union_bytes = float((hU * 2 * row).sum())
         result["host_kv"] = {
-            "ms_per_step": round(host_ms, 3), "value": round(heads_tokens / (host_ms * 1e-3), 1),
+            "batch": hw.B, "ms_per_step": round(host_ms, 3),
+            "value": round(hw.heads_tokens() / (host_ms * 1e-3), 1),
             "unit": "heads·tokens/s", "link_copy_GBps": round(link_gbs, 1),
             "kv_bytes_over_link": round(union_bytes), "dense_kv_bytes": kv_bytes,
             "dense_kv_transfer_ms": round(dense_ms, 3), "speedup_vs_dense_transfer": round(dense_ms / host_ms, 2),
-            "note": "K/V in pinned host memory read in place by the kernels; low-rank keys in HBM"}
-        log("host-resident KV: %.3f ms/step, link %.1f GB/s, dense K/V transfer %.3f ms"
-            % (host_ms, link_gbs, dense_ms))
-        del hdec, kh, vh, dst
+            "note": "the first %d sequences of the workload with K/V in pinned host memory read in place by the "
+                    "kernels (low-rank keys in HBM), against moving the whole K/V over the same link" % hw.B}
+        log("host-resident KV (B=%d): %.3f ms/step, link %.1f GB/s, dense K/V transfer %.3f ms"
+            % (hw.B, host_ms, link_gbs, dense_ms))
+        del hdec, kh, vh, dst, hD
 
     if not args.profile:
         # ---- (eps, delta): denominator relative error against dense fp64 attention
         lse_dense, out_dense = dense_reference(D)
         er, _ = rate_run(decs[0], lse_dense, out_dense, w.cfg["eps"], args.rate_seeds, 1_000_000)
         result["eps_violation"] = {k_: er[k_] for k_ in ("rate", "violations", "trials", "seeds", "cp95")}
+        result["eps_violation"]["mean_budget"] = er["mean_budget"]
         result["eps_violation"].update({"delta": w.cfg["delta"], "reference": "dense attention in fp64"})
         result["output_error"] = dict(er["output_error"], note="the budget bounds the denominator only; "
                                       "this is the measured relative L2 error of the outputs against dense fp64")
@@ -582,7 +602,7 @@ def main():
         # ---- the same workload with the hash-signature predictor (32 sign
         # bits per key under the workload's random directions, 4 bytes per
         # token instead of a rank-r row).  Context only.
-        if args.hash and proj is not None and r == 32:
+        if not args.no_legs and proj is not None and r == 32:
             hcfg = vsa.Config.from_dict(dict(w.cfg, predictor=vsa.PRED_HASH, rank=32))
             hdecs = [vsa.Decoder(q, k, v, bt, sl, hcfg, max_seq_len=w.max_seq_len, proj=proj,
                                  k_sig=vsa.sign_keys(k, proj), want_group_counts=True, workspace=ws)
@@ -612,6 +632,44 @@ def main():
                         "(vattn_sign_keys) scored by shared bits"}
             log("hash predictor: %.4f ms/step, eps violations %d / %d" % (hash_ms, hr["violations"], hr["trials"]))
             del hdecs
+
+    if not args.profile and not args.no_legs and args.workload == "llama8b_32k":
+        # ---- the output-level guarantee (numerator and denominator) against the
+        # denominator-only budget: union density, budget, step time, the
+        # denominator and numerator (eps, delta) rates and the output error.  On
+        # the tiny workload as stated (zero-mean values) and with values of a
+        # shared direction, and on the 32K workload with such values.
+        legs = [("tiny_1k", lambda: synthetic.tiny(), 1000),
+                ("tiny_1k_value_mean_3", lambda: synthetic.tiny(v_mean=3.0), 1000),
+                ("llama8b_32k_value_mean_3", lambda: synthetic.WORKLOADS[args.workload](v_mean=3.0),
+                 max(100, args.rate_seeds // 5))]
+        og = {}
+        for name, mk, seeds in legs:
+            ow = mk()
+            oD = Device(ow, dev, 1)
+            lse_o, out_o = dense_reference(oD)
+            Lo = ow.seq_lens.numpy().astype(np.float64)[:, None]
+            og[name] = {"seeds": seeds}
+            for gname, gval in (("denominator", 0), ("output", 1)):
+                od = oD.decoders(dict(ow.cfg, guarantee=gval), group_counts=True)[0]
+                oms, _, _ = time_steps([od], 20, 3, 70_000)
+                res_o, Uo = rate_run(od, lse_o, out_o, ow.cfg["eps"], seeds, 3_000_000)
+                og[name][gname] = {
+                    "ms_per_step": round(oms, 5), "union_density": round(float((Uo.cpu().numpy() / Lo).mean()), 4),
+                    "mean_budget": res_o["mean_budget"],
+                    "denominator_violation": {"rate": res_o["rate"], "cp95": res_o["cp95"]},
+                    "numerator_error": res_o["numerator_error"], "output_error": res_o["output_error"]}
+                log("%s %s: %.4f ms/step, density %.3f, denominator viol %.4f, numerator above eps %.4f, "
+                    "output above eps %.4f" % (name, gname, oms, og[name][gname]["union_density"], res_o["rate"],
+                                               res_o["numerator_error"]["rate_above_eps"],
+                                               res_o["output_error"]["rate_above_eps"]))
+                del od
+            og[name]["eps"] = ow.cfg["eps"]
+            del oD
+        og["note"] = ("guarantee=1 holds the numerator sum_i w_i e^{s_i} V_i to the same CLT bound as the "
+                      "denominator and takes the larger budget; numerator_error is |N_hat - N| / |N|")
+        result["output_guarantee"] = og
+        torch.cuda.empty_cache()
 
     if not args.profile and not args.no_cpu_baseline:
         import oracle

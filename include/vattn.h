@@ -71,6 +71,13 @@ typedef enum {
 
 typedef enum { VATTN_F32 = 0, VATTN_BF16 = 1 } vattn_dtype;
 
+/* What the sample size guarantees (vattn_cfg.guarantee). */
+typedef enum {
+    VATTN_GUARANTEE_DENOMINATOR = 0, /* the softmax denominator (the pages' relaxation)     */
+    VATTN_GUARANTEE_OUTPUT = 1       /* the denominator and the numerator sum w e^s V: the   */
+                                     /* budget is the larger of the two CLT budgets         */
+} vattn_guarantee;
+
 typedef enum {
     VATTN_PRED_EXACT = 0,   /* top-k on exact scores q_s . K_i (reads K)          */
     VATTN_PRED_LOWRANK = 1, /* top-k on (q_s P) . Kt_i with Kt = bf16(K P) (reads Kt) */
@@ -93,6 +100,21 @@ typedef struct {
     double eps;           /* > 0: relative accuracy target of the denominator         */
     double delta;         /* in (0, 1): failure probability                           */
     uint64_t seed;        /* Philox4x32-10 key; callers vary it per step and layer     */
+    int32_t guarantee;    /* vattn_guarantee.  VATTN_GUARANTEE_OUTPUT (SkyLight post   */
+                          /* "vAttention Computation": (eps, delta) on the intermediate */
+                          /* quantities; edgentiq post, "How vAttention Works": the     */
+                          /* denominator-only budget is a relaxation) also holds the    */
+                          /* numerator N = sum_i e^{s_i - m} V_i to the CLT bound in L2: */
+                          /* n_N = z^2 N_t^2 TR n_b / ((n_b - 1) eps^2 NN) with          */
+                          /* TR = sum_c max(n_b T2_c - T1_c^2, 0) and                    */
+                          /* NN = sum_c (n_b NF_c + N_t T1_c)^2, where over the base     */
+                          /* sample T1_c = sum E_i V_ic, T2_c = sum (E_i V_ic)^2, over   */
+                          /* the fixed set NF_c = sum E_i V_ic, E_i the fixed-point      */
+                          /* weights of the statistics; every sum in fp64, ascending     */
+                          /* tokens within 1024-token spans from +0, the spans in order, */
+                          /* channels ascending.  n = max(n_D, n_N) clamped as n_D.      */
+                          /* Reads the V rows of the fixed sets and base samples once    */
+                          /* more (two more kernels)                                     */
 } vattn_cfg;
 
 /* Inputs.  All pointers are device pointers except where noted.  k_cache and
@@ -135,7 +157,8 @@ typedef struct {
     int32_t idx_cap;  /* >= max_seq_len when idx != NULL                               */
     int32_t* counts;  /* [B, Hq, 6]: n_fixed, N_t, n_b, n, |I|, flags                  */
                       /*   flags bit0: n == N_t (exact), bit1: forced budget,          */
-                      /*   bit2: CLT budget below n_b raised to n_b                    */
+                      /*   bit2: CLT budget below n_b raised to n_b, bit3: the         */
+                      /*   numerator's budget exceeded the denominator's (output mode) */
     uint64_t* stats;  /* [B, Hq, 4]: SF, S1, S2 high word, S2 low word: exact sums     */
                       /*   of E_i = trunc(exp(s_i - m) 2^40) over I_f (SF) and over    */
                       /*   the base sample (S1, and S2 of E_i^2 as 128 bits)           */
@@ -144,6 +167,8 @@ typedef struct {
                       /*   score pass read (union of fixed sets and base samples);      */
                       /*   for byte accounting                                          */
     double z_used;    /* host, written by vattn_decode: fp32-rounded z                  */
+    double* num_stats; /* [B, Hq, 2] optional: TR, NN of the output-level mode (0 when   */
+                      /*   the head has no base sample); ignored in the denominator mode */
 } vattn_outputs;
 
 /* Bytes of device workspace vattn_decode needs for these shapes and cfg

@@ -67,4 +67,6 @@ class GpuCase:
         if self.dec.idx is not None:
             r["idx"] = self.dec.idx.cpu().numpy()
         r["gcounts"] = self.dec.group_counts.cpu().numpy()
+        if self.dec.num_stats is not None:
+            r["num_stats"] = self.dec.num_stats.cpu().numpy()
         return r

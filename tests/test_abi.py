@@ -318,3 +318,13 @@ def test_binding_rejects_bad_maintenance_tensors():
         vsa.sign_keys(t["k_cache"], t["proj"], k_sig=torch.zeros(20, 2, 16, dtype=torch.int16))
     with pytest.raises(ValueError, match="seq_lens must be int32"):
         vsa.key_gram(t["k_cache"], t["block_table"], t["seq_lens"].long(), 160)
+
+
+def test_guarantee_field(lib):
+    inp = _inputs()
+    for bad in (-1, 2):
+        assert lib.vattn_workspace_size(C.byref(inp), C.byref(_cfg(guarantee=bad))) == 0
+        assert _decode(lib, inp, _cfg(guarantee=bad)) == 4  # VATTN_E_CFG
+    den = lib.vattn_workspace_size(C.byref(inp), C.byref(_cfg(guarantee=0)))
+    out = lib.vattn_workspace_size(C.byref(inp), C.byref(_cfg(guarantee=1)))
+    assert out > den > 0  # the output-level mode's V-row lists and numerator partials

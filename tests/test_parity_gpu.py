@@ -37,6 +37,9 @@ def compare(w, g, o, groups=None, tag=""):
             assert np.array_equal(g["counts"][b, h], o["counts"][b, h]), \
                 (ctx, g["counts"][b, h], o["counts"][b, h])
             assert np.array_equal(g["stats"][b, h], o["stats"][b, h]), (ctx, g["stats"][b, h], o["stats"][b, h])
+            if "num_stats" in g:  # output-level mode: fp64 sums in one order on both sides
+                assert np.array_equal(g["num_stats"][b, h], o["num_stats"][b, h]), \
+                    (ctx, g["num_stats"][b, h], o["num_stats"][b, h])
             if "idx" in g and "idx" in o:
                 assert np.array_equal(g["idx"][b, h], o["idx"][b, h]), ctx
             L = int(w.seq_lens[b])
@@ -418,6 +421,64 @@ def test_concurrent_streams(pair):
 
 
 # ---------------------------------------------------------------------------
+# Output-level mode (guarantee = 1): the numerator statistics TR and NN
+# bit-identical to the oracle's (fp64 sums in one order), budgets and index
+# sets bit-exact, out/lse within tolerance.  Values with a shared direction
+# (v_mean) so the budgets stay below the tail.
+# ---------------------------------------------------------------------------
+OUTPUT_CASES = {
+    "out_tiny": lambda: synthetic.tiny(guarantee=1, v_mean=3.0),
+    "out_gqa4_bf16_ragged": lambda: synthetic.make(
+        name="out_gqa4_bf16_ragged", B=3, Hq=16, Hkv=4, d=128, seq_lens=(5000, 2500, 777), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=32, sinks=32, window=64, topk_ppm=25000, shuffle=True, data_seed=11,
+        guarantee=1, v_mean=2.0),
+    "out_g8_lowrank": lambda: synthetic.make(
+        name="out_g8_lowrank", B=2, Hq=16, Hkv=2, d=128, seq_lens=(9000, 4100), kv_dtype="bf16", recipe="lowrank",
+        predictor=1, rank=32, sinks=128, window=128, topk_ppm=25000, eps=0.05, data_seed=12, guarantee=1,
+        v_mean=3.0),
+    "out_d64_f32_g2": lambda: synthetic.make(
+        name="out_d64_f32_g2", B=2, Hq=4, Hkv=2, d=64, seq_lens=(3000, 1500), kv_dtype="f32", recipe="planted",
+        predictor=1, rank=16, sinks=8, window=16, topk_ppm=20000, data_seed=13, guarantee=1, v_mean=3.0),
+    "out_hash_g4": lambda: synthetic.make(
+        name="out_hash_g4", B=2, Hq=8, Hkv=2, d=128, seq_lens=(4000, 2222), kv_dtype="bf16", recipe="outlier",
+        predictor=2, rank=32, sinks=32, window=32, topk_ppm=25000, data_seed=40, guarantee=1, v_mean=2.0),
+    "out_premerge": lambda: synthetic.make(
+        name="out_premerge", B=1, Hq=4, Hkv=1, d=128, seq_lens=(40000,), kv_dtype="bf16", recipe="outlier",
+        predictor=1, rank=32, sinks=64, window=64, topk_ppm=25000, data_seed=19, guarantee=1, v_mean=3.0),
+    "out_zero_mean_dense": lambda: synthetic.make(
+        name="out_zero_mean", B=2, Hq=8, Hkv=2, d=128, seq_lens=(3000, 1234), kv_dtype="bf16", recipe="outlier",
+        predictor=1, rank=32, sinks=16, window=16, data_seed=24, guarantee=1),
+    "out_forced_small": lambda: synthetic.make(
+        name="out_forced_small", B=1, Hq=4, Hkv=1, d=64, seq_lens=(1500,), kv_dtype="f32", predictor=0,
+        sinks=4, window=4, topk_abs=16, force_budget=7, guarantee=1, v_mean=2.0),
+    "out_short_seqs": lambda: synthetic.make(
+        name="out_short", B=4, Hq=2, Hkv=1, d=64, seq_lens=(0, 1, 20, 50), kv_dtype="f32", predictor=0, sinks=2,
+        window=2, topk_abs=4, guarantee=1, v_mean=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(OUTPUT_CASES))
+def test_parity_output_mode(name):
+    run_both(OUTPUT_CASES[name](), seeds=(0, 1, 977), tag=name)
+
+
+def test_parity_output_mode_tiny_200_seeds():
+    w = synthetic.tiny(guarantee=1, v_mean=3.0)
+    GpuCase, log = _gpu()
+    log("[parity] tiny output mode x 200 seeds")
+    case = GpuCase(w)
+    arrays = w.oracle_arrays()
+    flagged = 0
+    for s in range(200):
+        cfg = dict(w.cfg, seed=s)
+        g = case.run(s)
+        o = oracle.decode(**arrays, cfg=cfg)
+        compare(w, g, o, tag="tiny output seed=%d" % s)
+        flagged += int(np.sum(o["counts"][..., 5] & 8 > 0))
+    assert flagged > 0  # the numerator's budget decided some heads
+
+
+# ---------------------------------------------------------------------------
 # Full-size workloads in the benchmark's launch configuration, sampled groups.
 # ---------------------------------------------------------------------------
 FULL = {
@@ -425,6 +486,8 @@ FULL = {
     "flat_128k": (lambda: synthetic.flat_128k(), [(0, 0), (0, 6)]),
     "ragged_b64": (lambda: synthetic.ragged_b64(), [(0, 1), (17, 4), (40, 0), (63, 7)]),
     "wide_gqa_64k": (lambda: synthetic.wide_gqa_64k(), [(1, 2), (3, 7)]),
+    "llama8b_32k_output_mode": (lambda: synthetic.llama8b_32k(name="llama8b_32k_output", guarantee=1, v_mean=3.0),
+                                [(0, 0), (6, 5)]),
     "llama8b_32k_hash": (lambda: synthetic.llama8b_32k(name="llama8b_32k_hash", predictor=2),
                          [(0, 0), (5, 3)]),
     # the longest sequence the library takes (2^20 tokens): 256 predictor

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libvattn.so")
 PAGE = 16
 F32, BF16 = 0, 1
 PRED_EXACT, PRED_LOWRANK, PRED_HASH = 0, 1, 2
+GUARANTEE_DENOMINATOR, GUARANTEE_OUTPUT = 0, 1
 
 STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYPE",
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
@@ -44,7 +45,7 @@ class vattn_cfg(C.Structure):
     _fields_ = [("sinks", C.c_int32), ("window", C.c_int32), ("topk_abs", C.c_int32),
                 ("topk_ppm", C.c_int32), ("base_ppm", C.c_int32), ("force_budget", C.c_int32),
                 ("predictor", C.c_int32), ("rank", C.c_int32), ("eps", C.c_double),
-                ("delta", C.c_double), ("seed", C.c_uint64)]
+                ("delta", C.c_double), ("seed", C.c_uint64), ("guarantee", C.c_int32)]
 
 
 class vattn_inputs(C.Structure):
@@ -59,7 +60,7 @@ class vattn_inputs(C.Structure):
 class vattn_outputs(C.Structure):
     _fields_ = [("out", C.c_void_p), ("lse", C.c_void_p), ("idx", C.c_void_p),
                 ("idx_cap", C.c_int32), ("counts", C.c_void_p), ("stats", C.c_void_p),
-                ("group_counts", C.c_void_p), ("z_used", C.c_double)]
+                ("group_counts", C.c_void_p), ("z_used", C.c_double), ("num_stats", C.c_void_p)]
 
 
 _lib = None
@@ -132,6 +133,7 @@ class Config:
     eps: float = 0.05
     delta: float = 0.05
     seed: int = 0
+    guarantee: int = GUARANTEE_DENOMINATOR
 
     @classmethod
     def from_dict(cls, d):
@@ -140,7 +142,7 @@ class Config:
     def to_c(self):
         return vattn_cfg(self.sinks, self.window, self.topk_abs, self.topk_ppm, self.base_ppm,
                          self.force_budget, self.predictor, self.rank, float(self.eps),
-                         float(self.delta), int(self.seed) & 0xFFFFFFFFFFFFFFFF)
+                         float(self.delta), int(self.seed) & 0xFFFFFFFFFFFFFFFF, int(self.guarantee))
 
 
 def _ptr(t):
@@ -297,6 +299,8 @@ class Decoder:
         self.stats = torch.empty(B, Hq, 4, dtype=torch.int64, device=dev) if want_stats else None
         self.group_counts = (torch.empty(B, k_cache.shape[1], 2, dtype=torch.int32, device=dev)
                              if want_group_counts else None)
+        self.num_stats = (torch.zeros(B, Hq, 2, dtype=torch.float64, device=dev)
+                          if cfg.guarantee == GUARANTEE_OUTPUT else None)
         self.ws_bytes = workspace_size(self.inputs, cfg)
         if self.ws_bytes == 0:
             raise VattnError(4, "vattn_workspace_size (invalid shapes or cfg)")
@@ -318,7 +322,7 @@ class Decoder:
                                      None if self.counts is None else self.counts.data_ptr(),
                                      None if self.stats is None else self.stats.data_ptr(),
                                      None if self.group_counts is None else self.group_counts.data_ptr(),
-                                     0.0)
+                                     0.0, None if self.num_stats is None else self.num_stats.data_ptr())
         self._ccfg = cfg.to_c()
 
     def set_seed(self, seed: int):

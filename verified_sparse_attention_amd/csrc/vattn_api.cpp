@@ -47,7 +47,7 @@ int pred_row(const vattn_inputs* in, const vattn_cfg* cfg) {
 }
 
 struct Shape {
-    int G, cp, ncp, kcap, cg, ncg, words, nparts, kcap2;
+    int G, cp, ncp, kcap, cg, ncg, words, nparts, kcap2, guarantee;
 };
 
 vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
@@ -77,8 +77,10 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
     }
     if (!(cfg->eps > 0.0) || !std::isfinite(cfg->eps)) return VATTN_E_CFG;
     if (!(cfg->delta > 0.0 && cfg->delta < 1.0)) return VATTN_E_CFG;
+    if (cfg->guarantee != VATTN_GUARANTEE_DENOMINATOR && cfg->guarantee != VATTN_GUARANTEE_OUTPUT) return VATTN_E_CFG;
     if (sh) {
         sh->G = G;
+        sh->guarantee = cfg->guarantee;
         // Predictor chunk: the keys of G heads stay in LDS (at most kPredKeys
         // and within the workgroup LDS limit).  Below that bound, aim for one
         // chunk per compute unit over the whole batch, but keep chunks of at
@@ -119,7 +121,8 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2, total;
+    size_t cand, bits, hs, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2,
+        brow, npart, total;
 };
 
 Layout layout(const vattn_inputs* in, const Shape& s) {
@@ -163,6 +166,11 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHq * s.nparts * sizeof(int32_t));
     L.hist2 = off;
     off += align_up(BHkv * s.nparts * vattn::kSampBins * sizeof(uint32_t));
+    const bool num = s.guarantee == VATTN_GUARANTEE_OUTPUT;  // the output-level mode's arrays
+    L.brow = off;
+    off += num ? align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t)) : 0;
+    L.npart = off;
+    off += num ? align_up(BHq * s.ncg * 3 * static_cast<size_t>(in->d) * sizeof(double)) : 0;
     L.total = off;
     return L;
 }
@@ -261,6 +269,9 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.crange2 = reinterpret_cast<uint32_t*>(ws + L.crange2);
     p.pcount = reinterpret_cast<int32_t*>(ws + L.pcount);
     p.hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
+    p.guarantee = cfg->guarantee;
+    p.brow = s.guarantee == VATTN_GUARANTEE_OUTPUT ? reinterpret_cast<uint32_t*>(ws + L.brow) : nullptr;
+    p.npart = s.guarantee == VATTN_GUARANTEE_OUTPUT ? reinterpret_cast<double*>(ws + L.npart) : nullptr;
     p.out = out->out;
     p.lse = out->lse;
     p.idx = out->idx;
@@ -268,6 +279,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.counts = out->counts;
     p.stats = out->stats;
     p.gcounts = out->group_counts;
+    p.nstats = s.guarantee == VATTN_GUARANTEE_OUTPUT ? out->num_stats : nullptr;
     out->z_used = p.z32;
     const int rc = vattn::launch_decode(p, hip_stream, events);
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;

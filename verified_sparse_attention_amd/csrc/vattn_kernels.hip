@@ -16,6 +16,9 @@
 //   budget   (b*Hq)          exact fixed-point denominator statistics of the
 //                            head's fixed set and base sample, CLT budget,
 //                            final-sample threshold, the group's dispatch weight
+//                            (output-level mode: statistics, then numstat
+//                            (b*Hkv, chunk) numerator partials, then
+//                            budget_num (b*Hq) the larger budget and threshold)
 //   gather   (chunk, b*Hkv)  over the union of the group's index sets, groups
 //                            densest first: K row (unless its score is cached)
 //                            and V row per token, weighted softmax partials
@@ -822,12 +825,15 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     uint32_t cnt;
     uint32_t pos = block_excl_scan(mine, wsum, cnt);
     uint32_t* lmeta = P.bmeta + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
+    uint32_t* lrow = P.brow ? P.brow + (static_cast<size_t>(bg) * P.ncg + c) * P.cg : nullptr;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (m4[e]) {
+            const uint32_t rw = row0 + ((4 * qd + e) & (kPage - 1));
             tmeta[pos] = m4[e];
-            trow[pos] = row0 + ((4 * qd + e) & (kPage - 1));
+            trow[pos] = rw;
             lmeta[pos] = m4[e];
+            if (lrow) lrow[pos] = rw;  // the V row, for the output-level statistics
             ++pos;
         }
     if (tid == 0) {
@@ -916,7 +922,40 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 // ===========================================================================
 constexpr int kStatsBatch = 4;  // entries of each of a wave's two chunks requested per lane at once
 
-template <int kThreads>  // per block
+// The final sample's threshold in the sample order (rank > 0: a new one; else
+// the whole tail, or the base sample's when n == n_b).  S.hist holds the
+// head's tail histogram.  All threads call.
+__device__ __forceinline__ void final_sample_threshold(const Plan& P, HeadSamp& SS, SelShared<1>& FS, HeadState* hsp,
+                                                       int bh, int bg, const Regions& R, uint32_t rank) {
+    const uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
+    const BinLists BL{P.soff + static_cast<size_t>(bg) * P.ncp * (kSampBins + 1),
+                      P.slist + static_cast<size_t>(bg) * P.ncp * P.cp, P.ncp, P.cp, R.lo, R.hi};
+    head_sample_threshold(SS, FS, BL, group_words(P, bg), rank, [&](int i) __attribute__((always_inline)) {
+        return bit_of(bits, i);
+    });
+    if (threadIdx.x == 0) {
+        const int n = hsp->n;
+        uint64_t thr = 0;  // n == N_t: the whole tail (n == 0: unused)
+        if (rank > 0) thr = SS.thr;
+        else if (n > 0 && n == R.nb) thr = hsp->thr_b;
+        hsp->thr_n = thr;
+    }
+}
+
+// The head's final budget is set (hsp->n): the sample weight, the group's
+// gather dispatch weight (expected member density; non-negative fp32 values
+// order as their bit patterns) and the rank of a new threshold, 0 unless the
+// sample is neither empty, the whole tail nor the base sample.  Thread 0.
+__device__ __forceinline__ int settle_budget(const Plan& P, HeadState* hsp, int bg, const Regions& R, int L) {
+    const int n = hsp->n, NT = R.NT, nb = R.nb;
+    atomicMax(&P.gw[bg], __float_as_uint(static_cast<float>(R.sp + R.wp + R.k + n) / static_cast<float>(L)));
+    hsp->wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
+    return (n > 0 && n < NT && n != nb) ? n : 0;
+}
+
+// DEFER (output-level mode): statistics, m and the denominator's budget only;
+// k_numstat and k_budget_num finish the budget and the threshold.
+template <int kThreads, bool DEFER>  // per block
 __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
     constexpr int NW = kThreads / 64;
     static_assert(NW >= 2, "one wave for m, one for the chunk offsets");
@@ -940,7 +979,8 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         return;
     }
     const int nc = (L + P.cg - 1) / P.cg;
-    for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
+    if constexpr (!DEFER)
+        for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
     if (wave == 0) {  // m: max pinned score over I_f and the base sample
         float m = -__builtin_inff();
         for (int c = lane; c < nc; c += 64) m = fmaxf(m, P.cmax[static_cast<size_t>(bh) * P.ncg + c]);
@@ -1068,30 +1108,166 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         }
         if (n == NT) flags |= 1;
         hsp->n = n;
-        // the group's gather dispatch weight: expected member density (non-negative
-        // fp32 values order as their bit patterns)
-        atomicMax(&P.gw[bg], __float_as_uint(static_cast<float>(R.sp + R.wp + R.k + n) / static_cast<float>(L)));
         hsp->flags = flags;
         hsp->m = m;
-        hsp->wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
-        // a new threshold unless the sample is empty, the whole tail or the base sample
-        s_nsel = (n > 0 && n < NT && n != nb) ? n : 0;
+        if constexpr (!DEFER) s_nsel = settle_budget(P, hsp, bg, R, L);
+    }
+    if constexpr (DEFER) return;
+    __syncthreads();
+    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel));
+}
+
+// ===========================================================================
+// Output-level mode.  SkyLight's post ("vAttention Computation") promises
+// (eps, delta) on the intermediate quantities and the edgentiq post ("How
+// vAttention Works") calls the denominator-only budget a relaxation; without
+// it the numerator N = sum_i e^{s_i - m} V_i is held to the same CLT bound.
+// With y_i = E_i V_i per channel (E_i the exact fixed-point weights of the
+// statistics), over each head's base sample T1 = sum y, T2 = sum y^2 and over
+// its fixed set NF = sum y, all fp64 in one order: ascending tokens within each
+// gather chunk from +0 (k_numstat, per chunk), then the chunk partials in
+// ascending chunk order (k_budget_num).  Then
+//   TR = sum_c max(n_b T2_c - T1_c^2, 0),  NN = sum_c (n_b NF_c + N_t T1_c)^2
+// (channels ascending) and the numerator's budget is the denominator's
+// expression with TR for M2 and NN for Y^2; the larger budget is taken.
+// ===========================================================================
+constexpr int kNumTile = 64;  // base-list members whose V rows are staged at once
+
+template <int D, typename KVT, int G>
+__global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
+    __shared__ float vs[kNumTile][D];       // the tile's V rows
+    __shared__ double es[kNumTile][G];      // E_i of each member for each head (0: not a member)
+    __shared__ uint32_t fx[kNumTile];       // fixed mask of each member
+    __shared__ float hm[G];
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int g = blockIdx.x, c = blockIdx.y, b = blockIdx.z, bg = b * P.Hkv + g;
+    const int L = P.seq_lens[b];
+    if (c * P.cg >= L) return;  // block-uniform; no partial for chunks past the end
+    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    if (tid < G) hm[tid] = P.hs[bh0 + tid].m;
+    const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;  // the chunk's base list
+    const int n = P.bcnt[static_cast<size_t>(bg) * P.ncg + c];
+    constexpr int NCH = (G * D + kChunkThreads - 1) / kChunkThreads;  // (head, channel) chains per thread
+    double p1[NCH], p2[NCH], pf[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) p1[k] = p2[k] = pf[k] = 0.0;
+    const KVT* vbase = static_cast<const KVT*>(P.v);
+    __syncthreads();
+    for (int t0 = 0; t0 < n; t0 += kNumTile) {
+        const int tn = min(kNumTile, n - t0);
+        for (int x = tid; x < tn * (D / 8); x += nthr) {  // 8 elements per load
+            const int mi = x / (D / 8), e8 = x - mi * (D / 8);
+            Raw8 r;
+            load_raw_nt(vbase + static_cast<size_t>(P.brow[lb + t0 + mi]) * D + 8 * e8, r);
+            float f[8];
+            widen<KVT>(r, f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vs[mi][8 * e8 + e] = f[e];
+        }
+        for (int x = tid; x < tn * G; x += nthr) {
+            const int mi = x / G, h = x - mi * G;
+            const uint32_t meta = P.bmeta[lb + t0 + mi];
+            const bool mem = (meta >> h) & 1u;
+            es[mi][h] = mem ? static_cast<double>(fixed_weight(P.bsc[(lb + t0 + mi) * G + h] - hm[h])) : -1.0;
+            if (h == 0) fx[mi] = meta >> 8;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int ch = tid + k * kChunkThreads;  // chain = head * D + channel
+            if (ch >= G * D) break;
+            const int h = ch / D, cc = ch - h * D;
+            for (int mi = 0; mi < tn; ++mi) {
+                const double e = es[mi][h];
+                if (e < 0.0) continue;  // not in this head's fixed set or base sample
+                const double y = e * static_cast<double>(vs[mi][cc]);
+                if ((fx[mi] >> h) & 1u) {
+                    pf[k] = pf[k] + y;
+                } else {
+                    p1[k] = p1[k] + y;
+                    p2[k] = p2[k] + y * y;
+                }
+            }
+        }
+        __syncthreads();  // the tile is restaged
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int ch = tid + k * kChunkThreads;
+        if (ch >= G * D) break;
+        const int h = ch / D, cc = ch - h * D;
+        double* out = P.npart + ((bh0 + h) * P.ncg + c) * 3 * D;
+        out[cc] = p1[k];
+        out[D + cc] = p2[k];
+        out[2 * D + cc] = pf[k];
+    }
+}
+
+template <int kThreads>  // per block
+__global__ __launch_bounds__(kThreads) void k_budget_num(Plan P) {
+    __shared__ HeadSamp SS;
+    __shared__ SelShared<1> FS;
+    __shared__ double tot[3][128];  // T1, T2, NF per channel (d <= 128)
+    __shared__ int s_nsel;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
+    const int bg = b * P.Hkv + g;
+    const int L = P.seq_lens[b];
+    const int D = P.d;
+    HeadState* hsp = P.hs + bh;
+    if (L == 0) {
+        if (tid == 0 && P.nstats) P.nstats[2 * bh] = P.nstats[2 * bh + 1] = 0.0;
+        return;
+    }
+    const Regions R = regions(P, L);
+    const int NT = R.NT, nb = R.nb;
+    for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
+    if (nb > 0) {  // the chunk partials, summed in chunk order
+        const int nc = (L + P.cg - 1) / P.cg;
+        const double* pp = P.npart + static_cast<size_t>(bh) * P.ncg * 3 * D;
+        for (int x = tid; x < 3 * D; x += nthr) {
+            double t = 0.0;
+            for (int cc = 0; cc < nc; ++cc) t = t + pp[static_cast<size_t>(cc) * 3 * D + x];
+            tot[x / D][x % D] = t;
+        }
     }
     __syncthreads();
-    const uint32_t rank = static_cast<uint32_t>(s_nsel);
-    const uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
-    const BinLists BL{P.soff + static_cast<size_t>(bg) * P.ncp * (kSampBins + 1),
-                      P.slist + static_cast<size_t>(bg) * P.ncp * P.cp, P.ncp, P.cp, R.lo, R.hi};
-    head_sample_threshold(SS, FS, BL, group_words(P, bg), rank, [&](int i) __attribute__((always_inline)) {
-        return bit_of(bits, i);
-    });
     if (tid == 0) {
-        const int n = hsp->n;
-        uint64_t thr = 0;  // n == N_t: the whole tail (n == 0: unused)
-        if (rank > 0) thr = SS.thr;
-        else if (n > 0 && n == R.nb) thr = hsp->thr_b;
-        hsp->thr_n = thr;
+        double TR = 0.0, NN = 0.0;
+        if (nb > 0) {
+            for (int c = 0; c < D; ++c) {
+                double m2 = static_cast<double>(nb) * tot[1][c] - tot[0][c] * tot[0][c];
+                if (m2 < 0.0) m2 = 0.0;
+                const double yc = static_cast<double>(nb) * tot[2][c] + static_cast<double>(NT) * tot[0][c];
+                TR = TR + m2;
+                NN = NN + yc * yc;
+            }
+        }
+        if (P.nstats) {
+            P.nstats[2 * bh] = TR;
+            P.nstats[2 * bh + 1] = NN;
+        }
+        if (P.force_budget < 0 && nb > 0 && nb < NT) {  // the CLT branch
+            const double z = P.z32;
+            const double num = (z * z * static_cast<double>(NT) * static_cast<double>(NT)) *
+                               (TR * static_cast<double>(nb));
+            const double den = (static_cast<double>(nb - 1) * (P.eps * P.eps)) * NN;
+            int nN;
+            if (den == 0.0) {
+                nN = num > 0.0 ? NT : 0;
+            } else {
+                const double r = num / den;
+                nN = r >= static_cast<double>(NT) ? NT : static_cast<int>(__builtin_ceil(r));
+            }
+            if (nN > hsp->n) {
+                hsp->n = nN;
+                hsp->flags = hsp->flags | 8 | (nN == NT ? 1 : 0);
+            }
+        }
+        s_nsel = settle_budget(P, hsp, bg, R, L);
     }
+    __syncthreads();
+    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel));
 }
 
 // ===========================================================================
@@ -1755,11 +1931,28 @@ static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) 
     hipLaunchKernelGGL((k_base<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
     if ((rc = launched()) || (rc = mk.mark(3))) return rc;
     // with many heads the per-head kernels run smaller blocks, several per CU
-    if (p.B * p.Hq >= kManyHeads)
-        hipLaunchKernelGGL(k_budget<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
-    else
-        hipLaunchKernelGGL(k_budget<kBudgetThreads>, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
-    if ((rc = launched()) || (rc = mk.mark(4))) return rc;
+    const bool many = p.B * p.Hq >= kManyHeads;
+    if (p.guarantee == 0) {
+        if (many)
+            hipLaunchKernelGGL((k_budget<kHeadThreadsMany, false>), dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+        else
+            hipLaunchKernelGGL((k_budget<kBudgetThreads, false>), dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
+        if ((rc = launched())) return rc;
+    } else {  // output-level mode: statistics, numerator partials, then the budget
+        if (many)
+            hipLaunchKernelGGL((k_budget<kHeadThreadsMany, true>), dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+        else
+            hipLaunchKernelGGL((k_budget<kBudgetThreads, true>), dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
+        if ((rc = launched())) return rc;
+        hipLaunchKernelGGL((k_numstat<D, KVT, G>), grid_h, dim3(kChunkThreads), 0, st, p);
+        if ((rc = launched())) return rc;
+        if (many)
+            hipLaunchKernelGGL(k_budget_num<kHeadThreadsMany>, dim3(p.B * p.Hq), dim3(kHeadThreadsMany), 0, st, p);
+        else
+            hipLaunchKernelGGL(k_budget_num<kBudgetThreads>, dim3(p.B * p.Hq), dim3(kBudgetThreads), 0, st, p);
+        if ((rc = launched())) return rc;
+    }
+    if ((rc = mk.mark(4))) return rc;
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
     if ((rc = launched())) return rc;
     return mk.mark(5);

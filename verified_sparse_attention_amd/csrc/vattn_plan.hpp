@@ -43,6 +43,7 @@ struct Plan {
     int B, Hq, Hkv, G, d, r, max_blocks, max_seq_len, words;
     // configuration
     int sinks, window, topk_abs, topk_ppm, base_ppm, force_budget, predictor, kv_bf16;
+    int guarantee;  // 0 denominator; 1 denominator and numerator (output-level mode)
     float scale32;
     double z32, eps;
     uint32_t seed_lo, seed_hi;
@@ -72,6 +73,8 @@ struct Plan {
                      // (ascending token order within the chunk; read by budget and gather)
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
+    uint32_t* brow;  // [B*Hkv][ncg][cg] V row of each base-pass member (output-level mode, else null)
+    double* npart;   // [B*Hq][ncg][3][d] numerator partials T1, T2, NF per chunk (output-level mode)
     uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
     uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
     uint32_t* gw;      // [B*Hkv] gather dispatch weight: max over the group's heads of (n_fixed + n) / L, fp32 bits
@@ -89,6 +92,7 @@ struct Plan {
     int32_t* counts;
     uint64_t* stats;
     int32_t* gcounts;  // [B*Hkv][2] optional
+    double* nstats;    // [B*Hq][2] numerator statistics TR, NN (output-level mode), optional
 };
 
 // Launches one decode step.  Returns 0 or a hipError_t value.

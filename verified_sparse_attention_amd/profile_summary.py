@@ -68,25 +68,33 @@ def _find(pattern):
 
 
 def _grid_rows(trace_dir):
-    """Per (decode-step kernel, workload launch) statistics from the kernel
-    trace.  Dispatches are taken in order; every decode step starts with a
-    k_predict, whose grid names the workload's launch configuration, and the
-    step's other kernels are attributed to it.  So the headline workload's
-    select, budget and combine are told from another workload's with the same
-    number of heads."""
+    """Per (decode-step kernel, step kind) statistics from the kernel trace.
+    Dispatches are taken in order and cut into decode steps at each k_predict;
+    a step's kind is its k_predict's instance and grid, plus "+numerator" when
+    the step runs the output-level mode's kernels.  One kind is one workload
+    launch, so the headline workload's select, budget and combine are told from
+    another workload's with the same number of heads."""
     path = _find(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
-    acc = collections.OrderedDict()
-    tag = None
+    steps, cur = [], None
     for r in rows:
         st = _stage(r["Kernel_Name"])
         if st is None or st == "k_project":
             continue
         grid = tuple(int(r["Grid_Size_%s" % a]) // max(int(r["Workgroup_Size_%s" % a]), 1) for a in "XYZ")
-        if st == "k_predict":
-            tag = "predict%s" % (grid,)
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        acc.setdefault((_short(r["Kernel_Name"]), grid, tag), []).append(dur)
+        if st == "k_predict" or cur is None:
+            cur = []
+            steps.append(cur)
+        cur.append((_short(r["Kernel_Name"]), grid, dur))
+    acc = collections.OrderedDict()
+    for step in steps:
+        head = step[0]
+        tag = "%s %s" % (head[0], head[1]) if head[0].startswith("k_predict") else "(no predict)"
+        if any(n.startswith("k_numstat") for n, _, _ in step):
+            tag += " +numerator"
+        for name, grid, dur in step:
+            acc.setdefault((name, grid, tag), []).append(dur)
     return acc
 
 
@@ -110,14 +118,15 @@ def stats(args):
     except SystemExit:
         grid = {}
     if grid:
-        lines += ["", "# decode-step kernels by workload launch: grid in workgroups, step = the k_predict grid "
-                      "of the decode step the dispatch belongs to; the headline workload's step is marked *",
-                  "%-34s %-16s %-26s %7s %9s %9s %9s" % ("kernel", "grid", "step", "calls", "mean_us",
+        lines += ["", "# decode-step kernels by step kind: grid in workgroups; step = the k_predict instance and grid "
+                      "that opened the dispatch's decode step (+numerator: output-level mode); the headline "
+                      "workload's steps are marked *",
+                  "%-34s %-16s %-52s %7s %9s %9s %9s" % ("kernel", "grid", "step", "calls", "mean_us",
                                                         "median_us", "max_us")]
         for (name, g, tag), d in sorted(grid.items(), key=lambda kv: (str(kv[0][2]), kv[0][0])):
             d = sorted(d)
-            star = "*" if args.headline_step and tag == "predict" + args.headline_step else " "
-            lines.append("%-34s %-16s %-26s %7d %9.2f %9.2f %9.2f %s" % (
+            star = "*" if args.headline_step and tag == args.headline_step else " "
+            lines.append("%-34s %-16s %-52s %7d %9.2f %9.2f %9.2f %s" % (
                 name, str(g), str(tag), len(d), sum(d) / len(d), d[len(d) // 2], d[-1], star))
     text = "\n".join(lines) + "\n"
     with open(args.out, "w") as f:
@@ -185,7 +194,7 @@ def main(argv=None):
     a.add_argument("--cmd", required=True)
     a.add_argument("--out", required=True)
     a.add_argument("--headline-step", default=None,
-                   help="the headline workload's k_predict grid in workgroups, e.g. '(4, 64, 1)'")
+                   help="the headline workload's step kind, e.g. 'k_predict<32, unsigned short, 4> (4, 64, 1)'")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
