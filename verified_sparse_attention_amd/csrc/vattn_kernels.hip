@@ -1133,69 +1133,138 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
 // ===========================================================================
 constexpr int kNumTile = 64;  // base-list members whose V rows are staged at once
 
+// One block per (gather chunk, group): the chunk's base list (ascending tokens)
+// is walked in tiles of kNumTile members whose V rows are staged raw in LDS;
+// the next tile's rows are requested before the current tile is summed.  Per
+// tile and head, one wave ballot lists the head's base-sample members and its
+// fixed members, each ascending; each thread owns (head, channel) chains and
+// adds to them the members of the head's lists in order (T1 and T2 over the
+// base-sample list, NF over the fixed list).
 template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
-    __shared__ float vs[kNumTile][D];       // the tile's V rows
-    __shared__ double es[kNumTile][G];      // E_i of each member for each head (0: not a member)
-    __shared__ uint32_t fx[kNumTile];       // fixed mask of each member
+    static_assert(kNumTile == 64, "one wave ballot per tile");
+    constexpr int NW = kChunkThreads / 64;
+    constexpr int RPL = sizeof(KVT) * 8 / 16;                 // 16-byte loads per 8 elements
+    constexpr int LPM = D / 8 * RPL;                          // 16-byte loads per member row
+    constexpr int VPT = (kNumTile * LPM + kChunkThreads - 1) / kChunkThreads;  // per thread and tile
+    constexpr int EPT = (kNumTile * G + kChunkThreads - 1) / kChunkThreads;
+    __shared__ __align__(16) KVT vs[kNumTile][D];  // the tile's V rows as stored
+    __shared__ double es[kNumTile][G];           // E_i of each member for each head
+    __shared__ uint32_t tm[kNumTile];            // base mask | fixed mask << 8 of each member
+    __shared__ uint8_t lst[2][G][kNumTile];      // per head: base-sample members, fixed members
+    __shared__ int lcnt[2][G];
+    __shared__ uint32_t rows[kGatherChunk];      // V rows of the chunk's members
     __shared__ float hm[G];
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.x, c = blockIdx.y, b = blockIdx.z, bg = b * P.Hkv + g;
     const int L = P.seq_lens[b];
     if (c * P.cg >= L) return;  // block-uniform; no partial for chunks past the end
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-    if (tid < G) hm[tid] = P.hs[bh0 + tid].m;
     const size_t lb = (static_cast<size_t>(bg) * P.ncg + c) * P.cg;  // the chunk's base list
     const int n = P.bcnt[static_cast<size_t>(bg) * P.ncg + c];
+    if (tid < G) hm[tid] = P.hs[bh0 + tid].m;
+    for (int x = tid; x < n; x += kChunkThreads) rows[x] = P.brow[lb + x];
     constexpr int NCH = (G * D + kChunkThreads - 1) / kChunkThreads;  // (head, channel) chains per thread
     double p1[NCH], p2[NCH], pf[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) p1[k] = p2[k] = pf[k] = 0.0;
-    const KVT* vbase = static_cast<const KVT*>(P.v);
+    // chain k: head hk[k], channel cc (the same for every k: the chains of a
+    // thread are kChunkThreads apart, a multiple of D); a wave's lanes share
+    // the head
+    const int cc = tid % D;
+    int hk[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) hk[k] = (tid + k * kChunkThreads) / D;
+    const uint4* vbase = static_cast<const uint4*>(P.v);
     __syncthreads();
+    uint4 vr[VPT];
+    float sr[EPT];
+    uint32_t mr[EPT];
+    auto request = [&](int t0) __attribute__((always_inline)) {
+        const int tn = min(kNumTile, n - t0);
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int x = tid + u * kChunkThreads, mi = x / LPM, part = x - mi * LPM;
+            if (mi < tn) vr[u] = nt_load16(vbase + static_cast<size_t>(rows[t0 + mi]) * LPM + part);
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int x = tid + u * kChunkThreads, mi = x / G, h = x - mi * G;
+            if (mi < tn) {
+                mr[u] = P.bmeta[lb + t0 + mi];
+                sr[u] = P.bsc[(lb + t0 + mi) * G + h];
+            }
+        }
+    };
+    if (n > 0) request(0);
     for (int t0 = 0; t0 < n; t0 += kNumTile) {
         const int tn = min(kNumTile, n - t0);
-        for (int x = tid; x < tn * (D / 8); x += nthr) {  // 8 elements per load
-            const int mi = x / (D / 8), e8 = x - mi * (D / 8);
-            Raw8 r;
-            load_raw_nt(vbase + static_cast<size_t>(P.brow[lb + t0 + mi]) * D + 8 * e8, r);
-            float f[8];
-            widen<KVT>(r, f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vs[mi][8 * e8 + e] = f[e];
+        for (int u = 0; u < VPT; ++u) {
+            const int x = tid + u * kChunkThreads, mi = x / LPM, part = x - mi * LPM;
+            if (mi < tn) reinterpret_cast<uint4*>(&vs[mi][0])[part] = vr[u];
         }
-        for (int x = tid; x < tn * G; x += nthr) {
-            const int mi = x / G, h = x - mi * G;
-            const uint32_t meta = P.bmeta[lb + t0 + mi];
-            const bool mem = (meta >> h) & 1u;
-            es[mi][h] = mem ? static_cast<double>(fixed_weight(P.bsc[(lb + t0 + mi) * G + h] - hm[h])) : -1.0;
-            if (h == 0) fx[mi] = meta >> 8;
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int x = tid + u * kChunkThreads, mi = x / G, h = x - mi * G;
+            if (mi < tn) {
+                es[mi][h] = static_cast<double>(fixed_weight(sr[u] - hm[h]));
+                if (h == 0) tm[mi] = mr[u];
+            }
         }
         __syncthreads();
+        for (int h = wave; h < G; h += NW) {  // lane = member of the tile
+            const uint32_t meta = lane < tn ? tm[lane] : 0u;
+            const bool mem = (meta >> h) & 1u, fix = (meta >> (8 + h)) & 1u;
+            const uint64_t bb = __ballot(mem && !fix), bf = __ballot(mem && fix);
+            const uint64_t below = (1ull << lane) - 1ull;
+            if (mem && !fix) lst[0][h][__popcll(bb & below)] = static_cast<uint8_t>(lane);
+            if (mem && fix) lst[1][h][__popcll(bf & below)] = static_cast<uint8_t>(lane);
+            if (lane == 0) {
+                lcnt[0][h] = __popcll(bb);
+                lcnt[1][h] = __popcll(bf);
+            }
+        }
+        __syncthreads();
+        if (t0 + kNumTile < n) request(t0 + kNumTile);  // block-uniform
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const int ch = tid + k * kChunkThreads;  // chain = head * D + channel
-            if (ch >= G * D) break;
-            const int h = ch / D, cc = ch - h * D;
-            for (int mi = 0; mi < tn; ++mi) {
-                const double e = es[mi][h];
-                if (e < 0.0) continue;  // not in this head's fixed set or base sample
-                const double y = e * static_cast<double>(vs[mi][cc]);
-                if ((fx[mi] >> h) & 1u) {
-                    pf[k] = pf[k] + y;
-                } else {
-                    p1[k] = p1[k] + y;
-                    p2[k] = p2[k] + y * y;
+            const int h = hk[k];
+            if (h >= G) break;  // wave-uniform
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {  // q = 0: base sample (T1, T2); q = 1: fixed set (NF)
+                const int nl = lcnt[q][h];
+                for (int j0 = 0; j0 < nl; j0 += 8) {
+                    double e[8];
+                    float vf[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int mi = lst[q][h][min(j0 + u, nl - 1)];
+                        e[u] = es[mi][h];
+                        if constexpr (sizeof(KVT) == 2) vf[u] = __uint_as_float(static_cast<uint32_t>(vs[mi][cc]) << 16);
+                        else vf[u] = vs[mi][cc];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (j0 + u >= nl) break;  // wave-uniform
+                        const double y = e[u] * static_cast<double>(vf[u]);
+                        if (q == 0) {
+                            p1[k] = p1[k] + y;
+                            p2[k] = p2[k] + y * y;
+                        } else {
+                            pf[k] = pf[k] + y;
+                        }
+                    }
                 }
             }
         }
-        __syncthreads();  // the tile is restaged
+        __syncthreads();  // the tile and its lists are restaged
     }
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int ch = tid + k * kChunkThreads;
+        const int ch = tid + k * kChunkThreads;  // chain = head * D + channel
         if (ch >= G * D) break;
-        const int h = ch / D, cc = ch - h * D;
+        const int h = ch / D;
         double* out = P.npart + ((bh0 + h) * P.ncg + c) * 3 * D;
         out[cc] = p1[k];
         out[D + cc] = p2[k];
