@@ -329,16 +329,23 @@ def main():
     value = heads_tokens / (ms_per_step * 1e-3)
     log("%.4f ms/step, %.4g heads*tokens/s (wall %.4f ms/step)" % (ms_per_step, value, t_wall * 1e3 / steps))
 
-    # ---- per-kernel durations with events on the launch stream, same steps
+    # ---- per-kernel durations with events on the launch stream, same steps and
+    # launches as the timed ones; then the same seeds once more with the group
+    # counts (|U_g|, |B_g|) the byte accounting needs
     nst = vsa.NUM_STAGES
     ev = HipEvents((nst + 1) * steps)
     stage_ms = np.zeros(nst)
     gsum = torch.zeros(w.B, w.Hkv, 2, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     for s in range(steps):
-        dd = pdecs[s % n_inst]
+        dd = decs[s % n_inst]
         dd.set_seed(s)
         dd.profiled(ev.ev[(nst + 1) * s:(nst + 1) * (s + 1)])
+    torch.cuda.synchronize()
+    for s in range(steps):
+        dd = pdecs[s % n_inst]
+        dd.set_seed(s)
+        dd()
         gsum += dd.group_counts
     torch.cuda.synchronize()
     for s in range(steps):

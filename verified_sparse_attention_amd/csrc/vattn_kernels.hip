@@ -617,10 +617,17 @@ __global__ __launch_bounds__(kSelectThreads) void k_premerge(Plan P) {
 // select: exact top-k, fixed-set bitmap, tail histograms, base threshold
 // ===========================================================================
 
-template <bool PM>  // PM: the candidates come pre-merged in P.nparts parts
+constexpr int kSelLdsWords = 4096;  // fixed-set bitmaps of up to 131072 tokens are built in LDS
+constexpr int kSelRegKeys = 8;      // candidate keys per thread held in registers (when they all fit)
+
+// PM: the candidates come pre-merged in P.nparts parts.  LB: the head's
+// fixed-set bitmap is built in LDS (max_seq_len <= 32 * kSelLdsWords) and
+// stored once at the end; otherwise it is built in place in global memory.
+template <bool PM, bool LB>
 __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     __shared__ TopkShared<1> TS;
     __shared__ HeadSamp SS;
+    __shared__ uint32_t lbits[LB ? kSelLdsWords : 1];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
     const int bg = b * P.Hkv + g;
@@ -642,13 +649,50 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
         if constexpr (PM) return static_cast<int>(pcnt[c]);
         else return chunk_candidates(cp, R, c);
     };
-    uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
+    uint32_t* __restrict__ gbits = P.bits + static_cast<size_t>(bh) * P.words;
+    uint32_t* __restrict__ bits = LB ? lbits : gbits;
     const uint32_t* soffg = P.soff + static_cast<size_t>(bg) * ncp * (kSampBins + 1);
     if (tid == 0 && P.gcounts && h % P.G == 0) {
         P.gcounts[2 * bg] = 0;
         P.gcounts[2 * bg + 1] = 0;
     }
     if (tid == 0 && h % P.G == 0) P.gw[bg] = 0u;  // the budgets raise it
+
+    // the candidates are requested first, so their loads overlap the tail
+    // histogram's: into registers when every slot fits, with the parts' key
+    // brackets
+    const int slots = nparts * pk;
+    const bool inreg = R.k > 0 && slots <= kSelRegKeys * nthr;  // block-uniform
+    uint64_t rk[kSelRegKeys];
+    bool rv[kSelRegKeys];
+#pragma unroll
+    for (int t = 0; t < kSelRegKeys; ++t) {
+        const int x = tid + t * nthr;
+        const int c = x / pk, p = x - c * pk;
+        rv[t] = inreg && x < slots && p < part_count(c);
+        rk[t] = rv[t] ? cand[x] : 0ull;
+    }
+    constexpr int kCB = 4;  // chunks whose loads are issued together
+    uint32_t tot = 0, lo = 0xFFFFFFFFu, hi = 0;
+    if (R.k > 0) {
+        for (int c0 = 0; c0 < nparts; c0 += kCB) {
+            uint32_t clo[kCB], chi[kCB];
+#pragma unroll
+            for (int t = 0; t < kCB; ++t) {
+                const int c = c0 + t;
+                const int nc = c < nparts ? part_count(c) : 0;
+                tot += static_cast<uint32_t>(nc);
+                const uint32_t* cr = crng + static_cast<size_t>(nc ? c : 0) * 2;
+                clo[t] = nc ? cr[0] : 0xFFFFFFFFu;
+                chi[t] = nc ? cr[1] : 0u;
+            }
+#pragma unroll
+            for (int t = 0; t < kCB; ++t) {
+                lo = min(lo, clo[t]);
+                hi = max(hi, chi[t]);
+            }
+        }
+    }
 
     // 1) bitmap: sinks [0, sp), window [hi, L); tail histogram = middle histogram
     const int wl = (L + 31) >> 5;
@@ -662,7 +706,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
         }
         bits[w] = word;
     }
-    constexpr int kCB = 4;  // chunks whose loads are issued together
     if constexpr (PM) {
         const uint32_t* h2 = P.hist2 + static_cast<size_t>(bg) * np * kSampBins;
         for (int x = tid; x < kSampBins; x += nthr) {
@@ -692,28 +735,15 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     // 2) exact top-k from the chunk candidates: set the bit and take the token
     //    out of the tail histogram (block_topk starts with a barrier)
     if (R.k > 0) {
-        uint32_t tot = 0, lo = 0xFFFFFFFFu, hi = 0;
-        for (int c0 = 0; c0 < nparts; c0 += kCB) {
-            uint32_t clo[kCB], chi[kCB];
-#pragma unroll
-            for (int t = 0; t < kCB; ++t) {
-                const int c = c0 + t;
-                const int nc = c < nparts ? part_count(c) : 0;
-                tot += static_cast<uint32_t>(nc);
-                const uint32_t* cr = crng + static_cast<size_t>(nc ? c : 0) * 2;
-                clo[t] = nc ? cr[0] : 0xFFFFFFFFu;
-                chi[t] = nc ? cr[1] : 0u;
-            }
-#pragma unroll
-            for (int t = 0; t < kCB; ++t) {
-                lo = min(lo, clo[t]);
-                hi = max(hi, chi[t]);
-            }
-        }
         const uint32_t want[1] = {static_cast<uint32_t>(R.k)}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
-        const int slots = nparts * pk;
         constexpr int kBatch = 8;  // candidate keys loaded before any is visited
         block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
+            if (inreg) {
+#pragma unroll
+                for (int t = 0; t < kSelRegKeys; ++t)
+                    if (rv[t]) f(0, static_cast<uint32_t>(rk[t] >> 32), ~static_cast<uint32_t>(rk[t]));
+                return;
+            }
             for (int x0 = tid; x0 < slots; x0 += kBatch * nthr) {
                 uint64_t kk[kBatch];
                 bool ok[kBatch];
@@ -742,8 +772,11 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     const uint32_t rank = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
     const BinLists BL{soffg, P.slist + static_cast<size_t>(bg) * ncp * cp, ncp, cp, R.lo, R.hi};
     head_sample_threshold(SS, TS.S, BL, uwg, rank, [&](int i) __attribute__((always_inline)) {
-        return bit_of_coherent(bits, i);
+        if constexpr (LB) return bit_of(lbits, i);   // complete after block_topk's closing barrier
+        else return bit_of_coherent(gbits, i);
     });
+    if constexpr (LB)
+        for (int w = tid; w < wl; w += nthr) gbits[w] = lbits[w];
     if (tid == 0) {
         HeadState hs{};  // statistics, budget and thresholds are filled in by the budget pass
         hs.L = L;
@@ -1389,6 +1422,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ float wred[NW][G];
     __shared__ float hmax[G], hsum[G];
     __shared__ int s_over;  // some member score exceeds its head's reference by kRescale
+    __shared__ int wfin[NW];
     static_assert(NW * D <= kGatherChunk, "per-wave sums fit in the weight array");
     float (*wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&sp[0][0]);  // reuses sp after the V pass
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -1465,11 +1499,16 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
             nfin += (m4[e] & 0xFFu) ? 1 : 0;
         }
     const int n = nu + static_cast<int>(cnt >> 16);
-    if (P.gcounts) {  // block-uniform
+    if (P.gcounts) {  // block-uniform: one atomic per block, after the barrier below
         for (int o = 32; o >= 1; o >>= 1) nfin += __shfl_xor(nfin, o, 64);
-        if (lane == 0 && nfin) atomicAdd(&P.gcounts[2 * bg], nfin);
+        if (lane == 0) wfin[wave] = nfin;
     }
     __syncthreads();
+    if (P.gcounts && tid == 0) {
+        int t = 0;
+        for (int w2 = 0; w2 < NW; ++w2) t += wfin[w2];
+        if (t) atomicAdd(&P.gcounts[2 * bg], t);
+    }
 
     // (1) scores into LDS (-inf for heads the token does not belong to).
     // Tokens of the base pass take their pinned scores from its list (entry
@@ -2068,13 +2107,16 @@ static int launch_g(const Plan& p, hipStream_t st, const Marks& mk) {
     if (rc) return rc;
     if ((rc = mk.mark(1))) return rc;
     // 2. exact top-k, bitmap, base threshold
+    const bool lds_bits = p.words <= kSelLdsWords;
     if (p.nparts > 0) {
         hipLaunchKernelGGL(k_premerge, dim3(p.B * p.Hq, p.nparts), dim3(kSelectThreads), 0, st, p);
         if ((rc = launched())) return rc;
-        hipLaunchKernelGGL(k_select<true>, dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+        if (lds_bits) hipLaunchKernelGGL((k_select<true, true>), dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
+        else hipLaunchKernelGGL((k_select<true, false>), dim3(p.B * p.Hq), dim3(kSelectThreads), 0, st, p);
     } else {
-        hipLaunchKernelGGL(k_select<false>, dim3(p.B * p.Hq),
-                           dim3(p.B * p.Hq >= kManyHeads ? kHeadThreadsMany : kSelectThreads), 0, st, p);
+        const dim3 blk(p.B * p.Hq >= kManyHeads ? kHeadThreadsMany : kSelectThreads);
+        if (lds_bits) hipLaunchKernelGGL((k_select<false, true>), dim3(p.B * p.Hq), blk, 0, st, p);
+        else hipLaunchKernelGGL((k_select<false, false>), dim3(p.B * p.Hq), blk, 0, st, p);
     }
     if ((rc = launched()) || (rc = mk.mark(2))) return rc;
     // 3-5. base scores, budget, gather
