@@ -121,7 +121,7 @@ vattn_status check(const vattn_inputs* in, const vattn_cfg* cfg, Shape* sh) {
 }
 
 struct Layout {
-    size_t cand, bits, hs, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, uw, crange, gw, cand2, crange2, pcount, hist2,
+    size_t cand, bits, hs, cmax, part, soff, slist, hh, bsc, bmeta, bcnt, crange, gw, cand2, crange2, pcount, hist2,
         brow, npart, total;
 };
 
@@ -152,8 +152,6 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t));
     L.bcnt = off;
     off += align_up(BHkv * s.ncg * sizeof(int32_t));
-    L.uw = off;
-    off += align_up(BHkv * (static_cast<size_t>(s.ncg) * s.cg) * sizeof(uint32_t));
     L.crange = off;
     off += align_up(BHq * s.ncp * 2 * sizeof(uint32_t));
     L.gw = off;
@@ -260,7 +258,6 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.bsc = reinterpret_cast<float*>(ws + L.bsc);
     p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
-    p.uw = reinterpret_cast<uint32_t*>(ws + L.uw);
     p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
     p.gw = reinterpret_cast<uint32_t*>(ws + L.gw);
     p.nparts = s.nparts;

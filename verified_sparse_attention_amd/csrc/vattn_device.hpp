@@ -37,6 +37,17 @@ __device__ __forceinline__ uint32_t word_of(const uint4& w, int e) {
     return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
 }
 
+// Sample words of the token quad qd (tokens 4 qd .. 4 qd + 3) of sequence b,
+// KV head g: one Philox4x32-10 block, recomputed wherever a pass needs them
+// (cheaper than storing 4 bytes per token and reading them back).
+__device__ __forceinline__ uint4 quad_words(uint32_t qd, uint32_t g, uint32_t b, uint32_t seed_lo, uint32_t seed_hi) {
+    return philox4x32_10(qd, g, b, 0, seed_lo, seed_hi);
+}
+
+__device__ __forceinline__ uint32_t token_word(uint32_t i, uint32_t g, uint32_t b, uint32_t seed_lo, uint32_t seed_hi) {
+    return word_of(quad_words(i >> 2, g, b, seed_lo, seed_hi), static_cast<int>(i & 3u));
+}
+
 // Sample order: ascending (Philox word u, token index i).  Stored complemented
 // so that "first n of the order" == "n largest keys".
 __device__ __forceinline__ uint64_t sample_key(uint32_t u, uint32_t i) {
@@ -326,6 +337,28 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return before + inc - v;
 }
 
+// N exclusive block scans at once: v[x] becomes the sum of v[x] over the
+// threads before this one.  wsum holds N * (waves) words.  Every thread
+// calls; ends with a barrier.
+template <int N>
+__device__ __forceinline__ void block_excl_scan_n(uint32_t (&v)[N], uint32_t* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    uint32_t inc[N];
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+        inc[x] = wave_incl_scan(v[x]);
+        if (lane == 63) wsum[x * nw + wave] = inc[x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < N; ++x) {
+        uint32_t before = 0;
+        for (int w = 0; w < wave; ++w) before += wsum[x * nw + w];
+        v[x] = before + inc[x] - v[x];
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
     const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
@@ -522,10 +555,11 @@ __device__ __forceinline__ void list_rank_pick(const uint64_t* list, int n, uint
 // every key above the boundary bucket and lists the boundary bucket's keys,
 // which are then ranked exactly.  Only a boundary bucket larger than
 // kListCap falls back to the radix select.  items(f) calls f(h, okey, index)
-// for every key of head h on this thread; emit(h, key) is called exactly once
-// for each of the want[h] largest keys topk_key(okey, index) of head h (for
-// every key when want[h] >= total[h]).  On return thr[h] is the smallest
-// emitted key (0 when everything was emitted).
+// for every key of head h on this thread; emit(h, pos, key) is called exactly
+// once for each of the want[h] largest keys topk_key(okey, index) of head h
+// (for every key when want[h] >= total[h]), with distinct positions
+// pos < want[h].  On return thr[h] is the smallest emitted key (0 when
+// everything was emitted).
 // ---------------------------------------------------------------------------
 template <int NH>
 struct TopkShared {
@@ -554,12 +588,13 @@ __device__ __forceinline__ int topk_bucket(uint32_t ok, float vmin, float scale)
     return bk < kTopBuckets - 1 ? bk : kTopBuckets - 1;
 }
 
-template <int NH, class Items, class Emit>
-__device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
-                           const uint32_t (&lo_ok)[NH], const uint32_t (&hi_ok)[NH], Items&& items,
-                           Emit&& emit) {
+// Per-head setup of a top-k: bucket maps, modes and counters in LDS, the
+// bucket histograms cleared.  Ends with a barrier; returns whether any head
+// needs the selection (mode 1).
+template <int NH>
+__device__ __forceinline__ bool topk_setup(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
+                                           const uint32_t (&lo_ok)[NH], const uint32_t (&hi_ok)[NH]) {
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     // per-head parameters live in LDS: the visitors index them by a head number
     // that need not be a compile-time constant after inlining
 #pragma unroll
@@ -577,6 +612,7 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
         T.scale[h] = ok ? scale : 0.0f;
         T.mode[h] = act ? 1u : all ? 2u : 0u;
         T.cnt[h] = 0;
+        T.aux[h] = 0;  // emission positions
         T.thr[h] = 0;
         T.bstar[h] = -1;
         T.above[h] = 0;
@@ -586,57 +622,35 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
     for (int h = 0; h < NH; ++h) any |= want[h] > 0 && want[h] < total[h];
     for (int x = tid; x < NH * kTopBuckets; x += nthr) (&T.S.hist[0][0])[x] = 0;
     __syncthreads();
-    // the heads' bucket maps in registers (the visitors' head numbers are
-    // compile-time constants once inlined)
-    uint32_t md[NH];
-    float vmn[NH], scl[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        md[h] = T.mode[h];
-        vmn[h] = T.vmin[h];
-        scl[h] = T.scale[h];
-    }
-    if (any) {
-        // (B) bucket histogram
-        items([&](int h, uint32_t ok, uint32_t) __attribute__((always_inline)) {
-            if (md[h] == 1u) atomicAdd(&T.S.hist[h][topk_bucket(ok, vmn[h], scl[h])], 1u);
-        });
-        __syncthreads();
-        for (int h = wave; h < NH; h += nwaves) {
-            if (T.mode[h] != 1u) continue;
-            int bin;
-            uint32_t before;
-            wave_rank_bin<kTopBuckets>(T.S.hist[h], T.want[h], true, bin, before);
-            if (lane == 0) {
-                T.bstar[h] = bin;
-                T.above[h] = before;
-            }
+    return any;
+}
+
+// The boundary bucket of every selecting head from its histogram: bstar, and
+// the number of keys above it.  Ends with a barrier.
+template <int NH>
+__device__ __forceinline__ void topk_rank(TopkShared<NH>& T) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    for (int h = wave; h < NH; h += nwaves) {
+        if (T.mode[h] != 1u) continue;
+        int bin;
+        uint32_t before;
+        wave_rank_bin<kTopBuckets>(T.S.hist[h], T.want[h], true, bin, before);
+        if (lane == 0) {
+            T.bstar[h] = bin;
+            T.above[h] = before;
         }
-        __syncthreads();
-    }
-    // (C) emit the keys above the boundary bucket, list the boundary bucket
-    int bst[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) bst[h] = T.bstar[h];
-    items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
-        if (md[h] == 2u) {
-            emit(h, topk_key(ok, idx));
-        } else if (md[h] == 1u) {
-            const int bk = topk_bucket(ok, vmn[h], scl[h]);
-            const int bs = bst[h];
-            if (bk > bs) {
-                emit(h, topk_key(ok, idx));
-            } else if (bk == bs) {
-                const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
-                if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
-            }
-        }
-    });
-    if (!any) {
-        __syncthreads();
-        return;
     }
     __syncthreads();
+}
+
+// After the keys above the boundary buckets are emitted and the buckets'
+// keys listed (and a barrier): rank each listed bucket and emit its keys
+// that belong to the top-k; a bucket too large for the list is ranked by the
+// radix select over boundary(f), which calls f(h, okey, index) for every key
+// of head h's boundary bucket on this thread.
+template <int NH, class Boundary, class Emit>
+__device__ __forceinline__ void topk_finish(TopkShared<NH>& T, Boundary&& boundary, Emit&& emit) {
+    const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
     uint32_t fmask = 0;
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -651,7 +665,7 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
         const int h = x / kListCap, e = x - h * kListCap;
         if (T.mode[h] == 1u && T.bstar[h] >= 0 && !((fmask >> h) & 1u) && e < static_cast<int>(T.cnt[h]) &&
             T.list[h][e] >= T.thr[h])
-            emit(h, T.list[h][e]);
+            emit(h, atomicAdd(&T.aux[h], 1u), T.list[h][e]);
     }
     if (fmask) {  // rare: a crowded boundary bucket, ranked by the radix select
         uint32_t fw[NH];
@@ -671,8 +685,8 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
                 ka[h] = ~0ull;
                 ko[h] = 0ull;
             }
-            items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
-                if (((fmask >> h) & 1u) && topk_bucket(ok, vmn[h], scl[h]) == bst[h]) {
+            boundary([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+                if ((fmask >> h) & 1u) {
                     const uint64_t key = topk_key(ok, idx);
                     ka[h] &= key;
                     ko[h] |= key;
@@ -694,20 +708,165 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
         }
         __syncthreads();
         block_select<NH>(T.S, fw, [&](auto&& visit) __attribute__((always_inline)) {
-            items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
-                if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h])
-                    visit(h, topk_key(ok, idx));
+            boundary([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+                if ((fmask >> h) & 1u) visit(h, topk_key(ok, idx));
             });
         }, true, T.kand, T.kor);
         __syncthreads();
-        items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
-            if (((fmask >> h) & 1u) && topk_bucket(ok, T.vmin[h], T.scale[h]) == T.bstar[h] &&
-                topk_key(ok, idx) >= T.S.thr[h])
-                emit(h, topk_key(ok, idx));
+        boundary([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+            if (((fmask >> h) & 1u) && topk_key(ok, idx) >= T.S.thr[h])
+                emit(h, atomicAdd(&T.aux[h], 1u), topk_key(ok, idx));
         });
         if (tid < NH && ((fmask >> tid) & 1u)) T.thr[tid] = T.S.thr[tid];
     }
     __syncthreads();
+}
+
+template <int NH, class Items, class Emit>
+__device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&want)[NH], const uint32_t (&total)[NH],
+                           const uint32_t (&lo_ok)[NH], const uint32_t (&hi_ok)[NH], Items&& items,
+                           Emit&& emit) {
+    const bool any = topk_setup<NH>(T, want, total, lo_ok, hi_ok);
+    // the heads' bucket maps in registers (the visitors' head numbers are
+    // compile-time constants once inlined)
+    uint32_t md[NH];
+    float vmn[NH], scl[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        md[h] = T.mode[h];
+        vmn[h] = T.vmin[h];
+        scl[h] = T.scale[h];
+    }
+    if (any) {
+        // (B) bucket histogram
+        items([&](int h, uint32_t ok, uint32_t) __attribute__((always_inline)) {
+            if (md[h] == 1u) atomicAdd(&T.S.hist[h][topk_bucket(ok, vmn[h], scl[h])], 1u);
+        });
+        __syncthreads();
+        topk_rank<NH>(T);
+    }
+    // (C) emit the keys above the boundary bucket, list the boundary bucket
+    int bst[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) bst[h] = T.bstar[h];
+    items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+        if (md[h] == 2u) {
+            emit(h, atomicAdd(&T.aux[h], 1u), topk_key(ok, idx));
+        } else if (md[h] == 1u) {
+            const int bk = topk_bucket(ok, vmn[h], scl[h]);
+            const int bs = bst[h];
+            if (bk > bs) {
+                emit(h, atomicAdd(&T.aux[h], 1u), topk_key(ok, idx));
+            } else if (bk == bs) {
+                const uint32_t pos = atomicAdd(&T.cnt[h], 1u);
+                if (pos < static_cast<uint32_t>(kListCap)) T.list[h][pos] = topk_key(ok, idx);
+            }
+        }
+    });
+    __syncthreads();
+    if (!any) return;
+    topk_finish<NH>(T, [&](auto&& f) __attribute__((always_inline)) {
+        items([&](int h, uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+            if (md[h] == 1u && topk_bucket(ok, vmn[h], scl[h]) == bst[h]) f(h, ok, idx);
+        });
+    }, emit);
+}
+
+// The same selection for keys at fixed per-thread slots, at most 32 per
+// thread, slot s holding a key of head (s / 4) % NH.  items(f) calls
+// f(s, okey, index) for every key on this thread (the head is the slot's);
+// fetch(s, g) calls g(okey, index) for slot s's key again.  The histogram
+// pass keeps each key's bucket (a byte per slot), so classing a key later is
+// one compare; the keys above the boundary bucket get positions from a block
+// scan of per-thread counts and only those slots are visited to emit them.
+template <int NH>
+__host__ __device__ constexpr uint32_t topk_head_slots(int h) {
+    uint32_t m = 0;
+    for (int s = 0; s < 32; ++s)
+        if ((s / 4) % NH == h) m |= 1u << s;
+    return m;
+}
+
+template <int NH, class Items, class Fetch, class Emit>
+__device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32_t (&want)[NH],
+                                                 const uint32_t (&total)[NH], const uint32_t (&lo_ok)[NH],
+                                                 const uint32_t (&hi_ok)[NH], Items&& items, Fetch&& fetch,
+                                                 Emit&& emit) {
+    const bool any = topk_setup<NH>(T, want, total, lo_ok, hi_ok);
+    uint32_t md[NH];
+    float vmn[NH], scl[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        md[h] = T.mode[h];
+        vmn[h] = T.vmin[h];
+        scl[h] = T.scale[h];
+    }
+    // (B) bucket histogram; every key's bucket kept
+    uint32_t pk[8];  // byte s % 4 of word s / 4: slot s's bucket
+    uint32_t have = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) pk[w] = 0;
+    items([&](int s, uint32_t ok, uint32_t) __attribute__((always_inline)) {
+        const int h = (s / 4) % NH;
+        const int bk = topk_bucket(ok, vmn[h], scl[h]);
+        if (md[h] == 1u) atomicAdd(&T.S.hist[h][bk], 1u);
+        pk[s / 4] |= static_cast<uint32_t>(bk) << (8 * (s % 4));
+        have |= 1u << s;
+    });
+    if (any) {
+        __syncthreads();
+        topk_rank<NH>(T);
+    }
+    // (C) classes: above the boundary bucket (emitted), in it (listed); a
+    //     head emitting everything has bst -1, an idle head 256
+    int bst[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) bst[h] = md[h] == 2u ? -1 : md[h] == 1u ? T.bstar[h] : kTopBuckets;
+    uint32_t emask = 0, lmask = 0;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+        const int bk = static_cast<int>((pk[s / 4] >> (8 * (s % 4))) & 0xFFu);
+        emask |= bk > bst[(s / 4) % NH] ? 1u << s : 0u;
+        lmask |= bk == bst[(s / 4) % NH] ? 1u << s : 0u;
+    }
+    emask &= have;
+    lmask &= have;
+    uint32_t cnt[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) cnt[h] = static_cast<uint32_t>(__builtin_popcount(emask & topk_head_slots<NH>(h)));
+    block_excl_scan_n<NH>(cnt, &T.S.hist[0][0]);  // the histograms are spent: the scan's scratch
+    // (D) list the boundary buckets, emit the keys above them, head by head
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        uint32_t m = lmask & topk_head_slots<NH>(h);
+        while (m) {
+            const int s = __builtin_ctz(m);
+            m &= m - 1;
+            fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
+                const uint32_t p = atomicAdd(&T.cnt[h], 1u);
+                if (p < static_cast<uint32_t>(kListCap)) T.list[h][p] = topk_key(ok, idx);
+            });
+        }
+        m = emask & topk_head_slots<NH>(h);
+        uint32_t p = cnt[h];
+        while (m) {
+            const int s = __builtin_ctz(m);
+            m &= m - 1;
+            fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { emit(h, p++, topk_key(ok, idx)); });
+        }
+    }
+    // the boundary bucket's selected keys take the positions after the keys above it
+    if (threadIdx.x < NH && T.mode[threadIdx.x] == 1u) T.aux[threadIdx.x] = T.above[threadIdx.x];
+    __syncthreads();
+    if (!any) return;
+    topk_finish<NH>(T, [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+            const int h = (s / 4) % NH;
+            if (((lmask >> s) & 1u) && md[h] == 1u)
+                fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { f(h, ok, idx); });
+        }
+    }, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -736,9 +895,9 @@ struct BinLists {
     int nchunks, cp, lo, hi;
 };
 
-template <class InFixed>
+template <class WordOf, class InFixed>
 __device__ __forceinline__ void head_sample_threshold(HeadSamp& S, SelShared<1>& F, const BinLists BL,
-                                                      const uint32_t* __restrict__ uw, uint32_t rank,
+                                                      WordOf&& word_of_token, uint32_t rank,
                                                       InFixed&& in_fixed) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
@@ -772,8 +931,7 @@ __device__ __forceinline__ void head_sample_threshold(HeadSamp& S, SelShared<1>&
             const int32_t* lst = BL.slist + static_cast<size_t>(c) * BL.cp;
             for (uint32_t p = a + lane; p < e; p += 64) {
                 const int i = lst[p];
-                const uint32_t u = uw[i];
-                if (!in_fixed(i)) f(sample_key(u, static_cast<uint32_t>(i)));
+                if (!in_fixed(i)) f(sample_key(word_of_token(i), static_cast<uint32_t>(i)));
             }
         }
     };

@@ -62,10 +62,6 @@ __device__ __forceinline__ size_t row_index(int page, int Hkv, int g, int slot, 
     return ((static_cast<size_t>(page) * Hkv + g) * kPage + slot) * static_cast<size_t>(width);
 }
 
-// Cached sample words of group bg (written by the predictor pass for the middle).
-__device__ __forceinline__ const uint32_t* group_words(const Plan& P, int bg) {
-    return P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
-}
 
 __host__ __device__ __forceinline__ size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
 
@@ -159,72 +155,39 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         qs[x] = P.q[(static_cast<size_t>(b) * P.Hq + g * G + h) * d + cc] * P.scale32;
     }
     __syncthreads();
-    uint32_t* uwg = P.uw + static_cast<size_t>(bg) * P.ncg * P.cg;
-    // a chunk spans at most kPredKeys tokens: kPhx quads per thread, kept in
-    // registers for the scatter below
-    constexpr int kPhx = kPredKeys / 4 / kPredThreads;
-    uint4 wq[kPhx];
-#pragma unroll
-    for (int e = 0; e < kPhx; ++e) {
+    // a chunk spans at most kPredKeys / G tokens: kPhx quads per thread, their
+    // words kept in registers for the scatter after the score stream.  With a
+    // low-rank or exact score stream the quads are computed inside it, one
+    // per iteration while the rows are in flight.
+    constexpr int kPhx = kPredKeys / G / 4 / kPredThreads;
+    static_assert(kPhx >= 1, "a quad per thread");
+    constexpr bool kKeep = kPhx <= 2;  // words held through the stream (else computed again)
+    uint4 wq[kKeep ? kPhx : 1];
+    auto sample_quad = [&](int e) __attribute__((always_inline)) {
         const int qd = (t0 >> 2) + tid + e * nthr;
         if (4 * qd < t1) {
-            wq[e] = philox4x32_10(static_cast<uint32_t>(qd), g, b, 0, P.seed_lo, P.seed_hi);
-            *reinterpret_cast<uint4*>(uwg + 4 * qd) = wq[e];  // chunks are disjoint at quad granularity
+            const uint4 w = quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi);
+            if constexpr (kKeep) wq[e] = w;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
                 const int i = 4 * qd + f;
-                if (i >= t0 && i < t1) atomicAdd(&shist[word_of(wq[e], f) >> (32 - kSampBits)], 1u);
+                if (i >= t0 && i < t1) atomicAdd(&shist[word_of(w, f) >> (32 - kSampBits)], 1u);
             }
         }
-    }
-    __syncthreads();
-    {
-        static_assert(kSampBins % kPredThreads == 0, "bins per thread");
-        constexpr int PER = kSampBins / kPredThreads;
-        uint32_t v[PER], sum = 0;
+    };
+    int phx = 0;  // quads done (wave-uniform)
+    if (kSig || R.k == 0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            v[e] = shist[PER * tid + e];
-            sum += v[e];
-        }
-        uint32_t total;
-        uint32_t run = block_excl_scan(sum, wsum, total);
-        uint32_t* so = P.soff + (static_cast<size_t>(bg) * P.ncp + c) * (kSampBins + 1);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            shist[PER * tid + e] = run;  // bin cursor for the scatter below
-            so[PER * tid + e] = run;
-            run += v[e];
-        }
-        if (tid == 0) so[kSampBins] = total;
-        __syncthreads();
-        // scatter into LDS (the score area is free until the stream), then one
-        // coalesced copy of the chunk's sorted list
-        int32_t* stage = reinterpret_cast<int32_t*>(keys);
-#pragma unroll
-        for (int e = 0; e < kPhx; ++e) {
-            const int qd = (t0 >> 2) + tid + e * nthr;
-            if (4 * qd < t1) {
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const int i = 4 * qd + f;
-                    if (i >= t0 && i < t1) stage[atomicAdd(&shist[word_of(wq[e], f) >> (32 - kSampBits)], 1u)] = i;
-                }
-            }
-        }
-        __syncthreads();
-        int32_t* sl = P.slist + (static_cast<size_t>(bg) * P.ncp + c) * P.cp;
-        for (int x = tid; x < t1 - t0; x += nthr) sl[x] = stage[x];
-        __syncthreads();  // the score stream reuses the staging area
+        for (int e = 0; e < kPhx; ++e) sample_quad(e);
+        phx = kPhx;
     }
 
     if (R.k > 0) {
-        // the heads' order-key brackets and candidate counters, reset before
-        // the barrier that ends step 1 (the stream's atomics follow it)
+        // the heads' order-key brackets, reset before the barrier that ends
+        // step 1 (the stream's atomics follow it)
         if (tid < G) {
             TS.lo[tid] = 0xFFFFFFFFu;
             TS.hi[tid] = 0;
-            TS.aux[tid] = 0;
         }
         // 1) low-rank queries q~ = pdot(q_s, P[:, j]) (the signature predictor
         //    signs these)
@@ -339,6 +302,10 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
                 load_raw_nt(gsrc + static_cast<uint64_t>(pg) * pstride + (tl % kPage) * ROW, kr[u]);
             }
 #pragma unroll
+            for (int e = 0; e < kPhx; ++e)
+                if (e == phx) sample_quad(e);
+            phx += phx < kPhx ? 1 : 0;
+#pragma unroll
             for (int u = 0; u < PU; ++u) {
                 const int tt = tb + sb + u * TPW + slot;
                 float kf[8];
@@ -373,8 +340,16 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         }
         }  // score stream
         __syncthreads();
+    }
+    // the quads a short stream left (their histogram counts are complete at
+    // the barrier that opens the top-k or the counting sort)
+#pragma unroll
+    for (int e = 0; e < kPhx; ++e)
+        if (e >= phx) sample_quad(e);
 
+    if (R.k > 0) {
         // 3) chunk top-kp per head, written as candidates (any order)
+        const int cbase = c * P.cp;
         const int kp = min(R.k, t1 - t0);
         const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
         if constexpr (kSig) {
@@ -504,25 +479,43 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         }
         const int ncp = P.ncp, kcap = P.kcap;
         uint64_t* __restrict__ cand = P.cand;
+        // each thread's keys sit at fixed slots: iteration it, head h, token
+        // e of the quad at offset o = o0 + 4 (tid + it nthr) take slot
+        // (it G + h) 4 + e (G cp <= kPredKeys: at most 8 / G iterations);
         // each visit reads 4 consecutive keys of every head with one 16-byte
         // LDS load per head (offsets from the 16-byte aligned chunk start)
+        constexpr int NIT = 8 / G;
+        static_assert(4 * kPredThreads * 8 >= kPredKeys, "a chunk's keys fit 32 slots per thread");
         const int o0 = (t0 - cbase) & ~3, o1 = t1 - cbase;
-        block_topk<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
-            for (int o = o0 + 4 * tid; o < o1; o += 4 * nthr) {
+        block_topk_slots<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int o = o0 + 4 * (tid + it * nthr);
+                if (o >= o1) continue;
                 uint4 kk[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) kk[h] = *reinterpret_cast<const uint4*>(keys + h * ks + o);
+                if (cbase + o >= t0 && o + 4 <= o1) {  // all four tokens in the chunk: no checks
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = cbase + o + e;
-                    if (t >= t0 && t < t1) {
+                    for (int h = 0; h < G; ++h)
 #pragma unroll
-                        for (int h = 0; h < G; ++h) f(h, word_of(kk[h], e), static_cast<uint32_t>(t));
-                    }
+                        for (int e = 0; e < 4; ++e)
+                            f((it * G + h) * 4 + e, word_of(kk[h], e), static_cast<uint32_t>(cbase + o + e));
+                } else {
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = cbase + o + e;
+                            if (t >= t0 && t < t1) f((it * G + h) * 4 + e, word_of(kk[h], e), static_cast<uint32_t>(t));
+                        }
                 }
             }
-        }, [&](int h, uint64_t key) __attribute__((always_inline)) {
-            const uint32_t pos = atomicAdd(&TS.aux[h], 1u);
+        }, [&](int s, auto&& g) __attribute__((always_inline)) {
+            const int it = s / (4 * G), h = (s / 4) % G, e = s % 4;
+            const int o = o0 + 4 * (tid + it * nthr) + e;
+            g(keys[h * ks + o], static_cast<uint32_t>(cbase + o));
+        }, [&](int h, uint32_t pos, uint64_t key) __attribute__((always_inline)) {
             if (pos < static_cast<uint32_t>(kp)) cand[((bh0 + h) * ncp + c) * kcap + pos] = key;
         });
         // order-key bracket of the candidates for the merge: [threshold key, chunk max]
@@ -532,6 +525,49 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             cr[1] = hi[tid];
         }
         }  // chunk top-k
+    }
+    // 4) the counting sort of the chunk's middle tokens by bin: offsets of
+    //    every bin (soff), the tokens staged in their bins' ranges in LDS
+    //    (the score area is free after the top-k), then one coalesced copy
+    __syncthreads();
+    {
+        static_assert(kSampBins % kPredThreads == 0, "bins per thread");
+        constexpr int PER = kSampBins / kPredThreads;
+        uint32_t v[PER], sum = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            v[e] = shist[PER * tid + e];
+            sum += v[e];
+        }
+        uint32_t total;
+        uint32_t run = block_excl_scan(sum, wsum, total);
+        uint32_t* so = P.soff + (static_cast<size_t>(bg) * P.ncp + c) * (kSampBins + 1);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            shist[PER * tid + e] = run;  // bin cursor for the scatter below
+            so[PER * tid + e] = run;
+            run += v[e];
+        }
+        if (tid == 0) so[kSampBins] = total;
+        __syncthreads();
+        int32_t* stage = reinterpret_cast<int32_t*>(keys);
+#pragma unroll
+        for (int e = 0; e < kPhx; ++e) {
+            const int qd = (t0 >> 2) + tid + e * nthr;
+            if (4 * qd < t1) {
+                uint4 w;
+                if constexpr (kKeep) w = wq[e];
+                else w = quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi);
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const int i = 4 * qd + f;
+                    if (i >= t0 && i < t1) stage[atomicAdd(&shist[word_of(w, f) >> (32 - kSampBits)], 1u)] = i;
+                }
+            }
+        }
+        __syncthreads();
+        int32_t* sl = P.slist + (static_cast<size_t>(bg) * P.ncp + c) * P.cp;
+        for (int x = tid; x < t1 - t0; x += nthr) sl[x] = stage[x];
     }
 }
 
@@ -580,7 +616,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_premerge(Plan P) {
         hi = max(hi, cr[1]);
     }
     const uint32_t keep = min(static_cast<uint32_t>(R.k), tot);
-    if (tid == 0) TS.aux[0] = 0;
     const uint64_t* __restrict__ cand = P.cand + (static_cast<size_t>(bh) * ncp + c0) * kcap;
     uint64_t* __restrict__ out = P.cand2 + (static_cast<size_t>(bh) * np + s) * P.kcap2;  // keep <= kcap2
     const int slots = (c1 - c0) * kcap;
@@ -601,8 +636,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_premerge(Plan P) {
             for (int t = 0; t < kBatch; ++t)
                 if (ok[t]) f(0, static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
         }
-    }, [&](int, uint64_t key) __attribute__((always_inline)) {
-        const uint32_t pos = atomicAdd(&TS.aux[0], 1u);
+    }, [&](int, uint32_t pos, uint64_t key) __attribute__((always_inline)) {
         if (pos < keep) out[pos] = key;
     });
     if (tid == 0) {
@@ -619,6 +653,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_premerge(Plan P) {
 
 constexpr int kSelLdsWords = 4096;  // fixed-set bitmaps of up to 131072 tokens are built in LDS
 constexpr int kSelRegKeys = 8;      // candidate keys per thread held in registers (when they all fit)
+constexpr int kSelTopList = 2048;   // top-k tokens listed in LDS before their sample words are computed
 
 // PM: the candidates come pre-merged in P.nparts parts.  LB: the head's
 // fixed-set bitmap is built in LDS (max_seq_len <= 32 * kSelLdsWords) and
@@ -628,12 +663,13 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     __shared__ TopkShared<1> TS;
     __shared__ HeadSamp SS;
     __shared__ uint32_t lbits[LB ? kSelLdsWords : 1];
+    __shared__ int32_t ltop[kSelTopList];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int bh = blockIdx.x, b = bh / P.Hq, h = bh % P.Hq, g = h / P.G;
     const int bg = b * P.Hkv + g;
     const int L = P.seq_lens[b];
     const Regions R = regions(P, L);
-    const uint32_t* uwg = group_words(P, bg);
+    const uint32_t slo = P.seed_lo, shi = P.seed_hi;
     // lambdas below capture these locals, never the kernel argument itself
     const int cp = P.cp, ncp = P.ncp, kcap = P.kcap;
     // candidate parts: the predictor chunks, or (few heads, many chunks) the
@@ -736,6 +772,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     //    out of the tail histogram (block_topk starts with a barrier)
     if (R.k > 0) {
         const uint32_t want[1] = {static_cast<uint32_t>(R.k)}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
+        const bool listed = R.k <= kSelTopList;  // block-uniform; positions are < R.k
         constexpr int kBatch = 8;  // candidate keys loaded before any is visited
         block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
             if (inreg) {
@@ -758,11 +795,19 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
                 for (int t = 0; t < kBatch; ++t)
                     if (ok[t]) f(0, static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
             }
-        }, [&](int, uint64_t key) __attribute__((always_inline)) {
+        }, [&](int, uint32_t pos, uint64_t key) __attribute__((always_inline)) {
             const uint32_t i = ~static_cast<uint32_t>(key);
             atomicOr(&bits[i >> 5], 1u << (i & 31));
-            atomicSub(&SS.hist[uwg[i] >> (32 - kSampBits)], 1u);
+            if (listed) ltop[pos] = static_cast<int32_t>(i);  // its sample word below, all lanes busy
+            else atomicSub(&SS.hist[token_word(i, g, b, slo, shi) >> (32 - kSampBits)], 1u);
         });
+        if (listed) {  // block_topk ends with a barrier
+            for (int x = tid; x < R.k; x += nthr) {
+                const uint32_t i = static_cast<uint32_t>(ltop[x]);
+                atomicSub(&SS.hist[token_word(i, g, b, slo, shi) >> (32 - kSampBits)], 1u);
+            }
+            __syncthreads();
+        }
     } else {
         __syncthreads();
     }
@@ -771,7 +816,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     // 3) base sample: first nb tail tokens in (word, index) order
     const uint32_t rank = (R.nb > 0 && R.nb < R.NT) ? static_cast<uint32_t>(R.nb) : 0u;
     const BinLists BL{soffg, P.slist + static_cast<size_t>(bg) * ncp * cp, ncp, cp, R.lo, R.hi};
-    head_sample_threshold(SS, TS.S, BL, uwg, rank, [&](int i) __attribute__((always_inline)) {
+    head_sample_threshold(SS, TS.S, BL, [&](int i) __attribute__((always_inline)) {
+        return token_word(static_cast<uint32_t>(i), g, b, slo, shi);
+    }, rank, [&](int i) __attribute__((always_inline)) {
         if constexpr (LB) return bit_of(lbits, i);   // complete after block_topk's closing barrier
         else return bit_of_coherent(gbits, i);
     });
@@ -827,7 +874,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
     const uint32_t row0 = live4 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     const bool anyM = live4 && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
-    const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+    const uint4 w = anyM ? quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi) : make_uint4(0, 0, 0, 0);
     uint32_t fw[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
@@ -963,7 +1010,11 @@ __device__ __forceinline__ void final_sample_threshold(const Plan& P, HeadSamp& 
     const uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
     const BinLists BL{P.soff + static_cast<size_t>(bg) * P.ncp * (kSampBins + 1),
                       P.slist + static_cast<size_t>(bg) * P.ncp * P.cp, P.ncp, P.cp, R.lo, R.hi};
-    head_sample_threshold(SS, FS, BL, group_words(P, bg), rank, [&](int i) __attribute__((always_inline)) {
+    const uint32_t b = static_cast<uint32_t>(bg / P.Hkv), g = static_cast<uint32_t>(bg % P.Hkv);
+    const uint32_t slo = P.seed_lo, shi = P.seed_hi;
+    head_sample_threshold(SS, FS, BL, [&](int i) __attribute__((always_inline)) {
+        return token_word(static_cast<uint32_t>(i), g, b, slo, shi);
+    }, rank, [&](int i) __attribute__((always_inline)) {
         return bit_of(bits, i);
     });
     if (threadIdx.x == 0) {
@@ -1446,7 +1497,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
     const uint32_t row0 = live4 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     const bool anyM = live4 && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
-    const uint4 w = anyM ? *reinterpret_cast<const uint4*>(group_words(P, bg) + 4 * qd) : make_uint4(0, 0, 0, 0);
+    const uint4 w = anyM ? quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi) : make_uint4(0, 0, 0, 0);
     uint32_t fw[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
@@ -1833,7 +1884,6 @@ __global__ __launch_bounds__(kThreads) void k_emit(Plan P) {
     const Regions R = regions(P, L);
     const HeadState hs = P.hs[bh];
     const uint32_t* bits = P.bits + static_cast<size_t>(bh) * P.words;
-    const uint32_t* uwg = group_words(P, b * P.Hkv + g);
     int32_t* out = P.idx + static_cast<size_t>(bh) * P.idx_cap;
     const int cap = P.idx_cap;
     int written = 0;
@@ -1846,7 +1896,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(Plan P) {
             const int qd = q0 + 64 * k;
             const bool live = 4 * qd < L;
             const bool anyM = live && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
-            w[k] = anyM ? *reinterpret_cast<const uint4*>(uwg + 4 * qd) : make_uint4(0, 0, 0, 0);
+            w[k] = anyM ? quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi) : make_uint4(0, 0, 0, 0);
             fw[k] = live ? bits[qd >> 3] : 0u;
         }
         uint32_t m[KQ], ex[KQ], run = 0;

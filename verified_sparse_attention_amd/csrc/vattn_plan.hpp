@@ -75,7 +75,6 @@ struct Plan {
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* brow;  // [B*Hkv][ncg][cg] V row of each base-pass member (output-level mode, else null)
     double* npart;   // [B*Hq][ncg][3][d] numerator partials T1, T2, NF per chunk (output-level mode)
-    uint32_t* uw;    // [B*Hkv][ncg * cg] Philox sample word of each middle token
     uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
     uint32_t* gw;      // [B*Hkv] gather dispatch weight: max over the group's heads of (n_fixed + n) / L, fp32 bits
     // pre-merged candidate parts (nparts > 0 only: few heads, many chunks)
