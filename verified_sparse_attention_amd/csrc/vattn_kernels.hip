@@ -43,7 +43,7 @@
 namespace vattn {
 
 constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
-constexpr int kBaseUnroll = 4;  // K rows in flight per lane group in the base pass
+constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass
 constexpr int kKeyPad = 16;     // words between the predictor's per-head key rows
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
@@ -773,6 +773,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
     if (R.k > 0) {
         const uint32_t want[1] = {static_cast<uint32_t>(R.k)}, total[1] = {tot}, lo1[1] = {lo}, hi1[1] = {hi};
         const bool listed = R.k <= kSelTopList;  // block-uniform; positions are < R.k
+        auto emit = [&](int, uint32_t pos, uint64_t key) __attribute__((always_inline)) {
+            const uint32_t i = ~static_cast<uint32_t>(key);
+            atomicOr(&bits[i >> 5], 1u << (i & 31));
+            if (listed) ltop[pos] = static_cast<int32_t>(i);  // its sample word below, all lanes busy
+            else atomicSub(&SS.hist[token_word(i, g, b, slo, shi) >> (32 - kSampBits)], 1u);
+        };
         constexpr int kBatch = 8;  // candidate keys loaded before any is visited
         block_topk<1>(TS, want, total, lo1, hi1, [&](auto&& f) __attribute__((always_inline)) {
             if (inreg) {
@@ -795,12 +801,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
                 for (int t = 0; t < kBatch; ++t)
                     if (ok[t]) f(0, static_cast<uint32_t>(kk[t] >> 32), ~static_cast<uint32_t>(kk[t]));
             }
-        }, [&](int, uint32_t pos, uint64_t key) __attribute__((always_inline)) {
-            const uint32_t i = ~static_cast<uint32_t>(key);
-            atomicOr(&bits[i >> 5], 1u << (i & 31));
-            if (listed) ltop[pos] = static_cast<int32_t>(i);  // its sample word below, all lanes busy
-            else atomicSub(&SS.hist[token_word(i, g, b, slo, shi) >> (32 - kSampBits)], 1u);
-        });
+        }, emit);
         if (listed) {  // block_topk ends with a barrier
             for (int x = tid; x < R.k; x += nthr) {
                 const uint32_t i = static_cast<uint32_t>(ltop[x]);
@@ -1046,7 +1047,7 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
     __shared__ HeadSamp SS;
     __shared__ SelShared<1> FS;
     __shared__ int coff[kMaxChunks + 1];  // member offsets of the group's base chunks
-    __shared__ uint64_t red[NW][4];
+    __shared__ uint64_t red[NW][5];
     __shared__ int s_nsel;
     __shared__ float s_m;
     const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
@@ -1063,8 +1064,18 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         return;
     }
     const int nc = (L + P.cg - 1) / P.cg;
-    if constexpr (!DEFER)
-        for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
+    if constexpr (!DEFER) {  // every load of the histogram requested before any is stored
+        constexpr int PER = (kSampBins + kThreads - 1) / kThreads;
+        uint32_t hv[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int x = tid + e * nthr;
+            hv[e] = x < kSampBins ? P.hh[static_cast<size_t>(bh) * kSampBins + x] : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (tid + e * nthr < kSampBins) SS.hist[tid + e * nthr] = hv[e];
+    }
     if (wave == 0) {  // m: max pinned score over I_f and the base sample
         float m = -__builtin_inff();
         for (int c = lane; c < nc; c += 64) m = fmaxf(m, P.cmax[static_cast<size_t>(bh) * P.ncg + c]);
@@ -1093,7 +1104,10 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         const int G = P.G;
         const uint32_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
         const float* bsc = P.bsc + static_cast<size_t>(bg) * P.ncg * P.cg * G + hg;
-        uint64_t sf = 0, s1 = 0, s2lo = 0, s2hi = 0;
+        // S2 = sum E^2 < 2^80 per entry, from E = a 2^20 + b: sums of a^2,
+        // a b and b^2 (each below 2^40 per entry, so below 2^60 over any
+        // sequence) are exact in 64 bits and give S2 = A2 2^40 + AB 2^21 + B2
+        uint64_t sf = 0, s1 = 0, a2 = 0, ab = 0, b2 = 0;
         for (int cw = wave; cw < nc; cw += 2 * NW) {
             const int ca = cw, cb = cw + NW;
             const int na = coff[ca + 1] - coff[ca], nb2 = cb < nc ? coff[cb + 1] - coff[cb] : 0;
@@ -1121,44 +1135,45 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
                         const uint64_t Es = fx ? 0ull : E;
                         sf += fx ? E : 0ull;
                         s1 += Es;
-                        const unsigned __int128 e2 = static_cast<unsigned __int128>(Es) * Es;
-                        const uint64_t lo = static_cast<uint64_t>(e2);
-                        s2hi += static_cast<uint64_t>(e2 >> 64) + ((s2lo + lo < s2lo) ? 1u : 0u);
-                        s2lo += lo;
+                        const uint32_t ea = static_cast<uint32_t>(Es >> 20), eb = static_cast<uint32_t>(Es) & 0xFFFFFu;
+                        a2 += static_cast<uint64_t>(ea) * ea;
+                        ab += static_cast<uint64_t>(ea) * eb;
+                        b2 += static_cast<uint64_t>(eb) * eb;
                     }
             }
         }
         for (int o = 32; o >= 1; o >>= 1) {
             sf += shfl_xor_u64(sf, o);
             s1 += shfl_xor_u64(s1, o);
-            const uint64_t olo = shfl_xor_u64(s2lo, o), ohi = shfl_xor_u64(s2hi, o);
-            const uint64_t nlo = s2lo + olo;
-            s2hi = s2hi + ohi + (nlo < s2lo ? 1u : 0u);
-            s2lo = nlo;
+            a2 += shfl_xor_u64(a2, o);
+            ab += shfl_xor_u64(ab, o);
+            b2 += shfl_xor_u64(b2, o);
         }
         if (lane == 0) {
             red[wave][0] = sf;
             red[wave][1] = s1;
-            red[wave][2] = s2hi;
-            red[wave][3] = s2lo;
+            red[wave][2] = a2;
+            red[wave][3] = ab;
+            red[wave][4] = b2;
         }
     }
     __syncthreads();
     if (tid == 0) {
         const float m = s_m;
-        uint64_t SF = 0, S1 = 0, S2lo = 0, S2hi = 0;
+        uint64_t SF = 0, S1 = 0, A2 = 0, AB = 0, B2 = 0;
         for (int w = 0; w < NW; ++w) {
             SF += red[w][0];
             S1 += red[w][1];
-            const uint64_t nlo = S2lo + red[w][3];
-            S2hi += red[w][2] + (nlo < S2lo ? 1u : 0u);
-            S2lo = nlo;
+            A2 += red[w][2];
+            AB += red[w][3];
+            B2 += red[w][4];
         }
+        const unsigned __int128 S2 = (static_cast<unsigned __int128>(A2) << 40) +
+                                     (static_cast<unsigned __int128>(AB) << 21) + B2;
         hsp->SF = SF;
         hsp->S1 = S1;
-        hsp->S2hi = S2hi;
-        hsp->S2lo = S2lo;
-        const unsigned __int128 S2 = (static_cast<unsigned __int128>(S2hi) << 64) | S2lo;
+        hsp->S2hi = static_cast<uint64_t>(S2 >> 64);
+        hsp->S2lo = static_cast<uint64_t>(S2);
         const int NT = R.NT, nb = R.nb;
         int n, flags = 0;
         if (P.force_budget >= 0) {
