@@ -750,22 +750,31 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(Plan P) {
             SS.hist[x] = sum;
         }
     }
-    for (int x = tid; !PM && x < kSampBins; x += nthr) {
-        uint32_t sum = 0;
-        for (int c0 = 0; c0 < ncp; c0 += kCB) {
-            uint32_t a[kCB], e[kCB];
+    if constexpr (!PM) {  // two bins of this thread and kCB chunks requested at once
+        constexpr int PER = 2;
+        for (int x0 = tid; x0 < kSampBins; x0 += PER * nthr) {
+            uint32_t sum[PER] = {};
+            for (int c0 = 0; c0 < ncp; c0 += kCB) {
+                uint32_t a[PER][kCB], e[PER][kCB];
 #pragma unroll
-            for (int t = 0; t < kCB; ++t) {
-                const int c = c0 + t;
-                const bool live = c < ncp && max(c * cp, R.lo) < min((c + 1) * cp, R.hi);
-                const uint32_t* off = soffg + static_cast<size_t>(live ? c : 0) * (kSampBins + 1) + x;
-                a[t] = live ? off[0] : 0u;
-                e[t] = live ? off[1] : 0u;
+                for (int u = 0; u < PER; ++u)
+#pragma unroll
+                    for (int t = 0; t < kCB; ++t) {
+                        const int x = x0 + u * nthr, c = c0 + t;
+                        const bool live = x < kSampBins && c < ncp && max(c * cp, R.lo) < min((c + 1) * cp, R.hi);
+                        const uint32_t* off = soffg + static_cast<size_t>(live ? c : 0) * (kSampBins + 1) + (live ? x : 0);
+                        a[u][t] = live ? off[0] : 0u;
+                        e[u][t] = live ? off[1] : 0u;
+                    }
+#pragma unroll
+                for (int u = 0; u < PER; ++u)
+#pragma unroll
+                    for (int t = 0; t < kCB; ++t) sum[u] += e[u][t] - a[u][t];
             }
 #pragma unroll
-            for (int t = 0; t < kCB; ++t) sum += e[t] - a[t];
+            for (int u = 0; u < PER; ++u)
+                if (x0 + u * nthr < kSampBins) SS.hist[x0 + u * nthr] = sum[u];
         }
-        SS.hist[x] = sum;
     }
 
     // 2) exact top-k from the chunk candidates: set the bit and take the token
@@ -850,6 +859,7 @@ template <int D, typename KVT, int G>
 __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     __shared__ uint32_t tmeta[kGatherChunk];
     __shared__ uint32_t trow[kGatherChunk];
+    __shared__ float tsc[G][kGatherChunk];  // the scores, stored to bsc one head row at a time
     __shared__ uint32_t wsum[kChunkThreads / 64];
     __shared__ float wmax[kChunkThreads / 64][G];
     __shared__ HeadView hv[G];
@@ -973,7 +983,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
 #pragma unroll
                 for (int e = 0; e < NH; ++e) {
                     if ((mk[u] >> hsel[e]) & 1u) lmax[e] = fmaxf(lmax[e], sv[e]);
-                    lsc[static_cast<size_t>(xl[u]) * G + hsel[e]] = sv[e];
+                    tsc[hsel[e]][xl[u]] = sv[e];
                 }
             }
         }
@@ -987,6 +997,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
         for (int e = 0; e < NH; ++e) wmax[wave][hsel[e]] = lmax[e];
     }
     __syncthreads();
+    for (int h = 0; h < G; ++h)
+        for (int x = tid; x < n; x += nthr) lsc[static_cast<size_t>(h) * P.cg + x] = tsc[h][x];
     if (tid < G) {
         float v = -__builtin_inff();
         for (int w = 0; w < nwaves; ++w) v = fmaxf(v, wmax[w][tid]);
@@ -1007,7 +1019,8 @@ constexpr int kStatsBatch = 4;  // entries of each of a wave's two chunks reques
 // the whole tail, or the base sample's when n == n_b).  S.hist holds the
 // head's tail histogram.  All threads call.
 __device__ __forceinline__ void final_sample_threshold(const Plan& P, HeadSamp& SS, SelShared<1>& FS, HeadState* hsp,
-                                                       int bh, int bg, const Regions& R, uint32_t rank) {
+                                                       int bh, int bg, const Regions& R, uint32_t rank, int n,
+                                                       uint64_t thr_b) {
     const uint32_t* __restrict__ bits = P.bits + static_cast<size_t>(bh) * P.words;
     const BinLists BL{P.soff + static_cast<size_t>(bg) * P.ncp * (kSampBins + 1),
                       P.slist + static_cast<size_t>(bg) * P.ncp * P.cp, P.ncp, P.cp, R.lo, R.hi};
@@ -1018,11 +1031,10 @@ __device__ __forceinline__ void final_sample_threshold(const Plan& P, HeadSamp& 
     }, rank, [&](int i) __attribute__((always_inline)) {
         return bit_of(bits, i);
     });
-    if (threadIdx.x == 0) {
-        const int n = hsp->n;
+    if (threadIdx.x == 0) {  // n and the base threshold are thread 0's
         uint64_t thr = 0;  // n == N_t: the whole tail (n == 0: unused)
         if (rank > 0) thr = SS.thr;
-        else if (n > 0 && n == R.nb) thr = hsp->thr_b;
+        else if (n > 0 && n == R.nb) thr = thr_b;
         hsp->thr_n = thr;
     }
 }
@@ -1031,8 +1043,8 @@ __device__ __forceinline__ void final_sample_threshold(const Plan& P, HeadSamp& 
 // gather dispatch weight (expected member density; non-negative fp32 values
 // order as their bit patterns) and the rank of a new threshold, 0 unless the
 // sample is neither empty, the whole tail nor the base sample.  Thread 0.
-__device__ __forceinline__ int settle_budget(const Plan& P, HeadState* hsp, int bg, const Regions& R, int L) {
-    const int n = hsp->n, NT = R.NT, nb = R.nb;
+__device__ __forceinline__ int settle_budget(const Plan& P, HeadState* hsp, int bg, const Regions& R, int L, int n) {
+    const int NT = R.NT, nb = R.nb;
     atomicMax(&P.gw[bg], __float_as_uint(static_cast<float>(R.sp + R.wp + R.k + n) / static_cast<float>(L)));
     hsp->wsamp = n > 0 ? static_cast<float>(static_cast<double>(NT) / static_cast<double>(n)) : 0.0f;
     return (n > 0 && n < NT && n != nb) ? n : 0;
@@ -1043,10 +1055,8 @@ __device__ __forceinline__ int settle_budget(const Plan& P, HeadState* hsp, int 
 template <int kThreads, bool DEFER>  // per block
 __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
     constexpr int NW = kThreads / 64;
-    static_assert(NW >= 2, "one wave for m, one for the chunk offsets");
     __shared__ HeadSamp SS;
     __shared__ SelShared<1> FS;
-    __shared__ int coff[kMaxChunks + 1];  // member offsets of the group's base chunks
     __shared__ uint64_t red[NW][5];
     __shared__ int s_nsel;
     __shared__ float s_m;
@@ -1063,6 +1073,8 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         }
         return;
     }
+    const uint64_t thr_b = tid == 0 ? hsp->thr_b : 0;  // the base threshold (the select's), for thread 0
+    int nfin = 0;                                       // the final budget, thread 0's
     const int nc = (L + P.cg - 1) / P.cg;
     if constexpr (!DEFER) {  // every load of the histogram requested before any is stored
         constexpr int PER = (kSampBins + kThreads - 1) / kThreads;
@@ -1076,22 +1088,36 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         for (int e = 0; e < PER; ++e)
             if (tid + e * nthr < kSampBins) SS.hist[tid + e * nthr] = hv[e];
     }
+    // each wave's first two chunks: member counts, masks and scores requested
+    // now, with the histogram and the chunk maxima (they need no m)
+    const int G = P.G;
+    const uint32_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
+    const float* bsc = P.bsc + static_cast<size_t>(bg) * P.ncg * P.cg * G + static_cast<size_t>(hg) * P.cg;
+    const int32_t* bcnt = P.bcnt + static_cast<size_t>(bg) * P.ncg;
+    auto request = [&](int ca, int y0, int na, int nb2, uint32_t (&tm)[2][kStatsBatch],
+                       float (&sv)[2][kStatsBatch]) __attribute__((always_inline)) {
+        const int cb = ca + NW;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int cc = q ? cb : ca, ncc = q ? nb2 : na;
+#pragma unroll
+            for (int v = 0; v < kStatsBatch; ++v) {
+                const int y = y0 + lane + 64 * v;
+                const size_t at = static_cast<size_t>(cc) * P.cg + y;
+                tm[q][v] = y < ncc ? bmeta[at] : 0u;
+                sv[q][v] = y < ncc ? bsc[static_cast<size_t>(cc) * P.cg * G + y] : 0.0f;  // head hg's row of the chunk
+            }
+        }
+    };
+    const int na0 = wave < nc ? bcnt[wave] : 0, nb0 = wave + NW < nc ? bcnt[wave + NW] : 0;
+    uint32_t tm0[2][kStatsBatch];
+    float sv0[2][kStatsBatch];
+    request(wave, 0, na0, nb0, tm0, sv0);
     if (wave == 0) {  // m: max pinned score over I_f and the base sample
         float m = -__builtin_inff();
         for (int c = lane; c < nc; c += 64) m = fmaxf(m, P.cmax[static_cast<size_t>(bh) * P.ncg + c]);
         for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
         if (lane == 0) s_m = m;
-    } else if (wave == 1) {  // member counts of the chunks -> offsets
-        const int32_t* cnt = P.bcnt + static_cast<size_t>(bg) * P.ncg;
-        uint32_t carry = 0;
-        for (int c0 = 0; c0 < nc; c0 += 64) {
-            const int c = c0 + lane;
-            const uint32_t v = c < nc ? static_cast<uint32_t>(cnt[c]) : 0u;
-            const uint32_t inc = wave_incl_scan(v);
-            if (c < nc) coff[c] = static_cast<int>(carry + inc - v);
-            carry += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
-        }
-        if (lane == 0) coff[nc] = static_cast<int>(carry);
     }
     __syncthreads();
 
@@ -1101,45 +1127,36 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
     // is used.
     {
         const float m = s_m;
-        const int G = P.G;
-        const uint32_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
-        const float* bsc = P.bsc + static_cast<size_t>(bg) * P.ncg * P.cg * G + hg;
         // S2 = sum E^2 < 2^80 per entry, from E = a 2^20 + b: sums of a^2,
         // a b and b^2 (each below 2^40 per entry, so below 2^60 over any
         // sequence) are exact in 64 bits and give S2 = A2 2^40 + AB 2^21 + B2
         uint64_t sf = 0, s1 = 0, a2 = 0, ab = 0, b2 = 0;
+        auto add = [&](const uint32_t (&tm)[2][kStatsBatch], const float (&sv)[2][kStatsBatch]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < kStatsBatch; ++v) {
+                    const bool mem = (tm[q][v] >> hg) & 1u, fx = (tm[q][v] >> (8 + hg)) & 1u;
+                    const uint64_t E = mem ? fixed_weight(sv[q][v] - m) : 0ull;
+                    const uint64_t Es = fx ? 0ull : E;
+                    sf += fx ? E : 0ull;
+                    s1 += Es;
+                    const uint32_t ea = static_cast<uint32_t>(Es >> 20), eb = static_cast<uint32_t>(Es) & 0xFFFFFu;
+                    a2 += static_cast<uint64_t>(ea) * ea;
+                    ab += static_cast<uint64_t>(ea) * eb;
+                    b2 += static_cast<uint64_t>(eb) * eb;
+                }
+        };
+        add(tm0, sv0);
         for (int cw = wave; cw < nc; cw += 2 * NW) {
-            const int ca = cw, cb = cw + NW;
-            const int na = coff[ca + 1] - coff[ca], nb2 = cb < nc ? coff[cb + 1] - coff[cb] : 0;
+            const int na = cw == wave ? na0 : bcnt[cw];
+            const int nb2 = cw == wave ? nb0 : (cw + NW < nc ? bcnt[cw + NW] : 0);
             const int nmax = max(na, nb2);
-            for (int y0 = 0; y0 < nmax; y0 += 64 * kStatsBatch) {
+            for (int y0 = cw == wave ? 64 * kStatsBatch : 0; y0 < nmax; y0 += 64 * kStatsBatch) {
                 uint32_t tm[2][kStatsBatch];
                 float sv[2][kStatsBatch];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int cc = q ? cb : ca, ncc = q ? nb2 : na;
-#pragma unroll
-                    for (int v = 0; v < kStatsBatch; ++v) {
-                        const int y = y0 + lane + 64 * v;
-                        const size_t at = static_cast<size_t>(cc) * P.cg + y;
-                        tm[q][v] = y < ncc ? bmeta[at] : 0u;
-                        sv[q][v] = y < ncc ? bsc[at * G] : 0.0f;
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int v = 0; v < kStatsBatch; ++v) {
-                        const bool mem = (tm[q][v] >> hg) & 1u, fx = (tm[q][v] >> (8 + hg)) & 1u;
-                        const uint64_t E = mem ? fixed_weight(sv[q][v] - m) : 0ull;
-                        const uint64_t Es = fx ? 0ull : E;
-                        sf += fx ? E : 0ull;
-                        s1 += Es;
-                        const uint32_t ea = static_cast<uint32_t>(Es >> 20), eb = static_cast<uint32_t>(Es) & 0xFFFFFu;
-                        a2 += static_cast<uint64_t>(ea) * ea;
-                        ab += static_cast<uint64_t>(ea) * eb;
-                        b2 += static_cast<uint64_t>(eb) * eb;
-                    }
+                request(cw, y0, na, nb2, tm, sv);
+                add(tm, sv);
             }
         }
         for (int o = 32; o >= 1; o >>= 1) {
@@ -1158,16 +1175,19 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         }
     }
     __syncthreads();
+    // lanes 0..4 of wave 0 sum one statistic each over the waves; thread 0
+    // then holds all five (wave-uniform values)
+    uint64_t col = 0;
+    if (wave == 0 && lane < 5)
+        for (int w = 0; w < NW; ++w) col += red[w][lane];
+    auto lane_u64 = [&](int l) __attribute__((always_inline)) {
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(col), l));
+        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(col >> 32), l));
+        return (static_cast<uint64_t>(hi) << 32) | lo;
+    };
+    const uint64_t SF = lane_u64(0), S1 = lane_u64(1), A2 = lane_u64(2), AB = lane_u64(3), B2 = lane_u64(4);
     if (tid == 0) {
         const float m = s_m;
-        uint64_t SF = 0, S1 = 0, A2 = 0, AB = 0, B2 = 0;
-        for (int w = 0; w < NW; ++w) {
-            SF += red[w][0];
-            S1 += red[w][1];
-            A2 += red[w][2];
-            AB += red[w][3];
-            B2 += red[w][4];
-        }
         const unsigned __int128 S2 = (static_cast<unsigned __int128>(A2) << 40) +
                                      (static_cast<unsigned __int128>(AB) << 21) + B2;
         hsp->SF = SF;
@@ -1209,11 +1229,12 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
         hsp->n = n;
         hsp->flags = flags;
         hsp->m = m;
-        if constexpr (!DEFER) s_nsel = settle_budget(P, hsp, bg, R, L);
+        if constexpr (!DEFER) s_nsel = settle_budget(P, hsp, bg, R, L, n);
+        nfin = n;
     }
     if constexpr (DEFER) return;
     __syncthreads();
-    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel));
+    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel), nfin, thr_b);
 }
 
 // ===========================================================================
@@ -1291,7 +1312,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
             const int x = tid + u * kChunkThreads, mi = x / G, h = x - mi * G;
             if (mi < tn) {
                 mr[u] = P.bmeta[lb + t0 + mi];
-                sr[u] = P.bsc[(lb + t0 + mi) * G + h];
+                sr[u] = P.bsc[lb * G + static_cast<size_t>(h) * P.cg + t0 + mi];
             }
         }
     };
@@ -1389,6 +1410,8 @@ __global__ __launch_bounds__(kThreads) void k_budget_num(Plan P) {
     }
     const Regions R = regions(P, L);
     const int NT = R.NT, nb = R.nb;
+    const uint64_t thr_b = tid == 0 ? hsp->thr_b : 0;  // thread 0's: the base threshold and
+    int nfin = tid == 0 ? hsp->n : 0;                   // the denominator's budget
     for (int x = tid; x < kSampBins; x += nthr) SS.hist[x] = P.hh[static_cast<size_t>(bh) * kSampBins + x];
     if (nb > 0) {  // the chunk partials, summed in chunk order
         const int nc = (L + P.cg - 1) / P.cg;
@@ -1427,15 +1450,16 @@ __global__ __launch_bounds__(kThreads) void k_budget_num(Plan P) {
                 const double r = num / den;
                 nN = r >= static_cast<double>(NT) ? NT : static_cast<int>(__builtin_ceil(r));
             }
-            if (nN > hsp->n) {
+            if (nN > nfin) {
+                nfin = nN;
                 hsp->n = nN;
                 hsp->flags = hsp->flags | 8 | (nN == NT ? 1 : 0);
             }
         }
-        s_nsel = settle_budget(P, hsp, bg, R, L);
+        s_nsel = settle_budget(P, hsp, bg, R, L, nfin);
     }
     __syncthreads();
-    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel));
+    final_sample_threshold(P, SS, FS, hsp, bh, bg, R, static_cast<uint32_t>(s_nsel), nfin, thr_b);
 }
 
 // ===========================================================================
@@ -1592,9 +1616,9 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         for (int e = 0; e < PER; ++e) {
             const int x = nu + tid + e * nthr;
             mm[e] = x < n ? tmeta[x] : 0u;
-            const size_t at = static_cast<size_t>(x < n ? x - nu : 0) * G;
+            const size_t at = static_cast<size_t>(x < n ? x - nu : 0);
 #pragma unroll
-            for (int h = 0; h < G; ++h) v[e][h] = x < n ? bsc[at + h] : 0.0f;
+            for (int h = 0; h < G; ++h) v[e][h] = x < n ? bsc[static_cast<size_t>(h) * P.cg + at] : 0.0f;
         }
         bool over = false;
 #pragma unroll

@@ -69,8 +69,8 @@ struct Plan {
     uint32_t* soff;  // [B*Hkv][ncp][kSampBins + 1] bin offsets of each chunk's middle tokens
     int32_t* slist;  // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
-    float* bsc;      // [B*Hkv][ncg][cg][G] pinned scores of the base-pass members, in list order
-                     // (ascending token order within the chunk; read by budget and gather)
+    float* bsc;      // [B*Hkv][ncg][G][cg] pinned scores of the base-pass members, in list order
+                     // (ascending token order within the chunk), one row per head; read by budget and gather
     uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* brow;  // [B*Hkv][ncg][cg] V row of each base-pass member (output-level mode, else null)
