@@ -835,24 +835,30 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
 #pragma unroll
     for (int h = 0; h < NH; ++h) cnt[h] = static_cast<uint32_t>(__builtin_popcount(emask & topk_head_slots<NH>(h)));
     block_excl_scan_n<NH>(cnt, &T.S.hist[0][0]);  // the histograms are spent: the scan's scratch
-    // (D) list the boundary buckets, emit the keys above them, head by head
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        uint32_t m = lmask & topk_head_slots<NH>(h);
+    // (D) list the boundary buckets' keys, then emit the keys above them: one
+    //     pass over each mask, a key's position its head's scan position plus
+    //     the head's emitted slots below it on this thread
+    {
+        uint32_t m = lmask;
         while (m) {
             const int s = __builtin_ctz(m);
             m &= m - 1;
+            const int h = (s / 4) % NH;
             fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) {
                 const uint32_t p = atomicAdd(&T.cnt[h], 1u);
                 if (p < static_cast<uint32_t>(kListCap)) T.list[h][p] = topk_key(ok, idx);
             });
         }
-        m = emask & topk_head_slots<NH>(h);
-        uint32_t p = cnt[h];
+        m = emask;
         while (m) {
             const int s = __builtin_ctz(m);
             m &= m - 1;
-            fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { emit(h, p++, topk_key(ok, idx)); });
+            const int h = (s / 4) % NH;
+            uint32_t p = cnt[0];
+#pragma unroll
+            for (int hh = 1; hh < NH; ++hh) p = h == hh ? cnt[hh] : p;
+            p += static_cast<uint32_t>(__builtin_popcount(emask & (topk_head_slots<NH>(0) << (4 * h)) & ((1u << s) - 1u)));
+            fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { emit(h, p, topk_key(ok, idx)); });
         }
     }
     // the boundary bucket's selected keys take the positions after the keys above it
