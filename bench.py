@@ -411,9 +411,23 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbs = 10 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    del dst
+    # ---- a plain read of the same 1 GiB (vattn_read_probe: 16-byte
+    # non-temporal loads, as the decode's streams): the ceiling of a read-only
+    # stream, which a copy understates
+    import verified_sparse_attention_amd as vsa
+    sink = torch.zeros(vsa.READ_PROBE_SINK, dtype=torch.int32, device=dev)
+    vsa.read_probe(src, sink)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(10):
+        vsa.read_probe(src, sink)
+    c1.record()
+    torch.cuda.synchronize()
+    read_gbs = 10 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, sink
     torch.cuda.empty_cache()
-    log("device copy %.0f GB/s (read + write)" % copy_gbs)
+    log("device copy %.0f GB/s (read + write), read %.0f GB/s" % (copy_gbs, read_gbs))
 
     result = {"metric": METRIC, "value": round(value, 1), "unit": "heads·tokens/s", "n_gpus": 1,
               "steps": steps, "warmup": warm, "ms_per_step": round(ms_per_step, 5),
@@ -433,6 +447,7 @@ def main():
                            "union_density": round(float((U / L).mean()), 4),
                            "kernel_frac": kernel_frac},
               "copy_ceiling_GBps": round(copy_gbs, 1),
+              "read_ceiling_GBps": round(read_gbs, 1),
               "stage_us": stages}
 
     # ---- key-side maintenance: append each sequence's newest token (K, V and

@@ -306,6 +306,19 @@ vattn_status vattn_key_gram(const void* k_cache, int32_t kv_dtype, const int32_t
                             int32_t Hkv, int32_t d, int32_t max_seq_len, float* gram, void* workspace,
                             size_t ws_bytes, void* hip_stream);
 
+/* Device read-stream calibration (no part of the method): reads every byte of
+ * buf once with 16-byte non-temporal loads, as the decode's streams do, and
+ * XORs the buffer's 32-bit words into the VATTN_READ_PROBE_SINK words of sink
+ * (one atomic per block, spread over the words; the caller clears sink): the
+ * XOR of the sink's words is then the XOR of the buffer's.  Timed over a
+ * large buffer it gives the device's read-only streaming rate, the ceiling of
+ * the decode's read-dominated kernels (a copy, which also writes,
+ * understates it).  buf: device, 16-byte aligned, bytes a positive multiple
+ * of 16; sink: VATTN_READ_PROBE_SINK device uint32 words.  VATTN_E_NULL /
+ * VATTN_E_SHAPE before any launch.  Asynchronous on hip_stream. */
+#define VATTN_READ_PROBE_SINK 1024
+vattn_status vattn_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
+
 /* z = Phi^-1(1 - delta/2) rounded to fp32, as vattn_decode uses it (host). */
 double vattn_z_from_delta(double delta);
 

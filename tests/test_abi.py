@@ -205,6 +205,17 @@ def test_key_gram_argument_checks(lib):
     assert call(wsb=ws - 1) == 5
 
 
+def test_read_probe_argument_checks(lib):
+    lib.vattn_read_probe.restype = C.c_int
+    lib.vattn_read_probe.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    P = C.c_void_p
+    assert lib.vattn_read_probe(None, 256, P(256), None) == 1
+    assert lib.vattn_read_probe(P(256), 256, None, None) == 1
+    assert lib.vattn_read_probe(P(256), 0, P(256), None) == 2
+    assert lib.vattn_read_probe(P(256), 100, P(256), None) == 2      # not a multiple of 16
+    assert lib.vattn_read_probe(P(264), 256, P(256), None) == 2      # misaligned buffer
+
+
 def test_workspace_size_monotone(lib):
     cfg = _cfg()
     prev = 0

@@ -572,6 +572,22 @@ def _gram_ref(w):
     return g, a
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 37])
+def test_read_probe_checksum(nbytes):
+    """vattn_read_probe XORs every 32-bit word of the buffer into the sink's
+    words: their XOR against numpy's XOR of the same words (sizes with a
+    ragged tail)."""
+    import torch
+    import verified_sparse_attention_amd as vsa
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(vsa.READ_PROBE_SINK, dtype=torch.int32, device="cuda")
+    vsa.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(host)
+
+
 @pytest.mark.parametrize("name,mk", [
     ("d128_ragged_shuffled", lambda: synthetic.make(
         name="gram_d128", B=3, Hq=8, Hkv=2, d=128, seq_lens=(5000, 777, 4096), kv_dtype="bf16",

@@ -29,7 +29,7 @@ STATUS = {0: "VATTN_OK", 1: "VATTN_E_NULL", 2: "VATTN_E_SHAPE", 3: "VATTN_E_DTYP
           4: "VATTN_E_CFG", 5: "VATTN_E_WORKSPACE", 6: "VATTN_E_UNSUPPORTED", 7: "VATTN_E_HIP"}
 EXPORTS = ("vattn_workspace_size", "vattn_decode", "vattn_decode_noalloc", "vattn_decode_profiled", "vattn_project_keys",
            "vattn_append_kv", "vattn_sign_keys", "vattn_append_kv_sig", "vattn_key_gram_workspace_size", "vattn_key_gram", "vattn_z_from_delta",
-           "vattn_status_string")
+           "vattn_read_probe", "vattn_status_string")
 NUM_STAGES = 7
 NOALLOC_SCRATCH_BYTES = 128 << 20  # VATTN_NOALLOC_SCRATCH_BYTES
 STAGES = ("predict", "select", "base", "budget", "gather", "combine", "emit")
@@ -107,6 +107,8 @@ def load():
             [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         lib.vattn_z_from_delta.restype = C.c_double
         lib.vattn_z_from_delta.argtypes = [C.c_double]
+        lib.vattn_read_probe.restype = C.c_int
+        lib.vattn_read_probe.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         lib.vattn_status_string.restype = C.c_char_p
         lib.vattn_status_string.argtypes = [C.c_int]
         _lib = lib
@@ -467,6 +469,27 @@ def key_gram(k_cache, block_table, seq_lens, max_seq_len, gram=None, workspace=N
     if rc != 0:
         raise VattnError(rc, "vattn_key_gram")
     return gram
+
+
+READ_PROBE_SINK = 1024  # VATTN_READ_PROBE_SINK
+
+
+def read_probe(buf, sink, stream=None):
+    """Reads every byte of the contiguous device tensor buf once (16-byte
+    non-temporal loads) and XORs its 32-bit words into the READ_PROBE_SINK
+    words of sink (an int32 device tensor the caller clears; the XOR of its
+    words is the buffer's).  Timed over a large buffer: the device's read-only
+    streaming rate."""
+    import torch
+    _require(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _require(nbytes > 0 and nbytes % 16 == 0 and buf.data_ptr() % 16 == 0,
+             "buf must hold a positive multiple of 16 bytes, 16-byte aligned")
+    _require(sink.is_cuda and sink.dtype == torch.int32 and sink.is_contiguous() and sink.numel() >= READ_PROBE_SINK,
+             "sink must be a contiguous int32 device tensor of READ_PROBE_SINK words")
+    rc = load().vattn_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream_handle(stream))
+    if rc != 0:
+        raise VattnError(rc, "vattn_read_probe")
 
 
 def z_from_delta(delta: float) -> float:

@@ -445,6 +445,14 @@ vattn_status vattn_key_gram(const void* k_cache, int32_t kv_dtype, const int32_t
     return rc == 0 ? VATTN_OK : VATTN_E_HIP;
 }
 
+static_assert(vattn::kProbeSink == VATTN_READ_PROBE_SINK, "one sink size");
+
+vattn_status vattn_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream) {
+    if (!buf || !sink) return VATTN_E_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4)) return VATTN_E_SHAPE;
+    return vattn::launch_read_probe(buf, bytes / 16, sink, hip_stream) == 0 ? VATTN_OK : VATTN_E_HIP;
+}
+
 const char* vattn_status_string(vattn_status s) {
     switch (s) {
         case VATTN_OK: return "VATTN_OK";

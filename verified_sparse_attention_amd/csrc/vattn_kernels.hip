@@ -2455,6 +2455,42 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* pos, cons
     return static_cast<int>(hipGetLastError());
 }
 
+// ===========================================================================
+// read-stream calibration: XOR of a buffer's words, every byte read once
+// ===========================================================================
+constexpr int kProbeUnroll = 4;  // 16-byte loads in flight per lane
+
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ buf, size_t n16, uint32_t* sink) {
+    uint32_t acc = 0;
+    const size_t stride = static_cast<size_t>(gridDim.x) * 256 * kProbeUnroll;
+    for (size_t base = static_cast<size_t>(blockIdx.x) * 256 * kProbeUnroll + threadIdx.x; base < n16;
+         base += stride) {
+        uint4 v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const size_t i = base + static_cast<size_t>(u) * 256;
+            v[u] = i < n16 ? nt_load16(buf + i) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (int o = 32; o >= 1; o >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), o, 64));
+    // one atomic per block, spread over the sink's words (one address would
+    // serialize them)
+    __shared__ uint32_t wx[4];
+    if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicXor(sink + blockIdx.x % kProbeSink, wx[0] ^ wx[1] ^ wx[2] ^ wx[3]);
+}
+
+int launch_read_probe(const void* buf, size_t n16, uint32_t* sink, void* stream) {
+    const size_t want = (n16 + 256 * kProbeUnroll - 1) / (256 * kProbeUnroll);
+    const int grid = static_cast<int>(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4*>(buf), n16, sink);
+    return launched();
+}
+
 int launch_sign(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint32_t* ksig,
                 int num_blocks, int Hkv, int d, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -26,6 +26,7 @@ constexpr int kGatherChunk = 4 * kChunkThreads;  // tokens per base/gather block
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kGramChunk = 4096;     // tokens per partial of the key Gram matrices
 constexpr int kGramTile = 128;       // tokens staged in LDS at a time
+constexpr int kProbeSink = 1024;     // words of the read probe's sink
 #define VATTN_MAX_SEQ_TOKENS (1 << 20)
 
 // Per (sequence, query head) state handed from kernel to kernel.
@@ -106,5 +107,6 @@ int launch_append(const void* k_new, const void* v_new, const int32_t* pos, cons
                   int proj_stride, int kv_bf16, int Hkv, int d, int r, void* stream);
 int launch_sign(const void* k_cache, int kv_bf16, const float* proj, int proj_stride, uint32_t* ksig,
                 int num_blocks, int Hkv, int d, void* stream);
+int launch_read_probe(const void* buf, size_t n16, uint32_t* sink, void* stream);
 
 }  // namespace vattn
