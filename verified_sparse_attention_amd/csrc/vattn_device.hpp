@@ -337,28 +337,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
     return before + inc - v;
 }
 
-// N exclusive block scans at once: v[x] becomes the sum of v[x] over the
-// threads before this one.  wsum holds N * (waves) words.  Every thread
-// calls; ends with a barrier.
-template <int N>
-__device__ __forceinline__ void block_excl_scan_n(uint32_t (&v)[N], uint32_t* wsum) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t inc[N];
-#pragma unroll
-    for (int x = 0; x < N; ++x) {
-        inc[x] = wave_incl_scan(v[x]);
-        if (lane == 63) wsum[x * nw + wave] = inc[x];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < N; ++x) {
-        uint32_t before = 0;
-        for (int w = 0; w < wave; ++w) before += wsum[x * nw + w];
-        v[x] = before + inc[x] - v[x];
-    }
-    __syncthreads();
-}
-
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
     const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
@@ -831,13 +809,27 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
     }
     emask &= have;
     lmask &= have;
+    // positions of the emitted keys: a wave scan of the per-thread counts and
+    // one counter add per wave and head (T.aux starts at 0; it ends at the
+    // number of keys above the boundary buckets, where the list stage goes on)
     uint32_t cnt[NH];
+    {
+        const int lane = threadIdx.x & 63;
+        uint32_t c[NH], incl[NH], wb[NH];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) cnt[h] = static_cast<uint32_t>(__builtin_popcount(emask & topk_head_slots<NH>(h)));
-    block_excl_scan_n<NH>(cnt, &T.S.hist[0][0]);  // the histograms are spent: the scan's scratch
+        for (int h = 0; h < NH; ++h) {
+            c[h] = static_cast<uint32_t>(__builtin_popcount(emask & topk_head_slots<NH>(h)));
+            incl[h] = wave_incl_scan(c[h]);
+            const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl[h]), 63));
+            wb[h] = (lane == 0 && tot) ? atomicAdd(&T.aux[h], tot) : 0u;
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            cnt[h] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wb[h]), 0)) + incl[h] - c[h];
+    }
     // (D) list the boundary buckets' keys, then emit the keys above them: one
-    //     pass over each mask, a key's position its head's scan position plus
-    //     the head's emitted slots below it on this thread
+    //     pass over each mask, a key's position its wave's base plus the
+    //     head's emitted slots below it on this thread
     {
         uint32_t m = lmask;
         while (m) {
@@ -861,8 +853,6 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
             fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { emit(h, p, topk_key(ok, idx)); });
         }
     }
-    // the boundary bucket's selected keys take the positions after the keys above it
-    if (threadIdx.x < NH && T.mode[threadIdx.x] == 1u) T.aux[threadIdx.x] = T.above[threadIdx.x];
     __syncthreads();
     if (!any) return;
     topk_finish<NH>(T, [&](auto&& f) __attribute__((always_inline)) {
