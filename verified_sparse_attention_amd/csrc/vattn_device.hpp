@@ -750,8 +750,8 @@ __device__ __forceinline__ void block_topk(TopkShared<NH>& T, const uint32_t (&w
     }, emit);
 }
 
-// The same selection for keys at fixed per-thread slots, at most 32 per
-// thread, slot s holding a key of head (s / 4) % NH.  items(f) calls
+// The same selection for keys at fixed per-thread slots, NS (a multiple of 4,
+// at most 32) per thread, slot s holding a key of head (s / 4) % NH.  items(f) calls
 // f(s, okey, index) for every key on this thread (the head is the slot's);
 // fetch(s, g) calls g(okey, index) for slot s's key again.  The histogram
 // pass keeps each key's bucket (a byte per slot), so classing a key later is
@@ -765,7 +765,7 @@ __host__ __device__ constexpr uint32_t topk_head_slots(int h) {
     return m;
 }
 
-template <int NH, class Items, class Fetch, class Emit>
+template <int NH, int NS, class Items, class Fetch, class Emit>
 __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32_t (&want)[NH],
                                                  const uint32_t (&total)[NH], const uint32_t (&lo_ok)[NH],
                                                  const uint32_t (&hi_ok)[NH], Items&& items, Fetch&& fetch,
@@ -779,11 +779,12 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
         vmn[h] = T.vmin[h];
         scl[h] = T.scale[h];
     }
+    static_assert(NS % 4 == 0 && NS <= 32, "slots in words of four");
     // (B) bucket histogram; every key's bucket kept
-    uint32_t pk[8];  // byte s % 4 of word s / 4: slot s's bucket
+    uint32_t pk[NS / 4];  // byte s % 4 of word s / 4: slot s's bucket
     uint32_t have = 0;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) pk[w] = 0;
+    for (int w = 0; w < NS / 4; ++w) pk[w] = 0;
     items([&](int s, uint32_t ok, uint32_t) __attribute__((always_inline)) {
         const int h = (s / 4) % NH;
         const int bk = topk_bucket(ok, vmn[h], scl[h]);
@@ -802,7 +803,7 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
     for (int h = 0; h < NH; ++h) bst[h] = md[h] == 2u ? -1 : md[h] == 1u ? T.bstar[h] : kTopBuckets;
     uint32_t emask = 0, lmask = 0;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 0; s < NS; ++s) {
         const int bk = static_cast<int>((pk[s / 4] >> (8 * (s % 4))) & 0xFFu);
         emask |= bk > bst[(s / 4) % NH] ? 1u << s : 0u;
         lmask |= bk == bst[(s / 4) % NH] ? 1u << s : 0u;
@@ -857,7 +858,7 @@ __device__ __forceinline__ void block_topk_slots(TopkShared<NH>& T, const uint32
     if (!any) return;
     topk_finish<NH>(T, [&](auto&& f) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
+        for (int s = 0; s < NS; ++s) {
             const int h = (s / 4) % NH;
             if (((lmask >> s) & 1u) && md[h] == 1u)
                 fetch(s, [&](uint32_t ok, uint32_t idx) __attribute__((always_inline)) { f(h, ok, idx); });

@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
         constexpr int NIT = 8 / G;
         static_assert(4 * kPredThreads * 8 >= kPredKeys, "a chunk's keys fit 32 slots per thread");
         const int o0 = (t0 - cbase) & ~3, o1 = t1 - cbase;
-        block_topk_slots<G>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
+        block_topk_slots<G, 32>(TS, want, total, lo, hi, [&](auto&& f) __attribute__((always_inline)) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int o = o0 + 4 * (tid + it * nthr);
