@@ -371,7 +371,9 @@ def main():
     names = vsa.STAGES
     dom = int(np.argmax(stage_ms))
     dom_name = names[dom]
-    stages = {names[k]: round(float(stage_ms[k]) * 1e3, 2) for k in range(nst)}
+    # the timed step requests no index set, so its emit stage is empty (the
+    # event pair alone) and is left out
+    stages = {names[k]: round(float(stage_ms[k]) * 1e3, 2) for k in range(nst) if names[k] != "emit"}
     log("stage us: %s" % stages)
     log("mean |U_g| %.0f (density %.3f), |B_g| %.0f" % (U.mean(), (U / L).mean(), Bc.mean()))
     dom_bytes = per_kernel_bytes.get(dom_name)
@@ -646,7 +648,7 @@ def main():
             result["hash_predictor"] = {
                 "ms_per_step": round(hash_ms, 5), "value": round(heads_tokens / (hash_ms * 1e-3), 1),
                 "unit": "heads·tokens/s", "union_density": round(float((Uh.cpu().numpy() / L).mean()), 4),
-                "stage_us": {names[k]: round(float(hst[k]) * 1e3, 2) for k in range(nst)},
+                "stage_us": {names[k]: round(float(hst[k]) * 1e3, 2) for k in range(nst) if names[k] != "emit"},
                 "predict_bytes": hpred_bytes,
                 "eps_violation": {k_: hr[k_] for k_ in ("rate", "violations", "trials", "seeds", "cp95")},
                 "output_error": hr["output_error"],
