@@ -490,6 +490,13 @@ FULL = {
                                 [(0, 0), (6, 5)]),
     "llama8b_32k_hash": (lambda: synthetic.llama8b_32k(name="llama8b_32k_hash", predictor=2),
                          [(0, 0), (5, 3)]),
+    # one query head per KV head at 2^20 tokens: predictor chunks of 32768
+    # tokens, the largest one block takes (eight slot iterations per thread,
+    # sample words drawn again for the counting sort)
+    "g1_1m_chunk32k": (lambda: synthetic.make(
+        name="g1_1m_chunk32k", B=1, Hq=8, Hkv=8, d=64, seq_lens=(1 << 20,), kv_dtype="bf16",
+        recipe="outlier", predictor=1, rank=32, sinks=64, window=64, topk_ppm=2500, eps=0.05,
+        data_seed=33), [(0, 0), (0, 5)]),
     # the longest sequence the library takes (2^20 tokens): 256 predictor
     # chunks pre-merged in parts, 1024 gather chunks, 32 emission passes
     "max_seq_1m": (lambda: synthetic.make(
