@@ -1284,17 +1284,17 @@ __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
     const int n = P.bcnt[static_cast<size_t>(bg) * P.ncg + c];
     if (tid < G) hm[tid] = P.hs[bh0 + tid].m;
     for (int x = tid; x < n; x += kChunkThreads) rows[x] = P.brow[lb + x];
-    constexpr int NCH = (G * D + kChunkThreads - 1) / kChunkThreads;  // (head, channel) chains per thread
-    double p1[NCH], p2[NCH], pf[NCH];
+    // a wave covers one head's channels, CPT consecutive ones per lane (a
+    // member's weight is read once for all of them), and heads wave,
+    // wave + NW, ... in turn
+    constexpr int CPT = D / 64, NHT = (G + NW - 1) / NW;
+    static_assert(D % 64 == 0, "a wave covers a head's channels");
+    const int cc = lane * CPT;
+    double p1[NHT][CPT], p2[NHT][CPT], pf[NHT][CPT];
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) p1[k] = p2[k] = pf[k] = 0.0;
-    // chain k: head hk[k], channel cc (the same for every k: the chains of a
-    // thread are kChunkThreads apart, a multiple of D); a wave's lanes share
-    // the head
-    const int cc = tid % D;
-    int hk[NCH];
+    for (int t = 0; t < NHT; ++t)
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) hk[k] = (tid + k * kChunkThreads) / D;
+        for (int k = 0; k < CPT; ++k) p1[t][k] = p2[t][k] = pf[t][k] = 0.0;
     const uint4* vbase = static_cast<const uint4*>(P.v);
     __syncthreads();
     uint4 vr[VPT];
@@ -1348,31 +1348,37 @@ __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
         __syncthreads();
         if (t0 + kNumTile < n) request(t0 + kNumTile);  // block-uniform
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int h = hk[k];
+        for (int t = 0; t < NHT; ++t) {
+            const int h = wave + t * NW;
             if (h >= G) break;  // wave-uniform
 #pragma unroll
             for (int q = 0; q < 2; ++q) {  // q = 0: base sample (T1, T2); q = 1: fixed set (NF)
                 const int nl = lcnt[q][h];
                 for (int j0 = 0; j0 < nl; j0 += 8) {
                     double e[8];
-                    float vf[8];
+                    float vf[8][CPT];
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const int mi = lst[q][h][min(j0 + u, nl - 1)];
                         e[u] = es[mi][h];
-                        if constexpr (sizeof(KVT) == 2) vf[u] = __uint_as_float(static_cast<uint32_t>(vs[mi][cc]) << 16);
-                        else vf[u] = vs[mi][cc];
+#pragma unroll
+                        for (int k = 0; k < CPT; ++k) {
+                            if constexpr (sizeof(KVT) == 2) vf[u][k] = __uint_as_float(static_cast<uint32_t>(vs[mi][cc + k]) << 16);
+                            else vf[u][k] = vs[mi][cc + k];
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         if (j0 + u >= nl) break;  // wave-uniform
-                        const double y = e[u] * static_cast<double>(vf[u]);
-                        if (q == 0) {
-                            p1[k] = p1[k] + y;
-                            p2[k] = p2[k] + y * y;
-                        } else {
-                            pf[k] = pf[k] + y;
+#pragma unroll
+                        for (int k = 0; k < CPT; ++k) {
+                            const double y = e[u] * static_cast<double>(vf[u][k]);
+                            if (q == 0) {
+                                p1[t][k] = p1[t][k] + y;
+                                p2[t][k] = p2[t][k] + y * y;
+                            } else {
+                                pf[t][k] = pf[t][k] + y;
+                            }
                         }
                     }
                 }
@@ -1381,14 +1387,16 @@ __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
         __syncthreads();  // the tile and its lists are restaged
     }
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        const int ch = tid + k * kChunkThreads;  // chain = head * D + channel
-        if (ch >= G * D) break;
-        const int h = ch / D;
+    for (int t = 0; t < NHT; ++t) {
+        const int h = wave + t * NW;
+        if (h >= G) break;
         double* out = P.npart + ((bh0 + h) * P.ncg + c) * 3 * D;
-        out[cc] = p1[k];
-        out[D + cc] = p2[k];
-        out[2 * D + cc] = pf[k];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            out[cc + k] = p1[t][k];
+            out[D + cc + k] = p2[t][k];
+            out[2 * D + cc + k] = pf[t][k];
+        }
     }
 }
 
