@@ -195,7 +195,7 @@ vattn_status vattn_decode(const vattn_inputs* in, const vattn_cfg* cfg, vattn_ou
  * still passes inputs and outputs exactly as for vattn_decode, with the same
  * results.  Returns VATTN_E_WORKSPACE, before any HIP call, when
  * vattn_workspace_size(in, cfg) exceeds VATTN_NOALLOC_SCRATCH_BYTES (e.g.
- * 8 sequences x 32K tokens x 32 query heads need 72 MiB and fit; 64 x 16K
+ * 8 sequences x 32K tokens x 32 query heads need 64 MiB and fit; 64 x 16K
  * do not); other errors as for vattn_decode.  Every call on one GPU shares that
  * GPU's array and leaves it holding its contents (no call needs it cleared):
  * two calls that overlap on one GPU (other streams, other host threads) race
