@@ -94,6 +94,8 @@ def _load():
             lib.orc_project_rows.argtypes = [P, C.c_int64, C.c_int, P, C.c_int, P]
             lib.orc_sign_rows.restype = None
             lib.orc_sign_rows.argtypes = [P, C.c_int64, C.c_int, P, P]
+            lib.orc_key_gram.restype = C.c_int
+            lib.orc_key_gram.argtypes = [C.c_int] * 5 + [P] * 5
             _lib = lib
     return _lib
 
@@ -270,3 +272,24 @@ def dense(*, q, k_cache, v_cache, block_table, seq_lens, groups=None, nthreads=1
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return dict(lse_dense=lse, out_dense=out)
+
+
+def key_gram(*, k_cache, block_table, seq_lens, **_):
+    """Per KV head, sum over every cached token of K K^T in fp64 ([Hkv, d, d]),
+    and the same sums of |K| |K|^T (the scale of an fp32 accumulation's error).
+    Takes the same arrays as decode (extra keys are ignored)."""
+    k_cache = np.ascontiguousarray(k_cache)
+    kv_bf16 = k_cache.dtype == np.uint16
+    _, Hkv, _, d = k_cache.shape
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, max_blocks = block_table.shape
+    gram = np.zeros((Hkv, d, d), dtype=np.float64)
+    absg = np.zeros((Hkv, d, d), dtype=np.float64)
+    rc = _load().orc_key_gram(B, Hkv, d, max_blocks, int(kv_bf16), _ptr(k_cache), _ptr(block_table),
+                              _ptr(seq_lens), _ptr(gram), _ptr(absg))
+    if rc == 5:
+        raise ValueError("oracle refused a non-finite cached key")
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return gram, absg

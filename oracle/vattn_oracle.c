@@ -691,3 +691,46 @@ int orc_dense(int B, int Hq, int Hkv, int d, int max_blocks, int kv_bf16, const 
     }
     return bad ? 5 : 0;
 }
+
+/*
+ * Key second moments per KV head: gram[g][i][j] = sum over every sequence b
+ * and every cached token t < seq_lens[b] of K_ti K_tj, in fp64 (the matrix
+ * whose leading eigenvectors are the principal directions of the keys, the
+ * PCA basis of the pith.science page "Loki: Low-rank Keys for Efficient
+ * Sparse Attention", abstract).  absg (may be NULL) receives the same sums of
+ * |K_ti| |K_tj|, the scale against which an fp32 accumulation's error is
+ * bounded.  Plain loops: sequences ascending, tokens ascending.  Returns 0, 1
+ * or 2 for bad arguments, 5 for a non-finite cached key.
+ */
+int orc_key_gram(int B, int Hkv, int d, int max_blocks, int kv_bf16, const void* k_cache,
+                 const int32_t* block_table, const int32_t* seq_lens, double* gram, double* absg) {
+    if (!k_cache || !block_table || !seq_lens || !gram) return 1;
+    if (B <= 0 || Hkv <= 0 || d <= 0 || max_blocks <= 0) return 2;
+    orc_ctx cx;
+    memset(&cx, 0, sizeof(cx));
+    cx.B = B; cx.Hkv = Hkv; cx.d = d; cx.max_blocks = max_blocks; cx.kv_bf16 = kv_bf16;
+    cx.block_table = block_table; cx.seq_lens = seq_lens;
+    memset(gram, 0, sizeof(double) * (size_t)Hkv * d * d);
+    if (absg) memset(absg, 0, sizeof(double) * (size_t)Hkv * d * d);
+    for (int b = 0; b < B; ++b) {
+        int L = seq_lens[b];
+        if (L < 0 || L > max_blocks * ORC_PAGE) return 2;
+        float* K = (float*)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * d);
+        for (int g = 0; g < Hkv; ++g) {
+            load_rows(&cx, k_cache, b, g, L, K);
+            if (!all_finite(K, (int64_t)L * d)) { free(K); return 5; }
+            double* G = gram + (size_t)g * d * d;
+            double* A = absg ? absg + (size_t)g * d * d : NULL;
+            for (int t = 0; t < L; ++t) {
+                const float* k = K + (size_t)t * d;
+                for (int i = 0; i < d; ++i)
+                    for (int j = 0; j < d; ++j) {
+                        G[(size_t)i * d + j] += (double)k[i] * (double)k[j];
+                        if (A) A[(size_t)i * d + j] += fabs((double)k[i]) * fabs((double)k[j]);
+                    }
+            }
+        }
+        free(K);
+    }
+    return 0;
+}

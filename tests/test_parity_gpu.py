@@ -573,10 +573,8 @@ def _host_keys(w):
 
 
 def _gram_ref(w):
-    keys = _host_keys(w)
-    g = sum(np.einsum("gti,gtj->gij", k, k) for k in keys)
-    a = sum(np.einsum("gti,gtj->gij", np.abs(k), np.abs(k)) for k in keys)
-    return g, a
+    """The oracle's fp64 key Gram and its |K| |K|^T scale (oracle.key_gram)."""
+    return oracle.key_gram(**w.oracle_arrays())
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 37])
@@ -604,9 +602,9 @@ def test_read_probe_checksum(nbytes):
         recipe="normal", predictor=1, rank=16, data_seed=52)),
 ])
 def test_key_gram_matches_fp64(name, mk):
-    """gram[g] = sum_t K_t K_t^T: bf16 products are exact in fp32 and the sums are
-    fp32, so each entry is within 1e-5 (about 170 fp32 ulps) of the sum of the
-    products' magnitudes of the fp64 value."""
+    """gram[g] = sum_t K_t K_t^T against the oracle's fp64 sums: bf16 products are
+    exact in fp32 and the sums are fp32, so each entry is within 1e-5 (about 170
+    fp32 ulps) of the sum of the products' magnitudes of the fp64 value."""
     import torch
     import verified_sparse_attention_amd as vsa
     _, log = _gpu()
