@@ -1835,17 +1835,34 @@ constexpr int kCombineThreads = 1024;
 template <int kThreads>  // per block
 __global__ __launch_bounds__(kThreads) void k_combine(Plan P) {
     constexpr int NW = kThreads / 64;
+    constexpr int U = 8;  // chunk loads in flight per thread
     __shared__ float wsh[kMaxChunks];
     __shared__ float rm[NW], rl[NW];
     __shared__ float accs[kThreads];
     const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / P.Hq;
+    const int D = P.d, ncg = P.ncg;
+    const float* pp = P.part + static_cast<size_t>(bh) * ncg * (D + 2);
+    // nthr / D groups of chunks per dimension
+    const int ngrp = nthr / D, e = tid % D, grp = tid / D;
+    // one round of loads at entry: the sequence length, this thread's chunk
+    // maximum and sum, the first U chunks' partial sums of its dimension and
+    // the head state (slots past the sequence's chunks hold stale values, which
+    // are dropped once its length is known)
     const int L = P.seq_lens[b];
-    const int D = P.d;
+    const float m0 = tid < ncg ? pp[static_cast<size_t>(tid) * (D + 2)] : -__builtin_inff();
+    const float l0 = tid < ncg ? pp[static_cast<size_t>(tid) * (D + 2) + 1] : 0.0f;
+    float v0[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = grp + u * ngrp;
+        v0[u] = c < ncg ? pp[static_cast<size_t>(c) * (D + 2) + 2 + e] : 0.0f;
+    }
+    HeadState hs{};
+    if (tid == 0) hs = P.hs[bh];
     const int nc = (L + P.cg - 1) / P.cg;
-    const float* pp = P.part + static_cast<size_t>(bh) * P.ncg * (D + 2);
-    float mloc = -__builtin_inff();
-    for (int c = tid; c < nc; c += nthr) mloc = fmaxf(mloc, pp[static_cast<size_t>(c) * (D + 2)]);
+    float mloc = tid < nc ? m0 : -__builtin_inff();
+    for (int c = tid + nthr; c < nc; c += nthr) mloc = fmaxf(mloc, pp[static_cast<size_t>(c) * (D + 2)]);
     for (int o = 1; o < 64; o <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
     if (lane == 0) rm[wave] = mloc;
     __syncthreads();
@@ -1853,10 +1870,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(Plan P) {
     for (int w = 0; w < NW; ++w) M = fmaxf(M, rm[w]);
     float lloc = 0.f;
     for (int c = tid; c < nc; c += nthr) {
-        const float* q = pp + static_cast<size_t>(c) * (D + 2);
-        const float wgt = (M == -__builtin_inff()) ? 0.0f : __expf(q[0] - M);
+        const float mc = c == tid ? m0 : pp[static_cast<size_t>(c) * (D + 2)];
+        const float lc = c == tid ? l0 : pp[static_cast<size_t>(c) * (D + 2) + 1];
+        const float wgt = (M == -__builtin_inff()) ? 0.0f : __expf(mc - M);
         wsh[c] = wgt;
-        lloc += wgt * q[1];
+        lloc += wgt * lc;
     }
     for (int o = 1; o < 64; o <<= 1) lloc += __shfl_xor(lloc, o, 64);
     if (lane == 0) rl[wave] = lloc;
@@ -1864,16 +1882,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(Plan P) {
     float l = 0.f;
     for (int w = 0; w < NW; ++w) l += rl[w];
     const bool ok = M != -__builtin_inff() && l > 0.f;
-    // nthr / D groups of chunks per dimension, 8 chunk loads in flight per thread
-    const int ngrp = nthr / D, e = tid % D, grp = tid / D;
-    constexpr int U = 8;
     float a = 0.f;
     for (int c0 = grp; c0 < nc; c0 += U * ngrp) {
         float v[U], wv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u * ngrp;
-            v[u] = c < nc ? pp[static_cast<size_t>(c) * (D + 2) + 2 + e] : 0.f;
+            v[u] = c < nc ? (c0 == grp ? v0[u] : pp[static_cast<size_t>(c) * (D + 2) + 2 + e]) : 0.f;
             wv[u] = c < nc ? wsh[c] : 0.f;
         }
 #pragma unroll
@@ -1888,7 +1903,6 @@ __global__ __launch_bounds__(kThreads) void k_combine(Plan P) {
     }
     if (tid == 0) {
         P.lse[bh] = ok ? M + __logf(l) : -__builtin_inff();
-        const HeadState& hs = P.hs[bh];
         if (P.counts) {
             int32_t* ct = P.counts + static_cast<size_t>(bh) * 6;
             if (L == 0) {
