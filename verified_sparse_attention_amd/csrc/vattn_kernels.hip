@@ -1526,41 +1526,28 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
     const int bg = gather_group(P, tid), b = bg / P.Hkv, g = bg % P.Hkv, c = blockIdx.x;
-    const int T0 = c * P.cg;
-    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
-    constexpr int PER = kGatherChunk / kChunkThreads;  // list entries per thread
-    // one round of loads: the sequence length, the heads' state, the quad's
-    // page and each head's bitmap word, and this thread's entries of the
-    // chunk's cached scores (entry y = tid + e * nthr of the base pass's list,
-    // the rank among the cached tokens it takes below).  None waits for the
-    // length: the page and bitmap reads are bounded by the table and bitmap
-    // sizes and the score reads by the chunk's slots, and whatever lies past
-    // the sequence's end or the list's is dropped once they are known.
     const int L = P.seq_lens[b];
+    const int T0 = c * P.cg;
+    if (T0 >= L) return;
+    if (tid == 0) s_over = 0;
+    const Regions R = regions(P, L);
+    const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    // the heads' state, the quad's page, sample words and each head's bitmap
+    // word are requested together
     if (tid < G) {
         const HeadState& s = P.hs[bh0 + tid];
         hv[tid] = HeadView{s.thr_b, s.thr_n, s.nb, s.n, s.wsamp, s.m};
     }
-    const int qd = (T0 >> 2) + tid;
-    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
-    const int32_t page = (qd >> 2) < P.max_blocks ? btrow[qd >> 2] : 0;
-    uint32_t fw[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) fw[h] = (qd >> 3) < P.words ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
-    const float* bsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
-    float cv[PER][G];
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-#pragma unroll
-        for (int h = 0; h < G; ++h) cv[e][h] = bsc[static_cast<size_t>(h) * P.cg + tid + e * nthr];
-    if (T0 >= L) return;
-    if (tid == 0) s_over = 0;
-    const Regions R = regions(P, L);
     const int T1 = min(T0 + P.cg, L);
+    const int qd = (T0 >> 2) + tid;
     const bool live4 = 4 * qd < T1;
-    const uint32_t row0 = live4 ? (static_cast<uint32_t>(page) * P.Hkv + g) * kPage : 0u;
+    const int32_t* btrow = P.bt + static_cast<size_t>(b) * P.max_blocks;
+    const uint32_t row0 = live4 ? (static_cast<uint32_t>(btrow[qd >> 2]) * P.Hkv + g) * kPage : 0u;
     const bool anyM = live4 && 4 * qd + 3 >= R.lo && 4 * qd < R.hi;
     const uint4 w = anyM ? quad_words(static_cast<uint32_t>(qd), g, b, P.seed_lo, P.seed_hi) : make_uint4(0, 0, 0, 0);
+    uint32_t fw[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) fw[h] = live4 ? P.bits[(bh0 + h) * P.words + (qd >> 3)] : 0u;
     __syncthreads();
 
     // membership: meta = final mask | fixed mask << 8 | score cached << 16.
@@ -1627,16 +1614,19 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     // rows below.
     constexpr int LPT = D / 8, TPW = 64 / LPT;
     const int j = lane % LPT, slot = lane / LPT;
+    const float* bsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
     const KVT* kbase = static_cast<const KVT*>(P.k);
     {
+        constexpr int PER = kGatherChunk / kChunkThreads;  // list entries per thread
         float v[PER][G];
         uint32_t mm[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int x = nu + tid + e * nthr;  // the cached entry of rank tid + e * nthr
+            const int x = nu + tid + e * nthr;
             mm[e] = x < n ? tmeta[x] : 0u;
+            const size_t at = static_cast<size_t>(x < n ? x - nu : 0);
 #pragma unroll
-            for (int h = 0; h < G; ++h) v[e][h] = x < n ? cv[e][h] : 0.0f;
+            for (int h = 0; h < G; ++h) v[e][h] = x < n ? bsc[static_cast<size_t>(h) * P.cg + at] : 0.0f;
         }
         bool over = false;
 #pragma unroll
