@@ -318,5 +318,23 @@ def wide_gqa_64k(seed=0, eps=0.05, B=4, L=65536, **kw):
     return make(**args)
 
 
+def repaged(w: Workload, seed: int = 0) -> Workload:
+    """The same workload with its cache pages moved to a seeded permutation of
+    the physical page ids and the block table rewritten to match: every token's
+    K and V (and so every result) are unchanged, only the physical layout of
+    the cache differs."""
+    import dataclasses
+    gen = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(w.k_cache.shape[0], generator=gen)  # new id of page p
+    k = torch.empty_like(w.k_cache)
+    v = torch.empty_like(w.v_cache)
+    k[perm] = w.k_cache
+    v[perm] = w.v_cache
+    bt = w.block_table.clone()
+    used = bt >= 0
+    bt[used] = perm[bt[used].long()].to(torch.int32)
+    return dataclasses.replace(w, name=w.name + "_repaged", k_cache=k, v_cache=v, block_table=bt)
+
+
 WORKLOADS = {"tiny_1k": tiny, "llama8b_32k": llama8b_32k, "flat_128k": flat_128k,
              "ragged_b64": ragged_b64, "wide_gqa_64k": wide_gqa_64k}

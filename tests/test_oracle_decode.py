@@ -418,3 +418,19 @@ def test_each_group_uses_its_own_basis():
             assert np.array_equal(full[key][:, hs], own[key][:, hs]), (g, key)
         differs += int(not np.array_equal(full["idx"][:, hs], other["idx"][:, hs]))
     assert differs > 0  # the bases matter: another head's basis selects other tokens
+
+
+def test_results_do_not_depend_on_page_layout():
+    """The pages of a cache moved to other physical ids (block table rewritten
+    to match) hold the same tokens: index sets, counts, statistics and outputs
+    are identical (a mixed-up page or token index would move them)."""
+    for w in (synthetic.tiny(seed=0),
+              synthetic.make(name="repage_lowrank", B=2, Hq=8, Hkv=2, d=64, seq_lens=(1500, 700),
+                             kv_dtype="bf16", predictor=1, rank=16, sinks=8, window=16, topk_ppm=30000,
+                             data_seed=77)):
+        r = synthetic.repaged(w, seed=3)
+        assert not np.array_equal(r.block_table.numpy(), w.block_table.numpy())
+        a = oracle.decode(**w.oracle_arrays(), cfg=w.cfg)
+        b = oracle.decode(**r.oracle_arrays(), cfg=r.cfg)
+        for key in ("idx", "counts", "stats", "out", "lse"):
+            assert np.array_equal(a[key], b[key]), key
