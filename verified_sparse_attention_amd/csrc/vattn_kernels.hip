@@ -1532,6 +1532,10 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     if (tid == 0) s_over = 0;
     const Regions R = regions(P, L);
     const size_t bh0 = static_cast<size_t>(b) * P.Hq + g * G;
+    // the row passes walk the member list from a block-dependent start
+    // (cyclically): with the pages of the sequences laid out alike, blocks that
+    // run together would otherwise read rows at the same page offsets in step
+    const int rot = static_cast<int>(((static_cast<uint32_t>(c) * 2654435761u) ^ (static_cast<uint32_t>(bg) * 40503u)) >> 22);
     // the heads' state, the quad's page, sample words and each head's bitmap
     // word are requested together
     if (tid < G) {
@@ -1659,14 +1663,16 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
             for (int e = 0; e < 8; ++e) qreg[h][e] = P.q[(bh0 + h) * D + 8 * j + e] * P.scale32;
         bool over = false;
+        const int rk = nu > 0 ? rot % nu : 0;
         for (int base = wave * TPW * KU; base < nu; base += nwaves * TPW * KU) {
             Raw8 kr[KU];
             uint32_t mk[KU];
 #pragma unroll
             for (int u = 0; u < KU; ++u) {
                 const int x = base + u * TPW + slot;
-                mk[u] = x < nu ? tmeta[x] : 0u;
-                load_raw_nt(kbase + static_cast<size_t>(trow[x < nu ? x : 0]) * D + 8 * j, kr[u]);
+                const int xr = x < nu ? (x + rk < nu ? x + rk : x + rk - nu) : 0;
+                mk[u] = x < nu ? tmeta[xr] : 0u;
+                load_raw_nt(kbase + static_cast<size_t>(trow[xr]) * D + 8 * j, kr[u]);
             }
 #pragma unroll
             for (int u = 0; u < KU; ++u) {
@@ -1677,13 +1683,14 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 for (int h = 0; h < G; ++h) part[h] = chain8(qreg[h], kf);
                 spread_across_lanes<G, LPT>(part, sv, j);
                 const int x = base + u * TPW + slot;
+                const int xr = x + rk < nu ? x + rk : x + rk - nu;
                 if (fin && x < nu) {
 #pragma unroll
                     for (int e = 0; e < NH; ++e) {
                         const int h = hsel[e];
                         const bool mem = (mk[u] >> h) & 1u;
                         over |= mem && sv[e] > hv[h].m + kRescale;
-                        sp[h][x] = mem ? sv[e] : -__builtin_inff();
+                        sp[h][xr] = mem ? sv[e] : -__builtin_inff();
                     }
                 }
             }
@@ -1763,19 +1770,21 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
             int x0;
         };
         // rows past the list end reread the last row with weight 0 (no branches)
+        const int rv = n > 0 ? rot % n : 0;
         auto issue = [&](VBatch& bt, int b0) __attribute__((always_inline)) {
             bt.x0 = b0;
 #pragma unroll
             for (int u = 0; u < kGatherUnrollV; ++u) {
-                const int x = min(b0 + u * TPW + slot, n - 1);
-                load_raw_nt(vbase + static_cast<size_t>(trow[x]) * D + 8 * j, bt.vr[u]);
+                const int x = b0 + u * TPW + slot;
+                const int xc = x < n ? (x + rv < n ? x + rv : x + rv - n) : n - 1;
+                load_raw_nt(vbase + static_cast<size_t>(trow[xc]) * D + 8 * j, bt.vr[u]);
             }
         };
         auto accumulate = [&](const VBatch& bt) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < kGatherUnrollV; ++u) {
                 const int x = bt.x0 + u * TPW + slot;
-                const int xc = min(x, n - 1);
+                const int xc = x < n ? (x + rv < n ? x + rv : x + rv - n) : n - 1;
                 float vf[8];
                 widen<KVT>(bt.vr[u], vf);
 #pragma unroll
