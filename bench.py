@@ -51,6 +51,10 @@ def parse():
                          "are also measured at base-sample rates of 5, 10 and 20%% of the tail")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the hash-predictor, output-level and host-resident K/V legs")
+    ap.add_argument("--layout-leg", action="store_true",
+                    help="also time the workload with its pages in a permuted block table (same tokens, results "
+                         "compared bit for bit); opt-in so the default run's kernel trace holds the headline's "
+                         "dispatches only")
     ap.add_argument("--pca-basis", action="store_true",
                     help="also time and rate-check the workload with per-KV-head PCA predictor bases")
     return ap.parse_args()
@@ -567,7 +571,7 @@ def main():
             % (hw.B, host_ms, link_gbs, dense_ms))
         del hdec, kh, vh, dst, hD
 
-    if not args.no_legs and not args.profile and args.workload == "llama8b_32k":
+    if args.layout_leg and not args.profile and args.workload == "llama8b_32k":
         # ---- the same workload with a globally shuffled block table: the same
         # tokens in pages scattered over the cache, so only the physical
         # layout differs (and the results must not)
