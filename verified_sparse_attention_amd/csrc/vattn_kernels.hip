@@ -43,7 +43,8 @@
 namespace vattn {
 
 constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
-constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass
+constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass (fp32 K)
+constexpr int kBaseUnrollBf16 = 12;  // the same for bf16 K (8-byte-narrower rows: 12 fit the same registers)
 constexpr int kKeyPad = 16;     // words between the predictor's per-head key rows
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
@@ -957,7 +958,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     const KVT* kbase = static_cast<const KVT*>(P.k);
     float* lsc = P.bsc + (static_cast<size_t>(bg) * P.ncg + c) * P.cg * G;
     const int n = static_cast<int>(cnt);
-    constexpr int kBU = kBaseUnroll;
+    constexpr int kBU = std::is_same<KVT, uint16_t>::value ? kBaseUnrollBf16 : kBaseUnroll;
     for (int base = wave * TPW * kBU; base < n; base += nwaves * TPW * kBU) {
         Raw8 kr[kBU];
         int xl[kBU];
