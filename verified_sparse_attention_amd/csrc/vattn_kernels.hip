@@ -1478,7 +1478,7 @@ __global__ __launch_bounds__(kThreads) void k_budget_num(Plan P) {
 // stream of V rows accumulating sum_i p_i V_i.  Every weight is computed once.
 // ===========================================================================
 constexpr float kRescale = 16.0f;  // reference-maximum headroom for the weights (e^16)
-constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group
+constexpr int kGatherUnrollV = 6;  // V rows per batch and lane group (4 with eight heads per group)
 constexpr int kGatherUnrollK = 8;  // K rows per batch and lane group (VALU scoring)
 
 // Group of a gather block.  Block row y takes the group of rank y when the
@@ -1765,9 +1765,12 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     {
+        // eight heads keep 8 x 8 accumulators per lane: 4 rows per batch keep the
+        // kernel at 3 waves per SIMD (146 VGPRs; 6 rows take 182, 2 waves)
+        constexpr int VU = G == 8 ? 4 : kGatherUnrollV;
         const KVT* vbase = static_cast<const KVT*>(P.v);
         struct VBatch {
-            Raw8 vr[kGatherUnrollV];
+            Raw8 vr[VU];
             int x0;
         };
         // rows past the list end reread the last row with weight 0 (no branches)
@@ -1775,7 +1778,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         auto issue = [&](VBatch& bt, int b0) __attribute__((always_inline)) {
             bt.x0 = b0;
 #pragma unroll
-            for (int u = 0; u < kGatherUnrollV; ++u) {
+            for (int u = 0; u < VU; ++u) {
                 const int x = b0 + u * TPW + slot;
                 const int xc = x < n ? (x + rv < n ? x + rv : x + rv - n) : n - 1;
                 load_raw_nt(vbase + static_cast<size_t>(trow[xc]) * D + 8 * j, bt.vr[u]);
@@ -1783,7 +1786,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
         };
         auto accumulate = [&](const VBatch& bt) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < kGatherUnrollV; ++u) {
+            for (int u = 0; u < VU; ++u) {
                 const int x = bt.x0 + u * TPW + slot;
                 const int xc = x < n ? (x + rv < n ? x + rv : x + rv - n) : n - 1;
                 float vf[8];
@@ -1796,10 +1799,10 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
                 }
             }
         };
-        // one batch of kGatherUnrollV rows per lane group per iteration, all
+        // one batch of VU rows per lane group per iteration, all
         // requested before any is accumulated (rows past the end reread the
         // last row with weight 0)
-        for (int b0 = wave * TPW * kGatherUnrollV; b0 < n; b0 += nwaves * TPW * kGatherUnrollV) {
+        for (int b0 = wave * TPW * VU; b0 < n; b0 += nwaves * TPW * VU) {
             VBatch bt;
             issue(bt, b0);
             accumulate(bt);
