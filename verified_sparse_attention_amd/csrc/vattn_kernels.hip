@@ -44,7 +44,7 @@ namespace vattn {
 
 constexpr int kUnroll = 4;      // token rows in flight per lane group in the predictor stream
 constexpr int kBaseUnroll = 8;  // K rows in flight per lane group in the base pass (fp32 K)
-constexpr int kBaseUnrollBf16 = 12;  // the same for bf16 K (8-byte-narrower rows: 12 fit the same registers)
+constexpr int kBaseUnrollBf16 = 12;  // the same for bf16 K (a lane's slice of a bf16 row takes half the registers)
 constexpr int kKeyPad = 16;     // words between the predictor's per-head key rows
 constexpr int kMaxChunks = (VATTN_MAX_SEQ_TOKENS + kGatherChunk - 1) / kGatherChunk;
 
