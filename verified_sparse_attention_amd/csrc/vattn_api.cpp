@@ -149,7 +149,7 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     L.bsc = off;
     off += align_up(BHkv * s.ncg * s.cg * s.G * sizeof(float));
     L.bmeta = off;
-    off += align_up(BHkv * s.ncg * s.cg * sizeof(uint32_t));
+    off += align_up(BHkv * s.ncg * s.cg * sizeof(uint16_t));
     L.bcnt = off;
     off += align_up(BHkv * s.ncg * sizeof(int32_t));
     L.crange = off;
@@ -256,7 +256,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.slist = reinterpret_cast<int32_t*>(ws + L.slist);
     p.hh = reinterpret_cast<uint32_t*>(ws + L.hh);
     p.bsc = reinterpret_cast<float*>(ws + L.bsc);
-    p.bmeta = reinterpret_cast<uint32_t*>(ws + L.bmeta);
+    p.bmeta = reinterpret_cast<uint16_t*>(ws + L.bmeta);
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
     p.gw = reinterpret_cast<uint32_t*>(ws + L.gw);

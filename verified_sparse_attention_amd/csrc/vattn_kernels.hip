@@ -916,7 +916,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
     }
     uint32_t cnt;
     uint32_t pos = block_excl_scan(mine, wsum, cnt);
-    uint32_t* lmeta = P.bmeta + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
+    uint16_t* lmeta = P.bmeta + (static_cast<size_t>(bg) * P.ncg + c) * P.cg;
     uint32_t* lrow = P.brow ? P.brow + (static_cast<size_t>(bg) * P.ncg + c) * P.cg : nullptr;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -924,7 +924,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_base(Plan P) {
             const uint32_t rw = row0 + ((4 * qd + e) & (kPage - 1));
             tmeta[pos] = m4[e];
             trow[pos] = rw;
-            lmeta[pos] = m4[e];
+            lmeta[pos] = static_cast<uint16_t>(m4[e]);
             if (lrow) lrow[pos] = rw;  // the V row, for the output-level statistics
             ++pos;
         }
@@ -1092,7 +1092,7 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
     // each wave's first two chunks: member counts, masks and scores requested
     // now, with the histogram and the chunk maxima (they need no m)
     const int G = P.G;
-    const uint32_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
+    const uint16_t* bmeta = P.bmeta + static_cast<size_t>(bg) * P.ncg * P.cg;
     const float* bsc = P.bsc + static_cast<size_t>(bg) * P.ncg * P.cg * G + static_cast<size_t>(hg) * P.cg;
     const int32_t* bcnt = P.bcnt + static_cast<size_t>(bg) * P.ncg;
     auto request = [&](int ca, int y0, int na, int nb2, uint32_t (&tm)[2][kStatsBatch],
@@ -1105,7 +1105,7 @@ __global__ __launch_bounds__(kThreads) void k_budget(Plan P) {
             for (int v = 0; v < kStatsBatch; ++v) {
                 const int y = y0 + lane + 64 * v;
                 const size_t at = static_cast<size_t>(cc) * P.cg + y;
-                tm[q][v] = y < ncc ? bmeta[at] : 0u;
+                tm[q][v] = y < ncc ? static_cast<uint32_t>(bmeta[at]) : 0u;
                 sv[q][v] = y < ncc ? bsc[static_cast<size_t>(cc) * P.cg * G + y] : 0.0f;  // head hg's row of the chunk
             }
         }
@@ -1312,7 +1312,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_numstat(Plan P) {
         for (int u = 0; u < EPT; ++u) {
             const int x = tid + u * kChunkThreads, mi = x / G, h = x - mi * G;
             if (mi < tn) {
-                mr[u] = P.bmeta[lb + t0 + mi];
+                mr[u] = static_cast<uint32_t>(P.bmeta[lb + t0 + mi]);
                 sr[u] = P.bsc[lb * G + static_cast<size_t>(h) * P.cg + t0 + mi];
             }
         }

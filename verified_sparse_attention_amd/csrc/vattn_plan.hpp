@@ -72,7 +72,7 @@ struct Plan {
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
     float* bsc;      // [B*Hkv][ncg][G][cg] pinned scores of the base-pass members, in list order
                      // (ascending token order within the chunk), one row per head; read by budget and gather
-    uint32_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8
+    uint16_t* bmeta; // [B*Hkv][ncg][cg] base mask | fixed mask << 8 (G <= 8 heads: 16 bits)
     int32_t* bcnt;   // [B*Hkv][ncg] members per base chunk
     uint32_t* brow;  // [B*Hkv][ncg][cg] V row of each base-pass member (output-level mode, else null)
     double* npart;   // [B*Hq][ncg][3][d] numerator partials T1, T2, NF per chunk (output-level mode)
