@@ -143,7 +143,7 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     L.soff = off;
     off += align_up(BHkv * s.ncp * (vattn::kSampBins + 1) * sizeof(uint32_t));
     L.slist = off;
-    off += align_up(BHkv * s.ncp * static_cast<size_t>(s.cp) * sizeof(int32_t));
+    off += align_up(BHkv * s.ncp * static_cast<size_t>(s.cp) * sizeof(uint16_t));
     L.hh = off;
     off += align_up(BHq * vattn::kSampBins * sizeof(uint32_t));
     L.bsc = off;
@@ -253,7 +253,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.cmax = reinterpret_cast<float*>(ws + L.cmax);
     p.part = reinterpret_cast<float*>(ws + L.part);
     p.soff = reinterpret_cast<uint32_t*>(ws + L.soff);
-    p.slist = reinterpret_cast<int32_t*>(ws + L.slist);
+    p.slist = reinterpret_cast<uint16_t*>(ws + L.slist);
     p.hh = reinterpret_cast<uint32_t*>(ws + L.hh);
     p.bsc = reinterpret_cast<float*>(ws + L.bsc);
     p.bmeta = reinterpret_cast<uint16_t*>(ws + L.bmeta);

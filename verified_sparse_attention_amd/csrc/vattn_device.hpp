@@ -884,11 +884,12 @@ struct HeadSamp {
 };
 
 // Chunk c of the middle holds its tokens grouped by bin: bin x of chunk c is
-// slist[c * cp + soff[c][x] .. c * cp + soff[c][x + 1]).  Chunks are the
+// slist[c * cp + soff[c][x] .. c * cp + soff[c][x + 1]), each entry the token's
+// offset from the chunk's first token, c * cp.  Chunks are the
 // predictor's; only those overlapping the middle [lo, hi) were written.
 struct BinLists {
     const uint32_t* soff;  // [nchunks][kSampBins + 1]
-    const int32_t* slist;  // [nchunks][cp]
+    const uint16_t* slist;  // [nchunks][cp] token offsets within the chunk
     int nchunks, cp, lo, hi;
 };
 
@@ -925,9 +926,9 @@ __device__ __forceinline__ void head_sample_threshold(HeadSamp& S, SelShared<1>&
             if (max(c * BL.cp, BL.lo) >= min((c + 1) * BL.cp, BL.hi)) continue;
             const uint32_t* off = BL.soff + static_cast<size_t>(c) * (kSampBins + 1) + bn;
             const uint32_t a = off[0], e = off[1];
-            const int32_t* lst = BL.slist + static_cast<size_t>(c) * BL.cp;
+            const uint16_t* lst = BL.slist + static_cast<size_t>(c) * BL.cp;
             for (uint32_t p = a + lane; p < e; p += 64) {
-                const int i = lst[p];
+                const int i = c * BL.cp + static_cast<int>(lst[p]);
                 if (!in_fixed(i)) f(sample_key(word_of_token(i), static_cast<uint32_t>(i)));
             }
         }

@@ -567,8 +567,11 @@ __global__ __launch_bounds__(kPredThreads) void k_predict(Plan P) {
             }
         }
         __syncthreads();
-        int32_t* sl = P.slist + (static_cast<size_t>(bg) * P.ncp + c) * P.cp;
-        for (int x = tid; x < t1 - t0; x += nthr) sl[x] = stage[x];
+        // stored as 16-bit offsets from the chunk's first token (a chunk spans
+        // at most kPredKeys tokens)
+        uint16_t* sl = P.slist + (static_cast<size_t>(bg) * P.ncp + c) * P.cp;
+        const int cfirst = c * P.cp;
+        for (int x = tid; x < t1 - t0; x += nthr) sl[x] = static_cast<uint16_t>(stage[x] - cfirst);
     }
 }
 

@@ -15,6 +15,7 @@ constexpr int kChunkThreads = 256;   // base scores and gather
 constexpr int kEmitThreads = 1024;   // index-set emission
 constexpr int kEmitQuads = 8;       // token quads per lane and pass of the index-set emission
 constexpr int kPredKeys = 32768;     // predictor keys held in LDS per block (128 KiB)
+static_assert(kPredKeys <= 65536, "a predictor chunk's token offsets fit 16 bits");
 constexpr int kSampBits = 11;        // sampler histogram: top bits of the Philox word
 constexpr int kSampBins = 1 << kSampBits;
 constexpr int kTopBuckets = 256;     // value-range buckets of the top-k select
@@ -68,7 +69,7 @@ struct Plan {
     float* cmax;     // [B*Hq][ncg] chunk max of pinned scores
     float* part;     // [B*Hq][ncg][d + 2] online-softmax partials (m, l, acc[d])
     uint32_t* soff;  // [B*Hkv][ncp][kSampBins + 1] bin offsets of each chunk's middle tokens
-    int32_t* slist;  // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin
+    uint16_t* slist; // [B*Hkv][ncp][cp] each chunk's middle tokens grouped by sample-word bin (offsets in the chunk)
     uint32_t* hh;    // [B*Hq][kSampBins] sampler-word histogram of each head's tail
     float* bsc;      // [B*Hkv][ncg][G][cg] pinned scores of the base-pass members, in list order
                      // (ascending token order within the chunk), one row per head; read by budget and gather
