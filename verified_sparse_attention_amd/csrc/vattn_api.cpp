@@ -154,8 +154,8 @@ Layout layout(const vattn_inputs* in, const Shape& s) {
     off += align_up(BHkv * s.ncg * sizeof(int32_t));
     L.crange = off;
     off += align_up(BHq * s.ncp * 2 * sizeof(uint32_t));
-    L.gw = off;
-    off += align_up(BHkv * sizeof(uint32_t));
+    L.gw = off;  // gw, then gorder
+    off += align_up(2 * BHkv * sizeof(uint32_t));
     L.cand2 = off;
     off += align_up(BHq * s.nparts * static_cast<size_t>(s.kcap2) * sizeof(uint64_t));
     L.crange2 = off;
@@ -260,6 +260,7 @@ static vattn_status decode_impl(const vattn_inputs* in, const vattn_cfg* cfg, va
     p.bcnt = reinterpret_cast<int32_t*>(ws + L.bcnt);
     p.crange = reinterpret_cast<uint32_t*>(ws + L.crange);
     p.gw = reinterpret_cast<uint32_t*>(ws + L.gw);
+    p.gorder = reinterpret_cast<int32_t*>(p.gw + static_cast<size_t>(in->B) * in->Hkv);
     p.nparts = s.nparts;
     p.kcap2 = s.kcap2;
     p.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);

@@ -1492,11 +1492,32 @@ constexpr int kGatherUnrollK = 8;  // K rows per batch and lane group (VALU scor
 // to keep HBM busy, stays short.  Every block derives the same order from the
 // group weights the budgets wrote.  With more groups than threads the rows
 // keep their own groups.
+// With more groups than a gather block has threads (up to kOrderMaxGroups), one
+// block ranks them once, into gorder, before the gather.
+constexpr int kOrderMaxGroups = 4096;
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void k_order(Plan P) {
+    __shared__ float w[kOrderMaxGroups];
+    const int ngr = P.B * P.Hkv;  // kChunkThreads < ngr <= kOrderMaxGroups
+    for (int x = threadIdx.x; x < ngr; x += blockDim.x) w[x] = __uint_as_float(P.gw[x]);
+    __syncthreads();
+    for (int x = threadIdx.x; x < ngr; x += blockDim.x) {
+        const float mine = w[x];
+        int rank = 0;
+        for (int u = 0; u < ngr; ++u) {
+            const float o = w[u];
+            rank += (o > mine || (o == mine && u < x)) ? 1 : 0;
+        }
+        P.gorder[rank] = x;
+    }
+}
+
 __device__ __forceinline__ int gather_group(const Plan& P, int tid) {
     __shared__ float gw[kChunkThreads];
     __shared__ int s_bg;
     const int ngr = P.B * P.Hkv, y = blockIdx.y;
-    if (ngr > kChunkThreads) return y;  // uniform over the grid
+    if (ngr > kChunkThreads) return ngr <= kOrderMaxGroups ? P.gorder[y] : y;  // uniform over the grid
     if (tid == 0) s_bg = y;
     const float mine = tid < ngr ? __uint_as_float(P.gw[tid]) : 0.0f;
     if (tid < ngr) gw[tid] = mine;
@@ -2188,6 +2209,11 @@ static int launch_chunk_kernels(const Plan& p, hipStream_t st, const Marks& mk) 
         if ((rc = launched())) return rc;
     }
     if ((rc = mk.mark(4))) return rc;
+    const int ngr = p.B * p.Hkv;
+    if (ngr > kChunkThreads && ngr <= kOrderMaxGroups) {
+        hipLaunchKernelGGL(k_order, dim3(1), dim3(kOrderThreads), 0, st, p);
+        if ((rc = launched())) return rc;
+    }
     hipLaunchKernelGGL((k_gather<D, KVT, G>), grid_c, dim3(kChunkThreads), 0, st, p);
     if ((rc = launched())) return rc;
     return mk.mark(5);

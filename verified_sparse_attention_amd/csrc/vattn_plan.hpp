@@ -79,6 +79,7 @@ struct Plan {
     double* npart;   // [B*Hq][ncg][3][d] numerator partials T1, T2, NF per chunk (output-level mode)
     uint32_t* crange;  // [B*Hq][ncp][2] order-key bracket (min, max) of each chunk's candidates
     uint32_t* gw;      // [B*Hkv] gather dispatch weight: max over the group's heads of (n_fixed + n) / L, fp32 bits
+    int32_t* gorder;   // [B*Hkv] groups by descending gw (ties to the lower group), for more groups than a gather block has threads
     // pre-merged candidate parts (nparts > 0 only: few heads, many chunks)
     int nparts, kcap2; // parts; key slots per part = min(k bound, cp * chunks in the largest part)
     uint64_t* cand2;   // [B*Hq][nparts][kcap2] each part's exact top-min(k, n) keys

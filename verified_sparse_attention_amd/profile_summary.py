@@ -30,7 +30,7 @@ from . import build as _build
 
 # must match the calibration copy in bench.py --profile
 CALIBRATION_BYTES = 256 << 20
-STAGE_KERNELS = ("k_predict", "k_premerge", "k_select", "k_base", "k_budget", "k_numstat", "k_gather", "k_combine", "k_emit",
+STAGE_KERNELS = ("k_predict", "k_premerge", "k_select", "k_base", "k_budget", "k_numstat", "k_order", "k_gather", "k_combine", "k_emit",
                  "k_project")
 
 
